@@ -43,8 +43,11 @@ from typing import Dict, List, Sequence, Tuple
 
 import numpy as np
 
-# Largest number of score-matrix entries one query block may hold (float64): 1 GiB.
-_BLOCK_ELEMS = 1 << 27
+# Largest number of score-matrix entries one query block may hold (float64): 256 MiB.
+# Blocks are evaluated in preallocated buffers with in-place operations; each query row
+# is still computed on its own, exactly as the definition states.
+_BLOCK_ELEMS = 1 << 25
+_MAX_ROWS = 256
 
 
 def default_scale(d: int) -> float:
@@ -53,7 +56,7 @@ def default_scale(d: int) -> float:
 
 
 def _row_block(n_keys: int) -> int:
-    return max(1, min(1024, _BLOCK_ELEMS // max(1, n_keys)))
+    return max(1, min(_MAX_ROWS, _BLOCK_ELEMS // max(1, n_keys)))
 
 
 def head_scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
@@ -73,23 +76,29 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> T
     """Softmax attention of one head: O = softmax(tau Q K^T) V and LSE per query row.
 
     Dense and bidirectional (Zellige §II-A): every query row sees every key row given.
-    ``LSE_i = m_i + ln sum_j exp(s_ij - m_i)`` with ``m_i = max_j s_ij``;
-    ``O_i = sum_j exp(s_ij - LSE_i) v_j``. Blocked over query rows only so that one
-    block of scores stays under 1 GiB; each row is computed independently.
+    ``LSE_i = m_i + ln l_i`` with ``m_i = max_j s_ij`` and ``l_i = sum_j exp(s_ij - m_i)``;
+    ``O_i = sum_j p_ij v_j`` with ``p_ij = exp(s_ij - LSE_i) = exp(s_ij - m_i) / l_i``.
+    Query rows are processed in blocks only to bound memory.
     """
-    lq, d = q.shape
+    lq = q.shape[0]
+    nk = k.shape[0]
     o = np.empty((lq, v.shape[1]), dtype=np.float64)
     lse = np.empty(lq, dtype=np.float64)
-    blk = _row_block(k.shape[0])
+    blk = _row_block(nk)
+    buf = np.empty((min(blk, lq), nk), dtype=np.float64)
+    kt = np.ascontiguousarray(k.T)
     for i0 in range(0, lq, blk):
         i1 = min(lq, i0 + blk)
-        s = head_scores(q[i0:i1], k, scale)
+        s = buf[: i1 - i0]
+        np.matmul(q[i0:i1], kt, out=s)
+        s *= scale                      # s_ij
         m = s.max(axis=1)
-        l_sum = np.exp(s - m[:, None]).sum(axis=1)
-        lse_b = m + np.log(l_sum)
-        p = np.exp(s - lse_b[:, None])
-        o[i0:i1] = p @ v
-        lse[i0:i1] = lse_b
+        s -= m[:, None]
+        np.exp(s, out=s)                # exp(s_ij - m_i)
+        l_sum = s.sum(axis=1)
+        lse[i0:i1] = m + np.log(l_sum)
+        s /= l_sum[:, None]             # p_ij
+        o[i0:i1] = s @ v
     return o, lse
 
 
@@ -110,17 +119,27 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, o: np.ndarray, ls
     subset of the queries (with their own O and LSE) gives exact dQ rows for them.
     """
     lq = q.shape[0]
-    dq = np.empty_like(q, dtype=np.float64)
-    dk = np.zeros_like(k, dtype=np.float64)
-    dv = np.zeros_like(v, dtype=np.float64)
+    nk = k.shape[0]
+    dq = np.empty((lq, k.shape[1]), dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
     dd = (do * o).sum(axis=1)
-    blk = _row_block(k.shape[0])
+    blk = _row_block(nk)
+    buf_p = np.empty((min(blk, lq), nk), dtype=np.float64)
+    buf_s = np.empty((min(blk, lq), nk), dtype=np.float64)
+    kt = np.ascontiguousarray(k.T)
+    vt = np.ascontiguousarray(v.T)
     for i0 in range(0, lq, blk):
         i1 = min(lq, i0 + blk)
-        s = head_scores(q[i0:i1], k, scale)
-        p = np.exp(s - lse[i0:i1, None])
-        dp = do[i0:i1] @ v.T
-        ds = p * (dp - dd[i0:i1, None])
+        p = buf_p[: i1 - i0]
+        np.matmul(q[i0:i1], kt, out=p)
+        p *= scale                      # s_ij
+        p -= lse[i0:i1, None]
+        np.exp(p, out=p)                # p_ij
+        ds = buf_s[: i1 - i0]
+        np.matmul(do[i0:i1], vt, out=ds)  # dp_ij
+        ds -= dd[i0:i1, None]
+        ds *= p                         # ds_ij
         dq[i0:i1] = scale * (ds @ k)
         dk += scale * (ds.T @ q[i0:i1])
         dv += p.T @ do[i0:i1]
