@@ -1,0 +1,253 @@
+"""Coalesced varlen attention for MI355X: thin Python binding of ``libzl.so``.
+
+The library runs one GPU's share of a mixed image-video DiT batch (the "Coalesced
+Attention Engine" of the Zellige page, §IV-D): whole sequences, Ulysses head subsets
+and ring KV-split parts in one persistent launch each for forward and backward, plus
+the exact LSE merge of ring parts. This module only marshals arguments: every step of
+the computation runs in the HIP kernels behind the C ABI of ``include/zl.h``. PyTorch
+provides device memory and the current stream.
+
+If ``libzl.so`` is missing, importing this package raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+__all__ = ["Plan", "ZlError", "attn_fwd", "attn_bwd", "lse_merge", "merge_groups", "lib_path", "SEGMENT_FIELDS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libzl.so")
+
+ZL_PLAN_HOST_ONLY = 1
+SEGMENT_FIELDS = ("seq", "head_begin", "head_end", "q_begin", "q_end", "kv_begin", "kv_end", "part")
+
+
+class ZlError(RuntimeError):
+    """A libzl call returned a non-zero status; the message is zl_last_error()."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libzl status {status}: {message}")
+        self.status = status
+
+
+class _Segment(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in SEGMENT_FIELDS]
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [("ws_fwd", ctypes.c_size_t), ("ws_bwd", ctypes.c_size_t), ("q_rows", ctypes.c_int64),
+                ("kv_rows", ctypes.c_int64), ("part_rows", ctypes.c_int64), ("n_groups", ctypes.c_int32),
+                ("n_parts_max", ctypes.c_int32), ("fwd_tiles", ctypes.c_int64), ("bwd_tiles", ctypes.c_int64),
+                ("fwd_flops", ctypes.c_double), ("bwd_flops", ctypes.c_double), ("d_head", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class _GroupInfo(ctypes.Structure):
+    _fields_ = [("n_parts", ctypes.c_int32), ("seq", ctypes.c_int32), ("n_rows", ctypes.c_int64),
+                ("o_row", ctypes.c_int64), ("part_row", ctypes.c_int64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m coalesced_varlen_attention_amd.build` "
+                          "(there is no fallback path)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, U32, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
+    sig = {
+        "zl_plan_build": (I32, [I32, P, P, P, I32, P, I32, F32, U32, ctypes.POINTER(P)]),
+        "zl_plan_info": (I32, [P, ctypes.POINTER(_PlanInfo)]),
+        "zl_plan_group": (I32, [P, I32, ctypes.POINTER(_GroupInfo)]),
+        "zl_plan_tiles": (I32, [P, I32, P, I64, ctypes.POINTER(I64)]),
+        "zl_plan_destroy": (None, [P]),
+        "zl_attn_fwd": (I32, [P, P, P, P, P, P, P, P, P, P]),
+        "zl_lse_merge": (I32, [I32, I64, I32, P, P, P, P, P]),
+        "zl_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, P]),
+        "zl_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise ZlError(status, _lib.zl_last_error().decode(errors="replace"))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class Plan:
+    """A validated, lowered segment list (``zl_plan_build``).
+
+    ``seq_q``/``seq_kv``: tokens per sequence; ``heads``: stored heads per sequence;
+    ``segments``: tuples ``(seq, head_begin, head_end, q_begin, q_end, kv_begin, kv_end, part)``.
+    """
+
+    def __init__(self, seq_q: Sequence[int], seq_kv: Sequence[int], heads: Sequence[int], segments, d: int,
+                 scale: Optional[float] = None, host_only: bool = False):
+        n = len(seq_q)
+        if len(seq_kv) != n or len(heads) != n:
+            raise ValueError("seq_q, seq_kv and heads must have the same length")
+        cu_q = (ctypes.c_int64 * (n + 1))()
+        cu_kv = (ctypes.c_int64 * (n + 1))()
+        for i in range(n):
+            cu_q[i + 1] = cu_q[i] + int(seq_q[i])
+            cu_kv[i + 1] = cu_kv[i] + int(seq_kv[i])
+        hs = (ctypes.c_int32 * n)(*[int(h) for h in heads])
+        segs = (_Segment * len(segments))()
+        for i, s in enumerate(segments):
+            for name, val in zip(SEGMENT_FIELDS, s):
+                setattr(segs[i], name, int(val))
+        self._h = ctypes.c_void_p()
+        flags = ZL_PLAN_HOST_ONLY if host_only else 0
+        _check(_lib.zl_plan_build(n, ctypes.cast(cu_q, ctypes.c_void_p), ctypes.cast(cu_kv, ctypes.c_void_p),
+                                  ctypes.cast(hs, ctypes.c_void_p), len(segments), ctypes.cast(segs, ctypes.c_void_p),
+                                  int(d), float(scale) if scale else 0.0, flags, ctypes.byref(self._h)))
+        info = _PlanInfo()
+        _check(_lib.zl_plan_info(self._h, ctypes.byref(info)))
+        self.info = {name: getattr(info, name) for name, _ in _PlanInfo._fields_}
+        self.d = int(d)
+        self.groups: List[dict] = []
+        for g in range(info.n_groups):
+            gi = _GroupInfo()
+            _check(_lib.zl_plan_group(self._h, g, ctypes.byref(gi)))
+            self.groups.append({name: getattr(gi, name) for name, _ in _GroupInfo._fields_})
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    def tiles(self, which: int) -> List[Tuple[int, int, int, int]]:
+        """Work queue items (segment, head, first row, rows): which=0 forward, 1 backward."""
+        cnt = ctypes.c_int64()
+        _check(_lib.zl_plan_tiles(self._h, which, None, 0, ctypes.byref(cnt)))
+        buf = (ctypes.c_int32 * (4 * cnt.value))()
+        _check(_lib.zl_plan_tiles(self._h, which, ctypes.cast(buf, ctypes.c_void_p), cnt.value, ctypes.byref(cnt)))
+        return [tuple(buf[4 * i:4 * i + 4]) for i in range(cnt.value)]
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) and self._h.value:
+            _lib.zl_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _check_tensor(t, name, dtype, rows, d, device):
+    import torch
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != rows * d:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {rows} x {d}")
+
+
+def attn_fwd(plan: Plan, q, k, v, o=None, lse=None, o_part=None, lse_part=None, workspace=None, stream=None):
+    """Forward of every segment of ``plan`` in one launch (``zl_attn_fwd``).
+
+    Returns ``(o, lse, o_part, lse_part)``; buffers not given are allocated with
+    ``torch.empty`` on ``q``'s device (rows no segment covers are left as allocated).
+    Ring groups still need ``merge_groups`` (or ``lse_merge``) to produce their final rows.
+    """
+    import torch
+    info, d, dev = plan.info, plan.d, q.device
+    _check_tensor(q, "q", torch.bfloat16, info["q_rows"], d, dev)
+    _check_tensor(k, "k", torch.bfloat16, info["kv_rows"], d, dev)
+    _check_tensor(v, "v", torch.bfloat16, info["kv_rows"], d, dev)
+    if o is None:
+        o = torch.empty(info["q_rows"], d, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(info["q_rows"], dtype=torch.float32, device=dev)
+    if info["n_groups"] > 0:
+        if o_part is None:
+            o_part = torch.empty(info["part_rows"], d, dtype=torch.float32, device=dev)
+        if lse_part is None:
+            lse_part = torch.empty(info["part_rows"], dtype=torch.float32, device=dev)
+        _check_tensor(o_part, "o_part", torch.float32, info["part_rows"], d, dev)
+        _check_tensor(lse_part, "lse_part", torch.float32, info["part_rows"], 1, dev)
+    _check_tensor(o, "o", torch.float32, info["q_rows"], d, dev)
+    _check_tensor(lse, "lse", torch.float32, info["q_rows"], 1, dev)
+    if workspace is None:
+        workspace = torch.empty(info["ws_fwd"], dtype=torch.uint8, device=dev)
+    if workspace.numel() < info["ws_fwd"]:
+        raise ValueError("workspace too small")
+    _check(_lib.zl_attn_fwd(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            _ptr(o_part), _ptr(lse_part), workspace.data_ptr(), _stream_handle(stream)))
+    return o, lse, o_part, lse_part
+
+
+def lse_merge(n_parts: int, n_rows: int, d: int, o_part, lse_part, o, lse, stream=None) -> None:
+    """Exact merge of ring partials (``zl_lse_merge``) on raw tensors or views.
+
+    ``o_part``: ``n_parts*n_rows*d`` floats, ``lse_part``: ``n_parts*n_rows``; results to
+    ``o`` (``n_rows*d``) and ``lse`` (``n_rows``). Views must be contiguous.
+    """
+    for t, n in ((o_part, n_parts * n_rows * d), (lse_part, n_parts * n_rows), (o, n_rows * d), (lse, n_rows)):
+        if not t.is_contiguous() or t.numel() < n:
+            raise ValueError("lse_merge: tensor too small or not contiguous")
+    _check(_lib.zl_lse_merge(int(n_parts), int(n_rows), int(d), o_part.data_ptr(), lse_part.data_ptr(),
+                             o.data_ptr(), lse.data_ptr(), _stream_handle(stream)))
+
+
+def merge_groups(plan: Plan, o_part, lse_part, o, lse, stream=None) -> None:
+    """Merge every ring group of ``plan`` into its final rows of ``o`` and ``lse``."""
+    d = plan.d
+    for g in plan.groups:
+        r0, n, p0, np_ = g["o_row"], g["n_rows"], g["part_row"], g["n_parts"]
+        lse_merge(np_, n, d, o_part[p0:p0 + np_ * n], lse_part[p0:p0 + np_ * n], o[r0:r0 + n], lse[r0:r0 + n],
+                  stream)
+
+
+def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward of every segment of ``plan`` (``zl_attn_bwd``): returns ``(dq, dk, dv)``."""
+    import torch
+    info, d, dev = plan.info, plan.d, q.device
+    _check_tensor(q, "q", torch.bfloat16, info["q_rows"], d, dev)
+    _check_tensor(k, "k", torch.bfloat16, info["kv_rows"], d, dev)
+    _check_tensor(v, "v", torch.bfloat16, info["kv_rows"], d, dev)
+    _check_tensor(do, "do", torch.bfloat16, info["q_rows"], d, dev)
+    _check_tensor(o, "o", torch.float32, info["q_rows"], d, dev)
+    _check_tensor(lse, "lse", torch.float32, info["q_rows"], 1, dev)
+    if dq is None:
+        dq = torch.empty(info["q_rows"], d, dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty(info["kv_rows"], d, dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty(info["kv_rows"], d, dtype=torch.float32, device=dev)
+    _check_tensor(dq, "dq", torch.float32, info["q_rows"], d, dev)
+    _check_tensor(dk, "dk", torch.float32, info["kv_rows"], d, dev)
+    _check_tensor(dv, "dv", torch.float32, info["kv_rows"], d, dev)
+    if workspace is None:
+        workspace = torch.empty(info["ws_bwd"], dtype=torch.uint8, device=dev)
+    if workspace.numel() < info["ws_bwd"]:
+        raise ValueError("workspace too small")
+    _check(_lib.zl_attn_bwd(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                            _stream_handle(stream)))
+    return dq, dk, dv

@@ -1,0 +1,190 @@
+// C ABI entry points: argument checks, workspace layout and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <string>
+
+#include "zl_internal.h"
+
+namespace zl {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+}  // namespace zl
+
+namespace {
+
+zl_status fail(zl_status st, const std::string& msg) {
+  zl::set_error(msg);
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr size_t kCounterBytes = 256;
+
+zl_status check_runnable(const zl_plan* plan, const char* who) {
+  if (!plan) return fail(ZL_ERR_INVALID, std::string(who) + ": plan is NULL");
+  if (!plan->dev_block) return fail(ZL_ERR_INVALID, std::string(who) + ": plan was built host-only and cannot run");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(ZL_ERR_HIP, std::string(who) + ": hipGetDevice failed");
+  if (dev != plan->device)
+    return fail(ZL_ERR_INVALID, std::string(who) + ": current device " + std::to_string(dev) +
+                                    " is not the plan's device " + std::to_string(plan->device));
+  return ZL_OK;
+}
+
+bool has_final(const zl_plan* plan) {
+  for (const auto& s : plan->segs)
+    if (s.part < 0) return true;
+  return false;
+}
+
+zl_status launch_status(int rc, const char* who) {
+  if (rc != 0) {
+    hipError_t e = hipGetLastError();
+    return fail(ZL_ERR_HIP, std::string(who) + ": kernel launch failed: " + hipGetErrorString(e));
+  }
+  return ZL_OK;
+}
+
+}  // namespace
+
+extern "C" const char* zl_last_error(void) { return zl::g_last_error.c_str(); }
+
+extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
+  if (!plan || !info) return fail(ZL_ERR_INVALID, "zl_plan_info: NULL argument");
+  std::memset(info, 0, sizeof(*info));
+  info->ws_fwd = kCounterBytes;
+  info->ws_bwd = kCounterBytes + align256((size_t)plan->q_rows * sizeof(float));
+  info->q_rows = plan->q_rows;
+  info->kv_rows = plan->kv_rows;
+  info->part_rows = plan->part_rows;
+  info->n_groups = (int32_t)plan->groups.size();
+  info->n_parts_max = plan->n_parts_max;
+  info->fwd_tiles = (int64_t)plan->fwd_tiles.size();
+  info->bwd_tiles = (int64_t)plan->bwd_tiles.size();
+  info->fwd_flops = plan->fwd_flops;
+  info->bwd_flops = 2.5 * plan->fwd_flops;
+  info->d_head = plan->d;
+  info->softmax_scale = plan->scale;
+  return ZL_OK;
+}
+
+extern "C" zl_status zl_plan_group(const zl_plan* plan, int32_t g, zl_group_info_t* info) {
+  if (!plan || !info) return fail(ZL_ERR_INVALID, "zl_plan_group: NULL argument");
+  if (g < 0 || g >= (int32_t)plan->groups.size())
+    return fail(ZL_ERR_INVALID, "zl_plan_group: group " + std::to_string(g) + " out of range");
+  *info = plan->groups[g];
+  return ZL_OK;
+}
+
+extern "C" zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* out, int64_t cap, int64_t* count) {
+  if (!plan || !count) return fail(ZL_ERR_INVALID, "zl_plan_tiles: NULL argument");
+  if (which != 0 && which != 1) return fail(ZL_ERR_INVALID, "zl_plan_tiles: which must be 0 or 1");
+  const auto& v = which == 0 ? plan->fwd_tiles : plan->bwd_tiles;
+  *count = (int64_t)v.size();
+  if (cap < 0) return fail(ZL_ERR_INVALID, "zl_plan_tiles: negative capacity");
+  if (cap > 0 && !out) return fail(ZL_ERR_INVALID, "zl_plan_tiles: out is NULL");
+  const int64_t n = std::min<int64_t>(cap, (int64_t)v.size());
+  for (int64_t i = 0; i < n; ++i) {
+    out[4 * i + 0] = v[i].seg;
+    out[4 * i + 1] = v[i].head;
+    out[4 * i + 2] = v[i].row0;
+    out[4 * i + 3] = v[i].nrows;
+  }
+  return ZL_OK;
+}
+
+extern "C" zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void* k, const void* v, float* o,
+                                 float* lse, float* o_part, float* lse_part, void* workspace, void* stream) {
+  zl_status st = check_runnable(plan, "zl_attn_fwd");
+  if (st != ZL_OK) return st;
+  if (!q || !k || !v) return fail(ZL_ERR_INVALID, "zl_attn_fwd: q, k or v is NULL");
+  if (!workspace) return fail(ZL_ERR_INVALID, "zl_attn_fwd: workspace is NULL");
+  if (has_final(plan) && (!o || !lse)) return fail(ZL_ERR_INVALID, "zl_attn_fwd: o or lse is NULL");
+  if (!plan->groups.empty() && (!o_part || !lse_part))
+    return fail(ZL_ERR_INVALID, "zl_attn_fwd: the plan has ring groups but o_part or lse_part is NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(o_part, 16) ||
+      !aligned(workspace, 16) || !aligned(lse, 4) || !aligned(lse_part, 4))
+    return fail(ZL_ERR_INVALID, "zl_attn_fwd: q/k/v/o/o_part/workspace must be 16-byte aligned, lse 4-byte");
+  zl::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.segs = plan->d_segs;
+  p.tiles = plan->d_fwd;
+  p.n_tiles = (int32_t)plan->fwd_tiles.size();
+  p.counter = (int32_t*)workspace;
+  p.scale_log2 = plan->scale * 1.4426950408889634f;
+  const int per_cu = zl::fwd_blocks_per_cu(plan->d);
+  if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_fwd: forward kernel cannot be resident");
+  const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, p.n_tiles);
+  return launch_status(zl::launch_fwd(plan->d, p, grid, stream), "zl_attn_fwd");
+}
+
+extern "C" zl_status zl_lse_merge(int32_t n_parts, int64_t n_rows, int32_t d_head, const float* o_part,
+                                  const float* lse_part, float* o, float* lse, void* stream) {
+  if (d_head != 64 && d_head != 128)
+    return fail(ZL_ERR_UNSUPPORTED, "zl_lse_merge: d_head " + std::to_string(d_head) + " is not 64 or 128");
+  if (n_parts < 1) return fail(ZL_ERR_INVALID, "zl_lse_merge: n_parts must be >= 1");
+  if (n_rows < 0) return fail(ZL_ERR_INVALID, "zl_lse_merge: n_rows must be >= 0");
+  if (n_rows == 0) return ZL_OK;
+  if (!o_part || !lse_part || !o || !lse) return fail(ZL_ERR_INVALID, "zl_lse_merge: NULL pointer");
+  if (!aligned(o_part, 16) || !aligned(o, 16) || !aligned(lse_part, 4) || !aligned(lse, 4))
+    return fail(ZL_ERR_INVALID, "zl_lse_merge: o_part and o must be 16-byte aligned, lse 4-byte");
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    return fail(ZL_ERR_HIP, "zl_lse_merge: cannot query the device");
+  const int rows_per_block = 256 / (d_head / 4);
+  const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
+  const int grid = (int)std::min<int64_t>(blocks, (int64_t)n_cu * 16);
+  return launch_status(zl::launch_merge(d_head, n_parts, n_rows, o_part, lse_part, o, lse, grid, stream),
+                       "zl_lse_merge");
+}
+
+extern "C" zl_status zl_attn_bwd(const zl_plan* plan, const void* q, const void* k, const void* v, const float* o,
+                                 const float* lse, const void* d_o, float* dq, float* dk, float* dv, void* workspace,
+                                 void* stream) {
+  zl_status st = check_runnable(plan, "zl_attn_bwd");
+  if (st != ZL_OK) return st;
+  if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv || !workspace)
+    return fail(ZL_ERR_INVALID, "zl_attn_bwd: NULL pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(d_o, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16) || !aligned(lse, 4))
+    return fail(ZL_ERR_INVALID, "zl_attn_bwd: tensors and workspace must be 16-byte aligned, lse 4-byte");
+  zl::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.d_o = d_o;
+  p.o = o;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.counter = (int32_t*)workspace;
+  p.dvec = (float*)((char*)workspace + kCounterBytes);
+  p.segs = plan->d_segs;
+  p.tiles = plan->d_bwd;
+  p.n_tiles = (int32_t)plan->bwd_tiles.size();
+  p.pre_tiles = plan->d_pre;
+  p.n_pre = (int32_t)plan->pre_tiles.size();
+  p.scale = plan->scale;
+  p.scale_log2 = plan->scale * 1.4426950408889634f;
+  const int per_cu = zl::bwd_blocks_per_cu(plan->d);
+  if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_bwd: backward kernel cannot be resident");
+  const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, p.n_tiles);
+  const int grid_pre = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)plan->n_cu * 8, p.n_pre));
+  return launch_status(zl::launch_bwd(plan->d, p, grid_pre, grid, stream), "zl_attn_bwd");
+}

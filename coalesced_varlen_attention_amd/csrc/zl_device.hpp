@@ -1,0 +1,64 @@
+// Device-side building blocks for gfx950 (CDNA4): bf16 MFMA tiles, transposed LDS reads,
+// lane-half exchange and bf16 rounding.
+//
+// Lane layouts used throughout (wave of 64 lanes, l = lane, i = element):
+//   v_mfma_f32_32x32x16_bf16  A[m][k]: m = l%32, k = 8*(l/32) + i (i < 8)
+//                             B[k][n]: n = l%32, k = 8*(l/32) + i
+//                             C[m][n]: n = l%32, m = 8*(i/4) + 4*(l/32) + i%4 (i < 16)
+//   ds_read_b64_tr_b16        within each group of 16 lanes, lane r supplies the address of
+//                             4 consecutive 16-bit values (row r of a 16x4 matrix S); lane i
+//                             receives S[4k + i/4][i%4] for k = 0..3. Pointing the 16 lanes at
+//                             a 4-row x 16-column block (lane r -> row r/4, columns 4*(r%4)..)
+//                             hands lane i the 4 rows of column i: a transposed load.
+//   v_permlane32_swap         swaps the upper half of one register with the lower half of
+//                             another; applied to (x, x) it yields both halves' values in
+//                             every lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zl {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#define ZL_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed read of four 16-bit values from LDS (see the layout note above).
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ZL_LDS i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Round-to-nearest-even conversion of 8 floats to bf16.
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+
+// max / sum of a value over lane l and lane l^32.
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace zl

@@ -1,0 +1,107 @@
+// Internal declarations shared by the host runtime (plan, API) and the HIP kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "zl.h"
+
+namespace zl {
+
+// Forward queue item: 128 query rows of one (segment, head). Backward queue item: 128 key
+// rows of one (segment, head), looping over the segment's query rows in blocks of 64.
+constexpr int kFwdRows = 128;
+constexpr int kBwdKeys = 128;
+constexpr int kBwdRows = 64;
+// Rows (token, head pairs) per item of the backward pre-pass.
+constexpr int kPreRows = 256;
+
+// A segment as the kernels see it. Rows are (token, head) pairs of d contiguous values.
+struct alignas(16) SegDev {
+  int64_t q_row0;     // query-side row of (token 0, head 0) of the segment's sequence
+  int64_t kv_row0;    // key-side row of (token 0, head 0)
+  int64_t part_row0;  // slab row of (token q_begin, head 0) for a ring part, else -1
+  int32_t nh;         // stored heads of the sequence (row stride between tokens = nh rows)
+  int32_t q_begin, q_end, kv_begin, kv_end;
+  int32_t head_begin, head_end;
+  int32_t part;
+  int32_t pad[2];
+};
+static_assert(sizeof(SegDev) == 64, "SegDev must stay 64 bytes");
+
+// One work item: segment index, head, first row (token) of the block, rows in the block.
+struct alignas(16) Tile {
+  int32_t seg, head, row0, nrows;
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  float* o_part;
+  float* lse_part;
+  const SegDev* segs;
+  const Tile* tiles;
+  int32_t n_tiles;
+  int32_t* counter;
+  float scale_log2;  // softmax scale times log2(e)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* d_o;
+  const float* o;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dvec;  // per query row: sum_c dO * O (workspace)
+  const SegDev* segs;
+  const Tile* tiles;
+  int32_t n_tiles;
+  const Tile* pre_tiles;  // (segment, head_begin, first token, tokens) per pre-pass item
+  int32_t n_pre;
+  int32_t* counter;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale times log2(e)
+};
+
+// Kernel launchers (defined next to their kernels). They return the launch status.
+int launch_fwd(int d, const FwdParams& p, int grid, void* stream);
+int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, void* stream);
+int launch_merge(int d, int32_t n_parts, int64_t n_rows, const float* o_part, const float* lse_part,
+                 float* o, float* lse, int grid, void* stream);
+// Workgroups of each persistent kernel that fit on one compute unit.
+int fwd_blocks_per_cu(int d);
+int bwd_blocks_per_cu(int d);
+
+void set_error(const std::string& msg);
+
+}  // namespace zl
+
+struct zl_plan {
+  int32_t d = 0;
+  int32_t n_seq = 0;
+  float scale = 0.f;
+  uint32_t flags = 0;
+  int device = -1;
+  int n_cu = 0;
+  int64_t q_rows = 0, kv_rows = 0, part_rows = 0;
+  int32_t n_parts_max = 0;
+  double fwd_flops = 0.0;
+  std::vector<zl::SegDev> segs;
+  std::vector<zl::Tile> fwd_tiles, bwd_tiles, pre_tiles;
+  std::vector<zl_group_info_t> groups;
+  // device copies (one allocation, carved into the three tables)
+  void* dev_block = nullptr;
+  const zl::SegDev* d_segs = nullptr;
+  const zl::Tile* d_fwd = nullptr;
+  const zl::Tile* d_bwd = nullptr;
+  const zl::Tile* d_pre = nullptr;
+};

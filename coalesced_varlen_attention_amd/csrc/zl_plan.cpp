@@ -1,0 +1,306 @@
+// Plan building: validation of the segment list and its lowering into device work queues.
+//
+// This is the rank-local lowering of the Zellige page (Moldable Sequence Placement for
+// Mixed Image-Video DiT Training, §IV-D "Coalesced Attention Engine"): the segments one GPU
+// holds (whole sequences, Ulysses head shards, ring KV-split parts; the (q,h,k) axes of
+// §IV-A / Table II) become one list of equal-shaped work items for one persistent launch,
+// without mixing attention across sequences. The pages order work by decreasing split
+// degree and pack fillers by decreasing price (§IV-C, Filler Packing); here the single GPU
+// has no collectives to order, so items are ordered by decreasing cost (rows x length of
+// the other side, the quadratic attention cost of §II-A) to keep the persistent workgroups
+// busy until the end, with ties left in (segment, head, block) order so that items sharing
+// K/V run side by side.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdio>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <new>
+#include <tuple>
+
+#include "zl_internal.h"
+
+namespace {
+
+zl_status fail(zl_status st, const std::string& msg) {
+  zl::set_error(msg);
+  return st;
+}
+
+std::string seg_str(int i, const zl_segment& s) {
+  char buf[200];
+  snprintf(buf, sizeof(buf), "segment %d {seq %d, heads [%d,%d), q [%d,%d), kv [%d,%d), part %d}", i, s.seq,
+           s.head_begin, s.head_end, s.q_begin, s.q_end, s.kv_begin, s.kv_end, s.part);
+  return buf;
+}
+
+struct Rect {  // a block of rows of one sequence: tokens [t0,t1) x heads [h0,h1)
+  int32_t t0, t1, h0, h1;
+  int32_t owner;  // segment index (or group id for grouped outputs)
+  int32_t group;  // group id, -1 for a final segment
+};
+
+bool overlap(const Rect& a, const Rect& b) {
+  return a.t0 < b.t1 && b.t0 < a.t1 && a.h0 < b.h1 && b.h0 < a.h1;
+}
+
+// Reports the first pair of overlapping rectangles (ignoring pairs in the same group).
+bool find_overlap(std::vector<Rect>& rs, bool same_group_ok, int* a, int* b) {
+  std::sort(rs.begin(), rs.end(), [](const Rect& x, const Rect& y) { return x.t0 < y.t0; });
+  for (size_t i = 0; i < rs.size(); ++i) {
+    for (size_t j = i + 1; j < rs.size() && rs[j].t0 < rs[i].t1; ++j) {
+      if (same_group_ok && rs[i].group >= 0 && rs[i].group == rs[j].group) continue;
+      if (overlap(rs[i], rs[j])) {
+        *a = rs[i].owner;
+        *b = rs[j].owner;
+        return true;
+      }
+    }
+  }
+  return false;
+}
+
+}  // namespace
+
+extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int64_t* cu_kv,
+                                   const int32_t* seq_heads, int32_t n_seg, const zl_segment* segs,
+                                   int32_t d_head, float softmax_scale, uint32_t flags, zl_plan** out) {
+  if (!out) return fail(ZL_ERR_INVALID, "zl_plan_build: out is NULL");
+  *out = nullptr;
+  if (d_head != 64 && d_head != 128)
+    return fail(ZL_ERR_UNSUPPORTED, "zl_plan_build: d_head " + std::to_string(d_head) + " is not 64 or 128");
+  if (flags & ~ZL_PLAN_HOST_ONLY) return fail(ZL_ERR_INVALID, "zl_plan_build: unknown flag bits");
+  if (n_seq < 1) return fail(ZL_ERR_INVALID, "zl_plan_build: n_seq must be >= 1");
+  if (!cu_q || !cu_kv || !seq_heads) return fail(ZL_ERR_INVALID, "zl_plan_build: NULL sequence array");
+  if (n_seg < 1 || !segs) return fail(ZL_ERR_INVALID, "zl_plan_build: need at least one segment");
+  if (!std::isfinite(softmax_scale)) return fail(ZL_ERR_INVALID, "zl_plan_build: softmax_scale is not finite");
+  if (cu_q[0] != 0 || cu_kv[0] != 0) return fail(ZL_ERR_INVALID, "zl_plan_build: cu_seqlens[0] must be 0");
+
+  auto plan = new (std::nothrow) zl_plan();
+  if (!plan) return fail(ZL_ERR_NOMEM, "zl_plan_build: out of host memory");
+  std::unique_ptr<zl_plan> guard(plan);
+  plan->d = d_head;
+  plan->n_seq = n_seq;
+  plan->flags = flags;
+  plan->scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_head);
+
+  std::vector<int64_t> lq(n_seq), lkv(n_seq), qoff(n_seq + 1, 0), kvoff(n_seq + 1, 0);
+  for (int s = 0; s < n_seq; ++s) {
+    lq[s] = cu_q[s + 1] - cu_q[s];
+    lkv[s] = cu_kv[s + 1] - cu_kv[s];
+    if (lq[s] < 0 || lkv[s] < 0)
+      return fail(ZL_ERR_INVALID, "zl_plan_build: cu_seqlens decreases at sequence " + std::to_string(s));
+    if (lq[s] > INT32_MAX || lkv[s] > INT32_MAX)
+      return fail(ZL_ERR_INVALID, "zl_plan_build: sequence " + std::to_string(s) + " is longer than 2^31-1 tokens");
+    if (seq_heads[s] < 1)
+      return fail(ZL_ERR_INVALID, "zl_plan_build: seq_heads[" + std::to_string(s) + "] must be >= 1");
+    qoff[s + 1] = qoff[s] + lq[s] * seq_heads[s];
+    kvoff[s + 1] = kvoff[s] + lkv[s] * seq_heads[s];
+    if (qoff[s + 1] > (INT64_C(1) << 48) || kvoff[s + 1] > (INT64_C(1) << 48))
+      return fail(ZL_ERR_INVALID, "zl_plan_build: packed row count too large");
+  }
+  plan->q_rows = qoff[n_seq];
+  plan->kv_rows = kvoff[n_seq];
+
+  // Segment checks and ring groups (keyed by sequence, query range and head range).
+  std::map<std::tuple<int, int, int, int, int>, int> group_of;
+  std::vector<std::vector<int>> group_members;
+  std::vector<int> seg_group(n_seg, -1);
+  for (int i = 0; i < n_seg; ++i) {
+    const zl_segment& g = segs[i];
+    if (g.seq < 0 || g.seq >= n_seq) return fail(ZL_ERR_INVALID, "zl_plan_build: " + seg_str(i, g) + ": no such sequence");
+    const int nh = seq_heads[g.seq];
+    if (g.head_begin < 0 || g.head_begin >= g.head_end || g.head_end > nh)
+      return fail(ZL_ERR_INVALID, "zl_plan_build: " + seg_str(i, g) + ": head range outside [0," + std::to_string(nh) + ") or empty");
+    if (g.q_begin < 0 || g.q_begin >= g.q_end || g.q_end > lq[g.seq])
+      return fail(ZL_ERR_INVALID, "zl_plan_build: " + seg_str(i, g) + ": query range outside [0," + std::to_string(lq[g.seq]) + ") or empty");
+    if (g.kv_begin < 0 || g.kv_begin >= g.kv_end || g.kv_end > lkv[g.seq])
+      return fail(ZL_ERR_INVALID, "zl_plan_build: " + seg_str(i, g) + ": key range outside [0," + std::to_string(lkv[g.seq]) + ") or empty");
+    if (g.part < -1) return fail(ZL_ERR_INVALID, "zl_plan_build: " + seg_str(i, g) + ": part must be >= -1");
+    if (g.part >= 0) {
+      auto key = std::make_tuple(g.seq, g.q_begin, g.q_end, g.head_begin, g.head_end);
+      auto it = group_of.find(key);
+      int gid;
+      if (it == group_of.end()) {
+        gid = (int)group_members.size();
+        group_of[key] = gid;
+        group_members.emplace_back();
+      } else {
+        gid = it->second;
+      }
+      group_members[gid].push_back(i);
+      seg_group[i] = gid;
+    }
+  }
+  const int n_groups = (int)group_members.size();
+  std::vector<int> part_segment_base(n_groups, 0);
+  for (int gid = 0; gid < n_groups; ++gid) {
+    auto& mem = group_members[gid];
+    const zl_segment& f = segs[mem[0]];
+    if (f.head_begin != 0 || f.head_end != seq_heads[f.seq])
+      return fail(ZL_ERR_INVALID, "zl_plan_build: " + seg_str(mem[0], f) +
+                                      ": a ring group must cover every stored head of its sequence");
+    std::vector<int> seen(mem.size(), -1);
+    for (int i : mem) {
+      const int p = segs[i].part;
+      if (p >= (int)mem.size() || seen[p] >= 0)
+        return fail(ZL_ERR_INVALID, "zl_plan_build: " + seg_str(i, segs[i]) + ": ring parts of a group must be numbered 0.." +
+                                        std::to_string(mem.size() - 1) + " once each");
+      seen[p] = i;
+    }
+    std::vector<int> by_kv(mem);
+    std::sort(by_kv.begin(), by_kv.end(), [&](int a, int b) { return segs[a].kv_begin < segs[b].kv_begin; });
+    for (size_t j = 1; j < by_kv.size(); ++j)
+      if (segs[by_kv[j]].kv_begin < segs[by_kv[j - 1]].kv_end)
+        return fail(ZL_ERR_INVALID, "zl_plan_build: " + seg_str(by_kv[j], segs[by_kv[j]]) + " and " +
+                                        seg_str(by_kv[j - 1], segs[by_kv[j - 1]]) + ": ring parts share key rows");
+    plan->n_parts_max = std::max<int32_t>(plan->n_parts_max, (int32_t)mem.size());
+  }
+
+  // No two writers of the same O rows; no two owners of the same K/V rows (outside a group).
+  {
+    std::vector<std::vector<Rect>> outs(n_seq), kvs(n_seq);
+    std::vector<char> group_done(n_groups, 0);
+    for (int i = 0; i < n_seg; ++i) {
+      const zl_segment& g = segs[i];
+      kvs[g.seq].push_back({g.kv_begin, g.kv_end, g.head_begin, g.head_end, i, seg_group[i]});
+      if (seg_group[i] >= 0) {
+        if (group_done[seg_group[i]]) continue;
+        group_done[seg_group[i]] = 1;
+      }
+      outs[g.seq].push_back({g.q_begin, g.q_end, g.head_begin, g.head_end, i, seg_group[i]});
+    }
+    for (int s = 0; s < n_seq; ++s) {
+      int a, b;
+      if (find_overlap(outs[s], false, &a, &b))
+        return fail(ZL_ERR_INVALID, "zl_plan_build: " + seg_str(a, segs[a]) + " and " + seg_str(b, segs[b]) +
+                                        " write the same output rows");
+      if (find_overlap(kvs[s], true, &a, &b))
+        return fail(ZL_ERR_INVALID, "zl_plan_build: " + seg_str(a, segs[a]) + " and " + seg_str(b, segs[b]) +
+                                        " own the same K/V rows (their dK/dV would collide)");
+    }
+  }
+
+  // Group slab layout.
+  plan->groups.resize(n_groups);
+  int64_t slab = 0;
+  for (int gid = 0; gid < n_groups; ++gid) {
+    const zl_segment& f = segs[group_members[gid][0]];
+    zl_group_info_t& gi = plan->groups[gid];
+    gi.n_parts = (int32_t)group_members[gid].size();
+    gi.seq = f.seq;
+    gi.n_rows = (int64_t)(f.q_end - f.q_begin) * seq_heads[f.seq];
+    gi.o_row = qoff[f.seq] + (int64_t)f.q_begin * seq_heads[f.seq];
+    gi.part_row = slab;
+    slab += gi.n_rows * gi.n_parts;
+  }
+  plan->part_rows = slab;
+
+  // Device segment table.
+  plan->segs.resize(n_seg);
+  for (int i = 0; i < n_seg; ++i) {
+    const zl_segment& g = segs[i];
+    zl::SegDev& d = plan->segs[i];
+    std::memset(&d, 0, sizeof(d));
+    d.q_row0 = qoff[g.seq];
+    d.kv_row0 = kvoff[g.seq];
+    d.nh = seq_heads[g.seq];
+    d.q_begin = g.q_begin;
+    d.q_end = g.q_end;
+    d.kv_begin = g.kv_begin;
+    d.kv_end = g.kv_end;
+    d.head_begin = g.head_begin;
+    d.head_end = g.head_end;
+    d.part = g.part;
+    d.part_row0 = -1;
+    if (g.part >= 0) {
+      const zl_group_info_t& gi = plan->groups[seg_group[i]];
+      d.part_row0 = gi.part_row + (int64_t)g.part * gi.n_rows;
+    }
+    plan->fwd_flops += 4.0 * (double)(g.q_end - g.q_begin) * (double)(g.kv_end - g.kv_begin) * (double)d_head *
+                       (double)(g.head_end - g.head_begin);
+  }
+
+  // Work queues, sorted by decreasing cost with a stable tie order.
+  struct Item {
+    zl::Tile t;
+    int64_t cost;
+  };
+  std::vector<Item> fwd, bwd;
+  for (int i = 0; i < n_seg; ++i) {
+    const zl_segment& g = segs[i];
+    const int64_t nq = g.q_end - g.q_begin, nk = g.kv_end - g.kv_begin;
+    for (int h = g.head_begin; h < g.head_end; ++h) {
+      for (int64_t r = g.q_begin; r < g.q_end; r += zl::kFwdRows) {
+        const int32_t n = (int32_t)std::min<int64_t>(zl::kFwdRows, g.q_end - r);
+        fwd.push_back({{i, h, (int32_t)r, n}, (int64_t)n * nk});
+      }
+      for (int64_t r = g.kv_begin; r < g.kv_end; r += zl::kBwdKeys) {
+        const int32_t n = (int32_t)std::min<int64_t>(zl::kBwdKeys, g.kv_end - r);
+        bwd.push_back({{i, h, (int32_t)r, n}, (int64_t)n * nq});
+      }
+    }
+    // Backward pre-pass rows: once per output row set (a ring group does it on part 0).
+    if (g.part <= 0) {
+      const int nhr = g.head_end - g.head_begin;
+      const int toks = std::max(1, zl::kPreRows / nhr);
+      for (int64_t t = g.q_begin; t < g.q_end; t += toks)
+        plan->pre_tiles.push_back({i, g.head_begin, (int32_t)t, (int32_t)std::min<int64_t>(toks, g.q_end - t)});
+    }
+  }
+  if (fwd.size() > (size_t)INT32_MAX || bwd.size() > (size_t)INT32_MAX || plan->pre_tiles.size() > (size_t)INT32_MAX)
+    return fail(ZL_ERR_INVALID, "zl_plan_build: too many work items");
+  auto by_cost = [](const Item& a, const Item& b) { return a.cost > b.cost; };
+  std::stable_sort(fwd.begin(), fwd.end(), by_cost);
+  std::stable_sort(bwd.begin(), bwd.end(), by_cost);
+  for (auto& it : fwd) plan->fwd_tiles.push_back(it.t);
+  for (auto& it : bwd) plan->bwd_tiles.push_back(it.t);
+
+  if (!(flags & ZL_PLAN_HOST_ONLY)) {
+    if (hipGetDevice(&plan->device) != hipSuccess) return fail(ZL_ERR_HIP, "zl_plan_build: hipGetDevice failed");
+    if (hipDeviceGetAttribute(&plan->n_cu, hipDeviceAttributeMultiprocessorCount, plan->device) != hipSuccess ||
+        plan->n_cu < 1)
+      return fail(ZL_ERR_HIP, "zl_plan_build: cannot query the compute unit count");
+    auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t b_segs = align(plan->segs.size() * sizeof(zl::SegDev));
+    const size_t b_fwd = align(plan->fwd_tiles.size() * sizeof(zl::Tile));
+    const size_t b_bwd = align(plan->bwd_tiles.size() * sizeof(zl::Tile));
+    const size_t b_pre = align(plan->pre_tiles.size() * sizeof(zl::Tile));
+    const size_t total = b_segs + b_fwd + b_bwd + b_pre;
+    if (hipMalloc(&plan->dev_block, total) != hipSuccess) {
+      plan->dev_block = nullptr;
+      (void)hipGetLastError();
+      return fail(ZL_ERR_NOMEM, "zl_plan_build: hipMalloc of " + std::to_string(total) + " bytes failed");
+    }
+    char* base = (char*)plan->dev_block;
+    plan->d_segs = (const zl::SegDev*)base;
+    plan->d_fwd = (const zl::Tile*)(base + b_segs);
+    plan->d_bwd = (const zl::Tile*)(base + b_segs + b_fwd);
+    plan->d_pre = (const zl::Tile*)(base + b_segs + b_fwd + b_bwd);
+    hipError_t e = hipSuccess;
+    e = hipMemcpy((void*)plan->d_segs, plan->segs.data(), plan->segs.size() * sizeof(zl::SegDev), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy((void*)plan->d_fwd, plan->fwd_tiles.data(), plan->fwd_tiles.size() * sizeof(zl::Tile), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy((void*)plan->d_bwd, plan->bwd_tiles.data(), plan->bwd_tiles.size() * sizeof(zl::Tile), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !plan->pre_tiles.empty())
+      e = hipMemcpy((void*)plan->d_pre, plan->pre_tiles.data(), plan->pre_tiles.size() * sizeof(zl::Tile), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(plan->dev_block);
+      plan->dev_block = nullptr;
+      return fail(ZL_ERR_HIP, std::string("zl_plan_build: upload failed: ") + hipGetErrorString(e));
+    }
+  }
+  *out = guard.release();
+  return ZL_OK;
+}
+
+extern "C" void zl_plan_destroy(zl_plan* plan) {
+  if (!plan) return;
+  if (plan->dev_block) (void)hipFree(plan->dev_block);
+  delete plan;
+}

@@ -1,0 +1,187 @@
+/*
+ * zl.h -- C ABI of the coalesced varlen attention library (libzl.so) for MI355X / gfx950.
+ *
+ * The library runs one GPU's share of a mixed image-video DiT batch: non-causal softmax
+ * attention, forward and backward, over a packed work list that mixes whole sequences,
+ * head subsets of long sequences and KV-split shards. It follows the "Coalesced Attention
+ * Engine" of the Zellige page (Moldable Sequence Placement for Mixed Image-Video DiT
+ * Training, §IV-D): a rank-local schedule is lowered into one launch that never mixes
+ * attention across sequences and writes every output at its input row, so outputs come
+ * back in rank-local input order. The q/h/kv ranges of a segment are the three axes of a
+ * placement option (§IV-A, Table II: all-gather (q,1,1), Ulysses (1,h,1), ring (1,1,k)).
+ *
+ * Data layout (all tensors owned by the caller, passed as raw device pointers):
+ *   Sequence s has Lq_s = cu_seqlens_q[s+1]-cu_seqlens_q[s] query tokens,
+ *   Lkv_s = cu_seqlens_kv[s+1]-cu_seqlens_kv[s] key/value tokens and nh_s = seq_heads[s]
+ *   stored heads. Its query-side rows are stored as [Lq_s][nh_s][d] and start at row
+ *   sum_{s'<s} Lq_s' * nh_s'; key-side rows likewise with Lkv. A "row" is one
+ *   (token, head) pair of d contiguous values. With one head count for every sequence this
+ *   is the usual packed varlen [T, H, d] layout.
+ *     Q, dO          bf16 [q_rows][d]          K, V       bf16 [kv_rows][d]
+ *     O, dQ          fp32 [q_rows][d]          dK, dV     fp32 [kv_rows][d]
+ *     LSE            fp32 [q_rows]             (natural-log log-sum-exp per row)
+ *
+ * Errors: every call returns a zl_status and never throws. A thread-local message for the
+ * last failure is available from zl_last_error(). Calls that take a stream enqueue work on
+ * it and return without synchronising: a fault on the device shows up at the caller's next
+ * synchronisation, not as a status.
+ */
+#ifndef ZL_H
+#define ZL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZL_OK = 0,
+  ZL_ERR_INVALID = -1,      /* bad argument: a range, a pointer, an overlap, a plan mismatch */
+  ZL_ERR_UNSUPPORTED = -2,  /* d_head other than 64 or 128 */
+  ZL_ERR_HIP = -3,          /* a HIP runtime call or kernel launch failed */
+  ZL_ERR_NOMEM = -4         /* host or device allocation failed */
+} zl_status;
+
+typedef struct zl_plan zl_plan; /* opaque; immutable after zl_plan_build, safe to share */
+
+/*
+ * One unit of rank-local work (§IV-D lowering; axes of §IV-A):
+ *   queries [q_begin, q_end) of sequence `seq` attend to its keys [kv_begin, kv_end),
+ *   for every stored head h in [head_begin, head_end).
+ * part == -1: the result is final and is written to O/LSE at the query rows.
+ * part >= 0: the segment is ring part `part` of a KV-split group. A group is the set of
+ *   segments with equal (seq, q range, head range); its parts must be numbered 0..n-1, have
+ *   disjoint key ranges, and cover every stored head of the sequence. Each part writes a
+ *   normalised partial O and its LSE to the partial slab (see zl_plan_group); the exact
+ *   merge is zl_lse_merge (ring attention accumulates the output block by block, §II-B).
+ * No two segments may write the same O rows, and no two may own the same K/V rows (their
+ * dK/dV would collide) unless they are parts of one group, whose key ranges are disjoint.
+ */
+typedef struct {
+  int32_t seq;
+  int32_t head_begin, head_end;
+  int32_t q_begin, q_end;
+  int32_t kv_begin, kv_end;
+  int32_t part;
+} zl_segment;
+
+typedef struct {
+  size_t ws_fwd;          /* workspace bytes zl_attn_fwd needs (device memory, 256-B aligned) */
+  size_t ws_bwd;          /* workspace bytes zl_attn_bwd needs */
+  int64_t q_rows;         /* packed query-side rows */
+  int64_t kv_rows;        /* packed key-side rows */
+  int64_t part_rows;      /* rows of the partial slab: o_part holds part_rows*d floats */
+  int32_t n_groups;       /* KV-split groups */
+  int32_t n_parts_max;    /* most parts in one group */
+  int64_t fwd_tiles;      /* work items of the forward queue */
+  int64_t bwd_tiles;      /* work items of the backward queue */
+  double fwd_flops;       /* sum over (segment, head) of 4*Lq*Lkv*d */
+  double bwd_flops;       /* 2.5 x fwd_flops */
+  int32_t d_head;
+  float softmax_scale;
+} zl_plan_info_t;
+
+typedef struct {
+  int32_t n_parts;        /* parts in the group */
+  int32_t seq;            /* its sequence */
+  int64_t n_rows;         /* rows of the group: (q_end-q_begin) * seq_heads[seq] */
+  int64_t o_row;          /* first row of the group in O and LSE (O elements start at o_row*d) */
+  int64_t part_row;       /* first slab row of part 0; part b starts at part_row + b*n_rows */
+} zl_group_info_t;
+
+/* Flags for zl_plan_build. */
+#define ZL_PLAN_HOST_ONLY 1u /* build and validate on the host only; no device tables, so the
+                                plan can be inspected but not run (used by CPU-only tests) */
+
+/*
+ * Validate the segment list and lower it into device work queues.
+ *   n_seq                 number of sequences (>= 1)
+ *   cu_seqlens_q/kv       host arrays of n_seq+1 token offsets, [0] == 0, non-decreasing;
+ *                         every sequence length must be below 2^31
+ *   seq_heads             host array of n_seq stored-head counts (>= 1)
+ *   n_seg, segs           host array of segments (see zl_segment), n_seg >= 1
+ *   d_head                64 or 128 (else ZL_ERR_UNSUPPORTED)
+ *   softmax_scale         tau in softmax(tau * Q K^T); <= 0 selects 1/sqrt(d_head)
+ *   flags                 0 or ZL_PLAN_HOST_ONLY
+ *   out                   receives the plan; the caller frees it with zl_plan_destroy
+ * The host arrays are copied; the plan owns its device tables (allocated on the current
+ * device) and nothing else. The forward queue holds one item per (segment, head, block of
+ * 128 query rows), the backward queue one per (segment, head, block of 128 key rows); each
+ * queue is sorted by decreasing cost (rows x length of the other side), ties kept in
+ * (segment, head, block) order.
+ */
+zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                        const int32_t* seq_heads, int32_t n_seg, const zl_segment* segs,
+                        int32_t d_head, float softmax_scale, uint32_t flags, zl_plan** out);
+
+/* Sizes and counts of a plan. */
+zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info);
+
+/* Layout of KV-split group g (0 <= g < n_groups), in the order of first appearance. */
+zl_status zl_plan_group(const zl_plan* plan, int32_t g, zl_group_info_t* info);
+
+/*
+ * Copy a work queue to the host for inspection: which = 0 forward, 1 backward.
+ * Each item is 4 int32: segment index, head, first row of the block, rows in the block.
+ * Writes min(cap, count) items to out (may be NULL when cap == 0); *count gets the total.
+ */
+zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* out, int64_t cap, int64_t* count);
+
+/* Free a plan and its device tables. NULL is ignored. */
+void zl_plan_destroy(zl_plan* plan);
+
+/*
+ * Forward (§IV-D coalesced call; §II-A attention). One persistent launch processes every
+ * segment of the plan:
+ *   q, k, v     bf16 device tensors in the packed layout
+ *   o, lse      fp32 outputs for part == -1 segments, written at their query rows
+ *   o_part,     fp32 partial slab, [part_rows][d] and [part_rows]; may be NULL only if the
+ *   lse_part    plan has no KV-split group
+ *   workspace   device memory of info.ws_fwd bytes, 256-B aligned, not shared with a
+ *               concurrent call (it holds the queue counter)
+ *   stream      hipStream_t, NULL for the default stream
+ * Rows that no segment covers are left untouched. Pointers must be 16-B aligned.
+ */
+zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void* k, const void* v,
+                      float* o, float* lse, float* o_part, float* lse_part,
+                      void* workspace, void* stream);
+
+/*
+ * Exact merge of n_parts normalised partial results over disjoint key blocks (ring
+ * accumulation, §II-B): for every row r,
+ *   LSE[r] = M + ln sum_b exp(lse_part[b][r] - M),  M = max_b lse_part[b][r]
+ *   O[r]   = sum_b exp(lse_part[b][r] - LSE[r]) * o_part[b][r]
+ * A part with lse = -inf has weight 0; a row whose parts are all -inf gets O = 0 and
+ * LSE = -inf.
+ *   o_part  fp32 [n_parts][n_rows][d_head]     lse_part  fp32 [n_parts][n_rows]
+ *   o       fp32 [n_rows][d_head] (output)     lse       fp32 [n_rows] (output)
+ * For a plan's group g, pass o_part + part_row*d, lse_part + part_row, o + o_row*d and
+ * lse + o_row from zl_plan_group. d_head is 64 or 128; pointers 16-B aligned.
+ */
+zl_status zl_lse_merge(int32_t n_parts, int64_t n_rows, int32_t d_head,
+                       const float* o_part, const float* lse_part, float* o, float* lse, void* stream);
+
+/*
+ * Backward (the exact backward of §V-A): gradients of f = sum over covered rows of
+ * dO . O with respect to Q, K and V, given the final (merged) O and LSE.
+ *   q, k, v, d_o   bf16 device tensors; o, lse the forward's final fp32 outputs
+ *   dq             fp32 [q_rows][d]: zeroed and accumulated here for every covered row;
+ *                  a KV-split group sums its parts
+ *   dk, dv         fp32 [kv_rows][d]: overwritten for every covered row
+ *   workspace      device memory of info.ws_bwd bytes (queue counter and row dot products)
+ * Rows that no segment covers are left untouched. Pointers must be 16-B aligned.
+ */
+zl_status zl_attn_bwd(const zl_plan* plan, const void* q, const void* k, const void* v,
+                      const float* o, const float* lse, const void* d_o,
+                      float* dq, float* dk, float* dv, void* workspace, void* stream);
+
+/* Thread-local message describing the last failure on this thread ("" if none). */
+const char* zl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZL_H */

@@ -1,0 +1,131 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI, run the oracle on
+the same seeded bf16 inputs, and compare.
+
+Tolerances (both must hold, per tensor, over every checked element): max-abs <= 2e-2 and
+relative L2 <= 5e-3, the bar the target sets for outputs and gradients.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+
+gpu_available = torch.cuda.is_available()
+requires_gpu = pytest.mark.skipif(not gpu_available, reason="needs a GPU")
+
+
+def zl():
+    import coalesced_varlen_attention_amd as z  # fails loudly if libzl.so is missing
+    return z
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def metrics(got: np.ndarray, ref: np.ndarray):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = got - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff) / den) if den > 0 else float(np.linalg.norm(diff))
+    return max_abs, rel
+
+
+def assert_close(name: str, got, ref, max_abs: float = MAX_ABS, rel_l2: float = REL_L2):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
+    assert np.isfinite(got).all(), f"{name}: non-finite values from the GPU"
+    ma, rl = metrics(got, ref)
+    print(f"  {name}: max-abs {ma:.3e}  rel-L2 {rl:.3e}  ({got.size} values)", flush=True)
+    assert ma <= max_abs and rl <= rel_l2, f"{name}: max-abs {ma:.3e} (<= {max_abs}), rel-L2 {rl:.3e} (<= {rel_l2})"
+    return ma, rl
+
+
+def make_plan(pack: W.Pack):
+    z = zl()
+    return z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale)
+
+
+def run_pack(pack: W.Pack, ins: dict, fill=float("nan")):
+    """Forward, ring merges and backward of a whole pack on cuda:0. Returns device tensors.
+
+    Output buffers start filled with ``fill`` so that rows no segment covers can be checked
+    to stay untouched.
+    """
+    z = zl()
+    dev = torch.device("cuda:0")
+    plan = make_plan(pack)
+    info = plan.info
+    q, k, v, do = (ins[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.full((info["q_rows"], pack.d), fill, dtype=torch.float32, device=dev)
+    lse = torch.full((info["q_rows"],), fill, dtype=torch.float32, device=dev)
+    o, lse, o_part, lse_part = z.attn_fwd(plan, q, k, v, o=o, lse=lse)
+    if info["n_groups"]:
+        z.merge_groups(plan, o_part, lse_part, o, lse)
+    dq = torch.full((info["q_rows"], pack.d), fill, dtype=torch.float32, device=dev)
+    dk = torch.full((info["kv_rows"], pack.d), fill, dtype=torch.float32, device=dev)
+    dv = torch.full((info["kv_rows"], pack.d), fill, dtype=torch.float32, device=dev)
+    z.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {"plan": plan, "o": o, "lse": lse, "o_part": o_part, "lse_part": lse_part, "dq": dq, "dk": dk, "dv": dv}
+
+
+def oracle_pack(pack: W.Pack, ins: dict):
+    """The oracle's forward and backward of the whole pack (small packs only)."""
+    q, k, v, do = (f64(ins[n]) for n in ("q", "k", "v", "do"))
+    args = (pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.softmax_scale())
+    f = oracle.pack_forward(*args, q, k, v)
+    b = oracle.pack_backward(*args, q, k, v, f["o"], f["lse"], do)
+    return {**f, **b}
+
+
+def compare_full(pack: W.Pack, ins: dict, out: dict, ref: dict):
+    """Element-wise parity on every covered row, ring partials included; uncovered rows
+    must still hold the NaN fill."""
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        g = f64(out[name])
+        r = ref[name]
+        cov = ~np.isnan(r if r.ndim == 1 else r[:, 0])
+        assert_close(name, g[cov], r[cov])
+        assert np.isnan(g[~cov]).all(), f"{name}: rows no segment covers were written"
+    plan = out["plan"]
+    lay = oracle.PackLayout(pack.seq_q, pack.seq_kv, pack.heads)
+    for g in plan.groups:
+        keys = {k for (k, _b) in ref["parts"]
+                if k[0] == g["seq"] and lay.q_off[k[0]] + k[1] * pack.heads[k[0]] == g["o_row"]}
+        assert len(keys) == 1, "ring group not found in the oracle's parts"
+        key = keys.pop()
+        s, q0, q1, h0, h1 = key
+        for b in range(g["n_parts"]):
+            po, pl = ref["parts"][(key, b)]
+            r0 = g["part_row"] + b * g["n_rows"]
+            go = f64(out["o_part"][r0:r0 + g["n_rows"]]).reshape(q1 - q0, h1 - h0, pack.d)
+            gl = f64(out["lse_part"][r0:r0 + g["n_rows"]]).reshape(q1 - q0, h1 - h0)
+            assert_close(f"o_part[{b}]", go, po)
+            assert_close(f"lse_part[{b}]", gl, pl)
+
+
+def seg_rows(pack: W.Pack, seg, head, side: str, t0=None, t1=None) -> np.ndarray:
+    """Packed row indices of (segment, head) on the query or key side."""
+    lay = oracle.PackLayout(pack.seq_q, pack.seq_kv, pack.heads)
+    s, h0, h1, q0, q1, k0, k1, part = seg
+    if side == "q":
+        return lay.q_index(s, q0 if t0 is None else t0, q1 if t1 is None else t1, head)
+    return lay.kv_index(s, k0 if t0 is None else t0, k1 if t1 is None else t1, head)
+
+
+def sample(n: int, count: int, rng) -> np.ndarray:
+    """First, last and uniformly drawn distinct positions in [0, n)."""
+    if n <= count:
+        return np.arange(n)
+    mid = rng.choice(np.arange(1, n - 1), size=count - 2, replace=False)
+    return np.sort(np.concatenate([[0, n - 1], mid]))

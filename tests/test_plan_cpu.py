@@ -1,0 +1,163 @@
+"""Host-side plan tests (no GPU): validation, work queues, cost order, ring-group layout."""
+import ctypes
+
+import pytest
+
+import coalesced_varlen_attention_amd as z
+import workloads as W
+
+ZL_ERR_INVALID, ZL_ERR_UNSUPPORTED = -1, -2
+
+
+def host_plan(pack):
+    return z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale, host_only=True)
+
+
+def expect_error(status, seq_q, seq_kv, heads, segs, d=128, scale=None, match=None):
+    with pytest.raises(z.ZlError) as e:
+        z.Plan(seq_q, seq_kv, heads, segs, d, scale, host_only=True)
+    assert e.value.status == status
+    if match:
+        assert match in str(e.value), str(e.value)
+
+
+@pytest.mark.parametrize("name,fwd,bwd", [("tiny", 44, 44), ("image", 10752, 10752), ("mixed", 33675, 33675),
+                                          ("ring", 23680, 23680), ("long", 29685, 29685)])
+def test_tile_counts(name, fwd, bwd):
+    p = host_plan(W.config(name))
+    assert p.info["fwd_tiles"] == fwd and p.info["bwd_tiles"] == bwd
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_flops_and_rows(name):
+    pack = W.config(name)
+    p = host_plan(pack)
+    assert p.info["fwd_flops"] == pack.flops_fwd()
+    assert p.info["bwd_flops"] == 2.5 * pack.flops_fwd()
+    assert p.info["q_rows"] == pack.q_rows() and p.info["kv_rows"] == pack.kv_rows()
+    assert abs(p.info["softmax_scale"] - pack.d ** -0.5) < 1e-7
+
+
+def test_mixed_pack_metric_flops():
+    # 60.31 TFLOP forward, 211.08 TFLOP forward+backward on the mixed image-video pack
+    p = host_plan(W.mixed())
+    assert abs(p.info["fwd_flops"] - 60.308e12) < 0.01e12
+    assert abs(3.5 * p.info["fwd_flops"] - 211.08e12) < 0.01e12
+    # fp32 O of this pack exceeds 2^31 bytes: offsets must be 64-bit
+    assert p.info["q_rows"] * 128 * 4 > 2 ** 31
+
+
+@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("name", ["tiny", "mixed", "ring"])
+def test_queue_covers_every_block_once_in_cost_order(name, which):
+    pack = W.config(name)
+    p = host_plan(pack)
+    tiles = p.tiles(which)
+    block = 128
+    seen = set()
+    for (seg, h, r0, n) in tiles:
+        s, h0, h1, q0, q1, k0, k1, part = pack.segments[seg]
+        lo, hi = (q0, q1) if which == 0 else (k0, k1)
+        assert h0 <= h < h1 and lo <= r0 and r0 + n <= hi and 1 <= n <= block
+        assert (r0 - lo) % block == 0 and (n == block or r0 + n == hi)
+        assert (seg, h, r0) not in seen
+        seen.add((seg, h, r0))
+    expected = sum((s[2] - s[1]) * -(-((s[4] - s[3]) if which == 0 else (s[6] - s[5])) // block) for s in pack.segments)
+    assert len(seen) == expected
+    other = lambda t: (pack.segments[t[0]][6] - pack.segments[t[0]][5]) if which == 0 else (pack.segments[t[0]][4] - pack.segments[t[0]][3])
+    costs = [t[3] * other(t) for t in tiles]
+    assert all(a >= b for a, b in zip(costs, costs[1:])), "queue not in decreasing cost order"
+    for a, b, ca, cb in zip(tiles, tiles[1:], costs, costs[1:]):
+        if ca == cb:
+            assert (a[0], a[1], a[2]) < (b[0], b[1], b[2]), "equal-cost items not in (segment, head, block) order"
+
+
+def test_ring_group_layout():
+    pack = W.ring()
+    p = host_plan(pack)
+    assert p.info["n_groups"] == 1 and p.info["n_parts_max"] == 8
+    g = p.groups[0]
+    assert g == {"n_parts": 8, "seq": 0, "n_rows": 9450 * 40, "o_row": 0, "part_row": 0}
+    assert p.info["part_rows"] == 8 * 9450 * 40
+
+
+def test_two_groups_stack_in_the_slab():
+    seg = ((0, 0, 2, 0, 10, 0, 5, 0), (0, 0, 2, 0, 10, 5, 9, 1), (1, 0, 3, 4, 8, 0, 3, 1), (1, 0, 3, 4, 8, 3, 6, 0))
+    p = z.Plan((10, 12), (9, 6), (2, 3), seg, 64, host_only=True)
+    g0, g1 = p.groups
+    assert g0["n_rows"] == 20 and g0["part_row"] == 0 and g0["o_row"] == 0
+    assert g1["n_rows"] == 12 and g1["part_row"] == 40 and g1["o_row"] == 20 + 4 * 3
+    assert p.info["part_rows"] == 40 + 24
+
+
+def test_validation_errors():
+    ok = (0, 0, 2, 0, 8, 0, 8, -1)
+    expect_error(ZL_ERR_UNSUPPORTED, [8], [8], [2], [ok], d=96, match="d_head")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(1, 0, 2, 0, 8, 0, 8, -1)], match="no such sequence")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 3, 0, 8, 0, 8, -1)], match="head range")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 1, 1, 0, 8, 0, 8, -1)], match="head range")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 3, 3, 0, 8, -1)], match="query range")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 9, 0, 8, -1)], match="query range")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 8, -1, 8, -1)], match="key range")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 8, 0, 8, -2)], match="part")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [], match="at least one segment")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [ok], scale=float("inf"), match="scale")
+    # overlapping outputs / aliased keys
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [ok, (0, 1, 2, 4, 8, 0, 8, -1)], match="same output rows")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 4, 0, 8, -1), (0, 0, 2, 4, 8, 2, 5, -1)],
+                 match="same K/V rows")
+    # ring groups
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 1, 0, 8, 0, 4, 0), (0, 0, 1, 0, 8, 4, 8, 1)],
+                 match="every stored head")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 8, 0, 4, 0), (0, 0, 2, 0, 8, 4, 8, 0)],
+                 match="numbered")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 8, 0, 4, 0), (0, 0, 2, 0, 8, 4, 8, 2)],
+                 match="numbered")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 8, 0, 5, 0), (0, 0, 2, 0, 8, 4, 8, 1)],
+                 match="share key rows")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 8, 0, 4, 0), (0, 0, 2, 0, 8, 4, 8, 1), ok],
+                 match="same output rows")
+
+
+def test_bad_sequence_arrays():
+    lib = z._lib
+    out = ctypes.c_void_p()
+    seg = z._Segment(0, 0, 1, 0, 4, 0, 4, -1)
+    cu_bad0 = (ctypes.c_int64 * 2)(1, 5)
+    cu = (ctypes.c_int64 * 2)(0, 4)
+    dec = (ctypes.c_int64 * 3)(0, 4, 3)
+    heads = (ctypes.c_int32 * 2)(1, 1)
+    zero_heads = (ctypes.c_int32 * 1)(0)
+    st = lib.zl_plan_build(1, ctypes.addressof(cu_bad0), ctypes.addressof(cu), ctypes.addressof(heads), 1,
+                           ctypes.addressof(seg), 64, 0.0, 1, ctypes.byref(out))
+    assert st == ZL_ERR_INVALID and b"cu_seqlens[0]" in lib.zl_last_error()
+    st = lib.zl_plan_build(2, ctypes.addressof(dec), ctypes.addressof(dec), ctypes.addressof(heads), 1,
+                           ctypes.addressof(seg), 64, 0.0, 1, ctypes.byref(out))
+    assert st == ZL_ERR_INVALID and b"decreases" in lib.zl_last_error()
+    st = lib.zl_plan_build(1, ctypes.addressof(cu), ctypes.addressof(cu), ctypes.addressof(zero_heads), 1,
+                           ctypes.addressof(seg), 64, 0.0, 1, ctypes.byref(out))
+    assert st == ZL_ERR_INVALID and b"seq_heads" in lib.zl_last_error()
+    st = lib.zl_plan_build(1, ctypes.addressof(cu), ctypes.addressof(cu), ctypes.addressof(heads), 1,
+                           ctypes.addressof(seg), 64, 0.0, 8, ctypes.byref(out))
+    assert st == ZL_ERR_INVALID and b"flag" in lib.zl_last_error()
+    assert lib.zl_plan_build(1, None, None, None, 1, None, 64, 0.0, 1, ctypes.byref(out)) == ZL_ERR_INVALID
+
+
+def test_host_only_plan_cannot_run_and_merge_checks():
+    p = host_plan(W.tiny())
+    lib = z._lib
+    assert lib.zl_attn_fwd(p.handle, 16, 16, 16, 16, 16, None, None, 16, None) == ZL_ERR_INVALID
+    assert b"host-only" in lib.zl_last_error()
+    assert lib.zl_attn_bwd(p.handle, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, None) == ZL_ERR_INVALID
+    assert lib.zl_attn_fwd(None, 16, 16, 16, 16, 16, None, None, 16, None) == ZL_ERR_INVALID
+    assert lib.zl_lse_merge(2, 10, 96, 16, 16, 16, 16, None) == ZL_ERR_UNSUPPORTED
+    assert lib.zl_lse_merge(0, 10, 128, 16, 16, 16, 16, None) == ZL_ERR_INVALID
+    assert lib.zl_lse_merge(2, -1, 128, 16, 16, 16, 16, None) == ZL_ERR_INVALID
+    assert lib.zl_lse_merge(2, 0, 128, None, None, None, None, None) == 0
+    assert lib.zl_lse_merge(2, 10, 128, 24, 16, 16, 16, None) == ZL_ERR_INVALID  # misaligned o_part
+
+
+def test_scale_override():
+    pack = W.tiny()
+    p = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, 0.3, host_only=True)
+    assert abs(p.info["softmax_scale"] - 0.3) < 1e-7
