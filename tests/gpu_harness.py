@@ -88,14 +88,20 @@ def oracle_pack(pack: W.Pack, ins: dict):
     return {**f, **b}
 
 
-def compare_full(pack: W.Pack, ins: dict, out: dict, ref: dict):
+def compare_full(pack: W.Pack, ins: dict, out: dict, ref: dict, scaled_max_abs: bool = False):
     """Element-wise parity on every covered row, ring partials included; uncovered rows
-    must still hold the NaN fill."""
+    must still hold the NaN fill.
+
+    ``scaled_max_abs``: for stress inputs far from N(0,1) (peaked queries, growing key
+    norms) the gradients reach magnitudes of 10 and more, and the bf16 rounding of P and
+    dS is relative to those magnitudes; the max-abs bound is then 2e-2 times the largest
+    reference magnitude (at least 1). The rel-L2 bound is unchanged."""
     for name in ("o", "lse", "dq", "dk", "dv"):
         g = f64(out[name])
         r = ref[name]
         cov = ~np.isnan(r if r.ndim == 1 else r[:, 0])
-        assert_close(name, g[cov], r[cov])
+        bound = MAX_ABS * max(1.0, float(np.max(np.abs(r[cov])))) if scaled_max_abs else MAX_ABS
+        assert_close(name, g[cov], r[cov], max_abs=bound)
         assert np.isnan(g[~cov]).all(), f"{name}: rows no segment covers were written"
     plan = out["plan"]
     lay = oracle.PackLayout(pack.seq_q, pack.seq_kv, pack.heads)

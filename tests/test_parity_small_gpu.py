@@ -14,12 +14,12 @@ from tests import gpu_harness as H
 pytestmark = [pytest.mark.gpu, H.requires_gpu]
 
 
-def _run(pack, ins=None):
+def _run(pack, ins=None, stress=False):
     ins = W.draw(pack) if ins is None else ins
     print(f"[case] {pack.name} d={pack.d} seqs={pack.seq_q}/{pack.seq_kv} segs={len(pack.segments)}", flush=True)
     out = H.run_pack(pack, ins)
     ref = H.oracle_pack(pack, ins)
-    H.compare_full(pack, ins, out, ref)
+    H.compare_full(pack, ins, out, ref, scaled_max_abs=stress)
     return out, ref
 
 
@@ -74,7 +74,7 @@ def test_peaked_softmax():
     pack = W.whole_pack("peaked", [257, 1000], [2, 2], 128, 16)
     ins = W.draw(pack)
     ins["q"] = (ins["q"].float() * 8).to(torch.bfloat16)
-    _run(pack, ins)
+    _run(pack, ins, stress=True)
 
 
 def test_drifting_max():
@@ -84,7 +84,7 @@ def test_drifting_max():
     rows = ins["k"].shape[0]
     ramp = torch.linspace(0.25, 3.0, rows).unsqueeze(1)
     ins["k"] = (ins["k"].float() * ramp).to(torch.bfloat16)
-    _run(pack, ins)
+    _run(pack, ins, stress=True)
 
 
 def test_block_diagonal_separation_bitwise():
@@ -99,5 +99,7 @@ def test_block_diagonal_separation_bitwise():
     b = H.run_pack(pack, ins2)
     q_other = np.r_[0:200, 800:800 + 154]
     for n in ("o", "lse"):
+        assert torch.equal(a[n][q_other].cpu(), b[n][q_other].cpu()), n
+    for n in ("dk", "dv"):  # written once per row, no atomics: bitwise too
         assert torch.equal(a[n][q_other].cpu(), b[n][q_other].cpu()), n
     assert not torch.equal(a["o"][200:800].cpu(), b["o"][200:800].cpu())
