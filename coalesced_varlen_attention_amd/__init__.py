@@ -41,7 +41,7 @@ class _PlanInfo(ctypes.Structure):
                 ("kv_rows", ctypes.c_int64), ("part_rows", ctypes.c_int64), ("n_groups", ctypes.c_int32),
                 ("n_parts_max", ctypes.c_int32), ("fwd_tiles", ctypes.c_int64), ("bwd_tiles", ctypes.c_int64),
                 ("fwd_flops", ctypes.c_double), ("bwd_flops", ctypes.c_double), ("d_head", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("dq_tiles", ctypes.c_int64)]
 
 
 class _GroupInfo(ctypes.Structure):
@@ -137,7 +137,7 @@ class Plan:
         return self._h
 
     def tiles(self, which: int) -> List[Tuple[int, int, int, int]]:
-        """Work queue items (segment, head, first row, rows): which=0 forward, 1 backward."""
+        """Work queue items (segment, head, first row, rows): 0 forward, 1 backward dK/dV, 2 backward dQ."""
         cnt = ctypes.c_int64()
         _check(_lib.zl_plan_tiles(self._h, which, None, 0, ctypes.byref(cnt)))
         buf = (ctypes.c_int32 * (4 * cnt.value))()

@@ -71,6 +71,7 @@ extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   info->bwd_tiles = (int64_t)plan->bwd_tiles.size();
   info->fwd_flops = plan->fwd_flops;
   info->bwd_flops = 2.5 * plan->fwd_flops;
+  info->dq_tiles = (int64_t)plan->dq_tiles.size();
   info->d_head = plan->d;
   info->softmax_scale = plan->scale;
   return ZL_OK;
@@ -86,8 +87,8 @@ extern "C" zl_status zl_plan_group(const zl_plan* plan, int32_t g, zl_group_info
 
 extern "C" zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* out, int64_t cap, int64_t* count) {
   if (!plan || !count) return fail(ZL_ERR_INVALID, "zl_plan_tiles: NULL argument");
-  if (which != 0 && which != 1) return fail(ZL_ERR_INVALID, "zl_plan_tiles: which must be 0 or 1");
-  const auto& v = which == 0 ? plan->fwd_tiles : plan->bwd_tiles;
+  if (which < 0 || which > 2) return fail(ZL_ERR_INVALID, "zl_plan_tiles: which must be 0, 1 or 2");
+  const auto& v = which == 0 ? plan->fwd_tiles : which == 1 ? plan->bwd_tiles : plan->dq_tiles;
   *count = (int64_t)v.size();
   if (cap < 0) return fail(ZL_ERR_INVALID, "zl_plan_tiles: negative capacity");
   if (cap > 0 && !out) return fail(ZL_ERR_INVALID, "zl_plan_tiles: out is NULL");
@@ -174,17 +175,23 @@ extern "C" zl_status zl_attn_bwd(const zl_plan* plan, const void* q, const void*
   p.dk = dk;
   p.dv = dv;
   p.counter = (int32_t*)workspace;
+  p.dq_counter = (int32_t*)((char*)workspace + 64);
   p.dvec = (float*)((char*)workspace + kCounterBytes);
   p.segs = plan->d_segs;
   p.tiles = plan->d_bwd;
   p.n_tiles = (int32_t)plan->bwd_tiles.size();
   p.pre_tiles = plan->d_pre;
   p.n_pre = (int32_t)plan->pre_tiles.size();
+  p.dq_tiles = plan->d_dq;
+  p.n_dq = (int32_t)plan->dq_tiles.size();
+  p.kv_ranges = plan->d_ranges;
   p.scale = plan->scale;
   p.scale_log2 = plan->scale * 1.4426950408889634f;
   const int per_cu = zl::bwd_blocks_per_cu(plan->d);
-  if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_bwd: backward kernel cannot be resident");
+  const int per_cu_dq = zl::dq_blocks_per_cu(plan->d);
+  if (per_cu < 1 || per_cu_dq < 1) return fail(ZL_ERR_HIP, "zl_attn_bwd: backward kernels cannot be resident");
   const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, p.n_tiles);
+  const int grid_dq = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu_dq, p.n_dq);
   const int grid_pre = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)plan->n_cu * 8, p.n_pre));
-  return launch_status(zl::launch_bwd(plan->d, p, grid_pre, grid, stream), "zl_attn_bwd");
+  return launch_status(zl::launch_bwd(plan->d, p, grid_pre, grid, grid_dq, stream), "zl_attn_bwd");
 }

@@ -1,50 +1,39 @@
-// Backward kernels: the pre-pass and the persistent main kernel.
+// Backward kernels: pre-pass, dK/dV (key-major) and dQ (query-major).
 //
 // Gradients of f = sum dO . O for softmax attention (the exact backward named on the Zellige
 // page, §V-A), recomputing the probabilities from the forward's LSE:
 //   P = exp(tau Q K^T - LSE),  dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
 //   dK = tau dS^T Q,  dQ = tau dS K,  with D_i = sum_c dO_ic O_ic.
 // For a ring part the LSE and O are the merged ones, so P is the global softmax restricted
-// to the part's keys and dQ sums over parts.
+// to the part's keys; dQ sums over every part of the group.
 //
-// Pre-pass: D for every covered query row, and dQ zeroed (dQ is accumulated with atomics).
-// Main kernel: one item = 128 key rows of one (segment, head); 4 waves x 32 keys. Each wave
-// keeps its K and V rows in registers as B operands of S = Q K^T and dP = dO V^T (lane = one
-// key column), so P and dS come out of the MFMA already in the B-operand layout of
-// dV^T = dO^T P and dK^T = Q^T dS; dO^T and Q^T are read from natural LDS tiles with
-// transposed LDS reads. dS^T goes through LDS once more to form dQ = dS K for the 64 query
-// rows of the step, which is added to global dQ with fp32 atomics. The loop over query
-// blocks starts at a block that depends on the key block, so that items of one head that
-// run at the same time add into different dQ rows.
+// Pre-pass: D for every covered query row; both queue counters zeroed.
+// dK/dV kernel: one item = 128 key rows of one (segment, head); 4 waves x 32 keys. Each wave
+//   keeps its K and V rows in registers as B operands of S = Q K^T and dP = dO V^T (lane = one
+//   key column), so P and dS come out of the MFMA already in the B-operand layout of
+//   dV^T = dO^T P and dK^T = Q^T dS; dO^T and Q^T are read from natural LDS tiles with
+//   transposed LDS reads. dK and dV accumulate in registers and are written once.
+// dQ kernel: one item = 128 query rows of one (segment or ring group, head); 4 waves x 32
+//   query rows, the forward's shape: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers
+//   (lane = one query row, whose LSE and D are then per-lane scalars), and
+//   dQ^T += K^T dS^T with K^T from transposed LDS reads. dQ is written once: no atomics.
+//   Computing dQ in its own query-major pass costs S and dP a second time, but fp32 atomics
+//   into dQ from every key block were measured to cost more than the whole key-major pass.
 #include "zl_device.hpp"
 #include "zl_internal.h"
 
 namespace zl {
 namespace {
 
-template <int D>
-struct BwdCfg {
-  static constexpr int kThreads = 256;
-  static constexpr int kBq = kBwdRows;                    // 64 query rows per step
-  static constexpr int kBk = kBwdKeys;                    // 128 keys per item
-  static constexpr int kQld = D + 8;                      // Q / dO row stride in LDS
-  static constexpr int kKld = D + 16;                     // K tile row stride in LDS
-  static constexpr int kSld = kBq + 8;                    // dS^T row stride in LDS
-  static constexpr int kSteps = D / 16;                   // k-steps over d
-  static constexpr int kCb = D / 32;                      // 32-wide column blocks over d
-  static constexpr int kQChunks = kBq * D / 8 / kThreads; // 16-B chunks per thread (Q or dO)
-  static constexpr int kKChunks = kBk * D / 8 / kThreads; // 16-B chunks per thread (K tile)
-  static constexpr int kRowChunks = D / 8;
-  // dQ: waves split (column block, 32-row block) pairs of the 64 x D output.
-  static constexpr int kWavesPerCb = 4 / kCb;             // 1 (D=128) or 2 (D=64)
-  static constexpr int kMbPerWave = 2 / kWavesPerCb;      // 2 (D=128) or 1 (D=64)
-};
+// ---------------------------------------------------------------------------------------------
+// Pre-pass: D_i = sum_c dO_ic O_ic for every covered query row (16 lanes per row).
 
-// D_i = sum_c dO_ic O_ic for every covered query row; dQ rows zeroed; queue counter zeroed.
-// 16 lanes per row, 16 rows per workgroup pass.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *p.counter = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *p.counter = 0;
+    *p.dq_counter = 0;
+  }
   constexpr int kPer = D / 16;  // elements per lane
   const int sub = threadIdx.x & 15;
   const int rsel = threadIdx.x >> 4;
@@ -65,7 +54,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
         const f32x4 o4 = *(const f32x4*)(p.o + e0 + u);
         const bf16x4 d4 = *(const bf16x4*)(gdo + e0 + u);
         acc += (float)d4[0] * o4[0] + (float)d4[1] * o4[1] + (float)d4[2] * o4[2] + (float)d4[3] * o4[3];
-        *(f32x4*)(p.dq + e0 + u) = f32x4{};
       }
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
@@ -74,13 +62,50 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// dK/dV kernel.
+
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
-  using C = BwdCfg<D>;
+struct KvCfg {
+  static constexpr int kThreads = 256;
+  static constexpr int kBq = kBwdRows;                    // 64 query rows per step
+  static constexpr int kQld = D + 8;                      // Q / dO row stride in LDS
+  static constexpr int kSteps = D / 16;                   // k-steps over d
+  static constexpr int kCb = D / 32;                      // 32-wide column blocks over d
+  static constexpr int kQChunks = kBq * D / 8 / kThreads; // 16-B chunks per thread (Q or dO)
+  static constexpr int kRowChunks = D / 8;
+};
+
+template <int D>
+__device__ __forceinline__ void kv_prefetch(u32x4 (&qpre)[KvCfg<D>::kQChunks], u32x4 (&dopre)[KvCfg<D>::kQChunks],
+                                            float& lpre, const bf16* qbase, const bf16* dobase, int64_t rs,
+                                            int64_t rowbase, int nh, int q0, int nrow, const float* lse,
+                                            const float* dvec, int tid) {
+  using C = KvCfg<D>;
+#pragma unroll
+  for (int c = 0; c < C::kQChunks; ++c) {
+    const int chunk = tid + c * C::kThreads;
+    const int r = chunk / C::kRowChunks;
+    const int col = (chunk % C::kRowChunks) * 8;
+    const int64_t off = (int64_t)(q0 + min(r, nrow - 1)) * rs + col;
+    qpre[c] = *(const u32x4*)(qbase + off);
+    dopre[c] = *(const u32x4*)(dobase + off);
+  }
+  if (tid < 2 * C::kBq) {
+    const int r = tid & (C::kBq - 1);
+    const int64_t row = rowbase + (int64_t)(q0 + min(r, nrow - 1)) * nh;
+    if (tid < C::kBq)
+      lpre = r < nrow ? lse[row] * 1.4426950408889634f : INFINITY;  // rows past the end: P = 0
+    else
+      lpre = r < nrow ? dvec[row] : 0.f;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
+  using C = KvCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 q_lds[C::kBq * C::kQld];
   __shared__ __attribute__((aligned(16))) bf16 do_lds[C::kBq * C::kQld];
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[C::kBk * C::kKld];
-  __shared__ __attribute__((aligned(16))) bf16 st_lds[C::kBk * C::kSld];
   __shared__ __attribute__((aligned(16))) float lse_lds[C::kBq];
   __shared__ __attribute__((aligned(16))) float dd_lds[C::kBq];
   __shared__ int32_t s_item;
@@ -122,27 +147,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
         vreg[s] = *(const bf16x8*)(gv + off + 16 * s);
       }
     }
-    // The item's K tile in LDS, then K^T operands for dQ: lane = output column c, k = key.
-    {
-      const bf16* kb = gk + (sg.kv_row0 + (int64_t)tile.row0 * nh + h) * D;
-#pragma unroll
-      for (int c = 0; c < C::kKChunks; ++c) {
-        const int chunk = tid + c * C::kThreads;
-        const int r = chunk / C::kRowChunks;
-        const int col = (chunk % C::kRowChunks) * 8;
-        const int key = min(r, nk - 1);
-        *(u32x4*)&k_lds[r * C::kKld + col] = *(const u32x4*)(kb + (int64_t)key * rs + col);
-      }
-    }
-    __syncthreads();
-    const int dq_cb = wave / C::kWavesPerCb;                   // this wave's dQ column block
-    const int dq_mb0 = (wave % C::kWavesPerCb) * C::kMbPerWave; // and first 32-row block
-    bf16x8 ktreg[C::kBk / 16];
-#pragma unroll
-    for (int ks = 0; ks < C::kBk / 16; ++ks) {
-      const bf16* kp = &k_lds[(16 * ks + 8 * hi + r_in) * C::kKld + dq_cb * 32 + c_in];
-      ktreg[ks] = cat(lds_read_tr(kp), lds_read_tr(kp + 4 * C::kKld));
-    }
 
     f32x16 dk_acc[C::kCb], dv_acc[C::kCb];
 #pragma unroll
@@ -153,40 +157,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
 
     const int n_q = sg.q_end - sg.q_begin;
     const int nqb = (n_q + C::kBq - 1) / C::kBq;
-    const int start = (tile.row0 / C::kBk + 3 * h) % nqb;
     const bf16* qbase = gq + (sg.q_row0 + (int64_t)sg.q_begin * nh + h) * D;
     const bf16* dobase = gdo + (sg.q_row0 + (int64_t)sg.q_begin * nh + h) * D;
     const int64_t rowbase = sg.q_row0 + (int64_t)sg.q_begin * nh + h;  // query-side row of local token 0
 
     u32x4 qpre[C::kQChunks], dopre[C::kQChunks];
     float lpre = 0.f;
-    auto prefetch = [&](int qb) {
-      const int q0 = qb * C::kBq;
-      const int nrow = min(C::kBq, n_q - q0);
-#pragma unroll
-      for (int c = 0; c < C::kQChunks; ++c) {
-        const int chunk = tid + c * C::kThreads;
-        const int r = chunk / C::kRowChunks;
-        const int col = (chunk % C::kRowChunks) * 8;
-        const int64_t off = (int64_t)(q0 + min(r, nrow - 1)) * rs + col;
-        qpre[c] = *(const u32x4*)(qbase + off);
-        dopre[c] = *(const u32x4*)(dobase + off);
-      }
-      if (tid < 2 * C::kBq) {
-        const int r = tid & (C::kBq - 1);
-        const int64_t row = rowbase + (int64_t)(q0 + min(r, nrow - 1)) * nh;
-        if (tid < C::kBq)
-          lpre = r < nrow ? p.lse[row] * 1.4426950408889634f : INFINITY;  // invalid rows: P = 0
-        else
-          lpre = r < nrow ? p.dvec[row] : 0.f;
-      }
-    };
-
-    prefetch(start);
-    for (int it = 0; it < nqb; ++it) {
-      const int qb = (start + it) % nqb;
-      const int q0 = qb * C::kBq;
-      const int nrow = min(C::kBq, n_q - q0);
+    kv_prefetch<D>(qpre, dopre, lpre, qbase, dobase, rs, rowbase, nh, 0, min(C::kBq, n_q), p.lse, p.dvec, tid);
+    for (int qb = 0; qb < nqb; ++qb) {
       // Stage this step's Q, dO, LSE (log2 units) and D in LDS.
 #pragma unroll
       for (int c = 0; c < C::kQChunks; ++c) {
@@ -201,7 +179,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
       else if (tid < 2 * C::kBq)
         dd_lds[tid - C::kBq] = lpre;
       __syncthreads();
-      if (it + 1 < nqb) prefetch((start + it + 1) % nqb);
+      if (qb + 1 < nqb) {
+        const int q0n = (qb + 1) * C::kBq;
+        kv_prefetch<D>(qpre, dopre, lpre, qbase, dobase, rs, rowbase, nh, q0n, min(C::kBq, n_q - q0n), p.lse,
+                       p.dvec, tid);
+      }
 
       // S = Q K^T and dP = dO V^T: two 32-row blocks, lane = this wave's key column.
       f32x16 sacc[2], dpacc[2];
@@ -245,12 +227,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
           pb[mb * 2 + hs] = to_bf16x8(a);
           dsb[mb * 2 + hs] = to_bf16x8(b);
         }
-        // dS^T to LDS for dQ: row = key, 4 consecutive query rows per store.
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 x = {dsv[4 * g], dsv[4 * g + 1], dsv[4 * g + 2], dsv[4 * g + 3]};
-          *(bf16x4*)&st_lds[key_local * C::kSld + mb * 32 + 8 * g + 4 * hi] = to_bf16x4(x);
-        }
       }
       // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per step, in the k order of P's rows.
 #pragma unroll
@@ -267,23 +243,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
         }
       }
       __syncthreads();
-      // dQ[q][c] = sum over the item's 128 keys of dS[q][key] K[key][c], then atomics.
-#pragma unroll
-      for (int m = 0; m < C::kMbPerWave; ++m) {
-        const int mb = dq_mb0 + m;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < C::kBk / 16; ++ks) {
-          const bf16* sp = &st_lds[(16 * ks + 8 * hi + r_in) * C::kSld + mb * 32 + c_in];
-          acc = mfma32(cat(lds_read_tr(sp), lds_read_tr(sp + 4 * C::kSld)), ktreg[ks], acc);
-        }
-        const int c = dq_cb * 32 + l32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qr = mb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
-          if (qr < nrow) unsafeAtomicAdd(p.dq + (rowbase + (int64_t)(q0 + qr) * nh) * D + c, acc[i] * p.scale);
-        }
-      }
     }
 
     // dK = tau dK^T, dV = dV^T, written once: lane = key, 4 consecutive columns per store.
@@ -302,33 +261,230 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
                                      dv_acc[cb][4 * g + 3]};
         }
     }
-    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ kernel.
+
+template <int D>
+struct DqCfg {
+  static constexpr int kThreads = 256;
+  static constexpr int kBk = 64;                          // keys per block
+  static constexpr int kKld = D + 16;                     // K row stride (natural and transposed reads)
+  static constexpr int kVld = D + 8;                      // V row stride (natural reads)
+  static constexpr int kSteps = D / 16;
+  static constexpr int kCb = D / 32;
+  static constexpr int kChunks = kBk * D / 8 / kThreads;
+  static constexpr int kRowChunks = D / 8;
+};
+
+template <int D>
+__device__ __forceinline__ void dq_load_block(u32x4 (&kreg)[DqCfg<D>::kChunks], u32x4 (&vreg)[DqCfg<D>::kChunks],
+                                              const bf16* kbase, const bf16* vbase, int64_t rs, int key0, int n_kv,
+                                              int tid) {
+  using C = DqCfg<D>;
+#pragma unroll
+  for (int c = 0; c < C::kChunks; ++c) {
+    const int chunk = tid + c * C::kThreads;
+    const int r = chunk / C::kRowChunks;
+    const int col = (chunk % C::kRowChunks) * 8;
+    const int key = min(key0 + r, n_kv - 1);
+    kreg[c] = *(const u32x4*)(kbase + (int64_t)key * rs + col);
+    vreg[c] = *(const u32x4*)(vbase + (int64_t)key * rs + col);
   }
 }
 
 template <int D>
-int blocks_per_cu_impl() {
-  static int cached = -1;
-  if (cached < 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_kernel<D>, 256, 0) != hipSuccess) n = 0;
-    cached = n;
+__device__ __forceinline__ void dq_store_block(const u32x4 (&kreg)[DqCfg<D>::kChunks],
+                                               const u32x4 (&vreg)[DqCfg<D>::kChunks], bf16* k_lds, bf16* v_lds,
+                                               int tid) {
+  using C = DqCfg<D>;
+#pragma unroll
+  for (int c = 0; c < C::kChunks; ++c) {
+    const int chunk = tid + c * C::kThreads;
+    const int r = chunk / C::kRowChunks;
+    const int col = (chunk % C::kRowChunks) * 8;
+    *(u32x4*)&k_lds[r * C::kKld + col] = kreg[c];
+    *(u32x4*)&v_lds[r * C::kVld + col] = vreg[c];
   }
-  return cached;
+}
+
+// Block j of a key-range chain: the range it lies in and its first key within the range.
+__device__ __forceinline__ void chain_block(const int32_t* ranges, int off, int len, int j, int bk, int* kv0,
+                                            int* n_kv, int* key0) {
+  for (int r = 0; r < len; ++r) {
+    const int b = ranges[2 * (off + r)], e = ranges[2 * (off + r) + 1];
+    const int nb = (e - b + bk - 1) / bk;
+    if (j < nb || r == len - 1) {
+      *kv0 = b;
+      *n_kv = e - b;
+      *key0 = j * bk;
+      return;
+    }
+    j -= nb;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][C::kBk * C::kKld];
+  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][C::kBk * C::kVld];
+  __shared__ int32_t s_item;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int r_in = (lane & 15) >> 2;
+  const int c_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const bf16* __restrict__ gq = (const bf16*)p.q;
+  const bf16* __restrict__ gk = (const bf16*)p.k;
+  const bf16* __restrict__ gv = (const bf16*)p.v;
+  const bf16* __restrict__ gdo = (const bf16*)p.d_o;
+
+  for (;;) {
+    if (tid == 0) s_item = atomicAdd(p.dq_counter, 1);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= p.n_dq) break;
+    const Tile tile = p.dq_tiles[item];
+    const SegDev sg = p.segs[tile.seg];
+    const int nh = sg.nh;
+    const int h = tile.head;
+    const int64_t rs = (int64_t)nh * D;
+
+    // This lane's query row (clamped; results of clamped rows are dropped), with its Q and dO
+    // as B operands (k = d) and its LSE (log2 units) and D as scalars.
+    const int qi = wave * 32 + l32;
+    const bool q_valid = qi < tile.nrows;
+    const int qtok = tile.row0 + (q_valid ? qi : tile.nrows - 1);
+    const int64_t qrow = sg.q_row0 + (int64_t)qtok * nh + h;
+    bf16x8 qreg[C::kSteps], doreg[C::kSteps];
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) {
+      qreg[s] = *(const bf16x8*)(gq + qrow * D + 8 * hi + 16 * s);
+      doreg[s] = *(const bf16x8*)(gdo + qrow * D + 8 * hi + 16 * s);
+    }
+    const float lse2 = p.lse[qrow] * 1.4426950408889634f;
+    const float dd = p.dvec[qrow];
+
+    int n_blk = 0;
+    for (int r = 0; r < sg.chain_len; ++r) {
+      const int len = p.kv_ranges[2 * (sg.chain_off + r) + 1] - p.kv_ranges[2 * (sg.chain_off + r)];
+      n_blk += (len + C::kBk - 1) / C::kBk;
+    }
+    const bf16* kseq = gk + (sg.kv_row0 + h) * D;
+    const bf16* vseq = gv + (sg.kv_row0 + h) * D;
+
+    f32x16 acc[C::kCb];
+#pragma unroll
+    for (int cb = 0; cb < C::kCb; ++cb) acc[cb] = f32x16{};
+
+    u32x4 kreg[C::kChunks], vreg[C::kChunks];
+    int kv0, n_kv, key0;
+    chain_block(p.kv_ranges, sg.chain_off, sg.chain_len, 0, C::kBk, &kv0, &n_kv, &key0);
+    dq_load_block<D>(kreg, vreg, kseq + (int64_t)kv0 * rs, vseq + (int64_t)kv0 * rs, rs, key0, n_kv, tid);
+    dq_store_block<D>(kreg, vreg, k_lds[0], v_lds[0], tid);
+    __syncthreads();
+
+    for (int j = 0; j < n_blk; ++j) {
+      const int buf = j & 1;
+      const int valid = n_kv - key0;  // keys of this block inside its range
+      if (j + 1 < n_blk) {
+        chain_block(p.kv_ranges, sg.chain_off, sg.chain_len, j + 1, C::kBk, &kv0, &n_kv, &key0);
+        dq_load_block<D>(kreg, vreg, kseq + (int64_t)kv0 * rs, vseq + (int64_t)kv0 * rs, rs, key0, n_kv, tid);
+      }
+
+      // Per 32-key half kb: S^T = K Q^T and dP^T = V dO^T, then
+      // dS^T = P^T (dP^T - D) with P^T = exp2(S^T tau log2e - LSE log2e) (keys past the range: 0),
+      // then dQ^T[c][q] += K^T[c][key] dS^T[key][q] in the k order of dS^T's rows.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        const bf16* kr = &k_lds[buf][(kb * 32 + l32) * C::kKld + 8 * hi];
+        const bf16* vr = &v_lds[buf][(kb * 32 + l32) * C::kVld + 8 * hi];
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s) {
+          sacc = mfma32(*(const bf16x8*)(kr + 16 * s), qreg[s], sacc);
+          dpacc = mfma32(*(const bf16x8*)(vr + 16 * s), doreg[s], dpacc);
+        }
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          f32x8 x;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = 8 * hs + u;
+            const int key = kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
+            const float pe = key < valid ? fast_exp2(fmaf(sacc[i], p.scale_log2, -lse2)) : 0.f;
+            x[u] = pe * (dpacc[i] - dd);
+          }
+          dsb[hs] = to_bf16x8(x);
+        }
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const int row = kb * 32 + 16 * hs + 4 * hi + r_in;
+#pragma unroll
+          for (int cb = 0; cb < C::kCb; ++cb) {
+            const bf16* kp = &k_lds[buf][row * C::kKld + cb * 32 + c_in];
+            acc[cb] = mfma32(cat(lds_read_tr(kp), lds_read_tr(kp + 8 * C::kKld)), dsb[hs], acc[cb]);
+          }
+        }
+      }
+      if (j + 1 < n_blk) dq_store_block<D>(kreg, vreg, k_lds[buf ^ 1], v_lds[buf ^ 1], tid);
+      __syncthreads();
+    }
+
+    if (q_valid) {
+      float* out = p.dq + qrow * D;
+#pragma unroll
+      for (int cb = 0; cb < C::kCb; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = cb * 32 + 8 * g + 4 * hi;
+          *(f32x4*)(out + c) = f32x4{acc[cb][4 * g] * p.scale, acc[cb][4 * g + 1] * p.scale,
+                                     acc[cb][4 * g + 2] * p.scale, acc[cb][4 * g + 3] * p.scale};
+        }
+    }
+  }
+}
+
+template <typename K>
+int occupancy(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess) n = 0;
+  return n;
 }
 
 }  // namespace
 
-int bwd_blocks_per_cu(int d) { return d == 64 ? blocks_per_cu_impl<64>() : blocks_per_cu_impl<128>(); }
+int bwd_blocks_per_cu(int d) {
+  static int c64 = -1, c128 = -1;
+  int& c = d == 64 ? c64 : c128;
+  if (c < 0) c = d == 64 ? occupancy(dkdv_kernel<64>) : occupancy(dkdv_kernel<128>);
+  return c;
+}
 
-int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, void* stream) {
+int dq_blocks_per_cu(int d) {
+  static int c64 = -1, c128 = -1;
+  int& c = d == 64 ? c64 : c128;
+  if (c < 0) c = d == 64 ? occupancy(dq_kernel<64>) : occupancy(dq_kernel<128>);
+  return c;
+}
+
+int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (d == 64) {
     hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(grid_pre), dim3(256), 0, s, p);
-    hipLaunchKernelGGL(bwd_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(dkdv_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(dq_kernel<64>, dim3(grid_dq), dim3(256), 0, s, p);
   } else {
     hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid_pre), dim3(256), 0, s, p);
-    hipLaunchKernelGGL(bwd_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(dkdv_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(dq_kernel<128>, dim3(grid_dq), dim3(256), 0, s, p);
   }
   return hipPeekAtLastError() == hipSuccess ? 0 : 1;
 }

@@ -10,8 +10,10 @@
 
 namespace zl {
 
-// Forward queue item: 128 query rows of one (segment, head). Backward queue item: 128 key
-// rows of one (segment, head), looping over the segment's query rows in blocks of 64.
+// Forward queue item: 128 query rows of one (segment, head). Backward dK/dV queue item: 128
+// key rows of one (segment, head), looping over the segment's query rows in blocks of 64.
+// Backward dQ queue item: 128 query rows of one (final segment or ring group, head), looping
+// over every key range of the segment (all parts of a ring group).
 constexpr int kFwdRows = 128;
 constexpr int kBwdKeys = 128;
 constexpr int kBwdRows = 64;
@@ -27,7 +29,8 @@ struct alignas(16) SegDev {
   int32_t q_begin, q_end, kv_begin, kv_end;
   int32_t head_begin, head_end;
   int32_t part;
-  int32_t pad[2];
+  int32_t chain_off;  // first (kv_begin, kv_end) pair of this segment's key-range chain
+  int32_t chain_len;  // pairs in the chain: 1, or the parts of a ring group (on part 0)
 };
 static_assert(sizeof(SegDev) == 64, "SegDev must stay 64 bytes");
 
@@ -67,19 +70,24 @@ struct BwdParams {
   int32_t n_tiles;
   const Tile* pre_tiles;  // (segment, head_begin, first token, tokens) per pre-pass item
   int32_t n_pre;
-  int32_t* counter;
+  const Tile* dq_tiles;   // dQ queue
+  int32_t n_dq;
+  const int32_t* kv_ranges;  // (kv_begin, kv_end) pairs of the key-range chains
+  int32_t* counter;     // dK/dV queue counter
+  int32_t* dq_counter;  // dQ queue counter
   float scale;       // softmax scale
   float scale_log2;  // softmax scale times log2(e)
 };
 
 // Kernel launchers (defined next to their kernels). They return the launch status.
 int launch_fwd(int d, const FwdParams& p, int grid, void* stream);
-int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, void* stream);
+int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, void* stream);
 int launch_merge(int d, int32_t n_parts, int64_t n_rows, const float* o_part, const float* lse_part,
                  float* o, float* lse, int grid, void* stream);
 // Workgroups of each persistent kernel that fit on one compute unit.
 int fwd_blocks_per_cu(int d);
 int bwd_blocks_per_cu(int d);
+int dq_blocks_per_cu(int d);
 
 void set_error(const std::string& msg);
 
@@ -96,7 +104,8 @@ struct zl_plan {
   int32_t n_parts_max = 0;
   double fwd_flops = 0.0;
   std::vector<zl::SegDev> segs;
-  std::vector<zl::Tile> fwd_tiles, bwd_tiles, pre_tiles;
+  std::vector<zl::Tile> fwd_tiles, bwd_tiles, pre_tiles, dq_tiles;
+  std::vector<int32_t> kv_ranges;
   std::vector<zl_group_info_t> groups;
   // device copies (one allocation, carved into the three tables)
   void* dev_block = nullptr;
@@ -104,4 +113,6 @@ struct zl_plan {
   const zl::Tile* d_fwd = nullptr;
   const zl::Tile* d_bwd = nullptr;
   const zl::Tile* d_pre = nullptr;
+  const zl::Tile* d_dq = nullptr;
+  const int32_t* d_ranges = nullptr;
 };

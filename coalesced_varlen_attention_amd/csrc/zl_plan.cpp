@@ -137,7 +137,6 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     }
   }
   const int n_groups = (int)group_members.size();
-  std::vector<int> part_segment_base(n_groups, 0);
   for (int gid = 0; gid < n_groups; ++gid) {
     auto& mem = group_members[gid];
     const zl_segment& f = segs[mem[0]];
@@ -225,19 +224,43 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
                        (double)(g.head_end - g.head_begin);
   }
 
+  // Key-range chains for the dQ queue: a final segment's own range, or on part 0 of a ring
+  // group every part's range in part order.
+  for (int i = 0; i < n_seg; ++i) {
+    const zl_segment& g = segs[i];
+    zl::SegDev& d = plan->segs[i];
+    d.chain_off = (int32_t)(plan->kv_ranges.size() / 2);
+    d.chain_len = 0;
+    if (g.part > 0) continue;
+    std::vector<int> members{i};
+    if (g.part == 0) {
+      members.assign(group_members[seg_group[i]].begin(), group_members[seg_group[i]].end());
+      std::sort(members.begin(), members.end(), [&](int a, int b) { return segs[a].part < segs[b].part; });
+    }
+    for (int m : members) {
+      plan->kv_ranges.push_back(segs[m].kv_begin);
+      plan->kv_ranges.push_back(segs[m].kv_end);
+    }
+    d.chain_len = (int32_t)members.size();
+  }
+
   // Work queues, sorted by decreasing cost with a stable tie order.
   struct Item {
     zl::Tile t;
     int64_t cost;
   };
-  std::vector<Item> fwd, bwd;
+  std::vector<Item> fwd, bwd, dq;
   for (int i = 0; i < n_seg; ++i) {
     const zl_segment& g = segs[i];
     const int64_t nq = g.q_end - g.q_begin, nk = g.kv_end - g.kv_begin;
+    int64_t chain_keys = 0;
+    for (int c = 0; c < plan->segs[i].chain_len; ++c)
+      chain_keys += plan->kv_ranges[2 * (plan->segs[i].chain_off + c) + 1] - plan->kv_ranges[2 * (plan->segs[i].chain_off + c)];
     for (int h = g.head_begin; h < g.head_end; ++h) {
       for (int64_t r = g.q_begin; r < g.q_end; r += zl::kFwdRows) {
         const int32_t n = (int32_t)std::min<int64_t>(zl::kFwdRows, g.q_end - r);
         fwd.push_back({{i, h, (int32_t)r, n}, (int64_t)n * nk});
+        if (g.part <= 0) dq.push_back({{i, h, (int32_t)r, n}, (int64_t)n * chain_keys});
       }
       for (int64_t r = g.kv_begin; r < g.kv_end; r += zl::kBwdKeys) {
         const int32_t n = (int32_t)std::min<int64_t>(zl::kBwdKeys, g.kv_end - r);
@@ -257,8 +280,10 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   auto by_cost = [](const Item& a, const Item& b) { return a.cost > b.cost; };
   std::stable_sort(fwd.begin(), fwd.end(), by_cost);
   std::stable_sort(bwd.begin(), bwd.end(), by_cost);
+  std::stable_sort(dq.begin(), dq.end(), by_cost);
   for (auto& it : fwd) plan->fwd_tiles.push_back(it.t);
   for (auto& it : bwd) plan->bwd_tiles.push_back(it.t);
+  for (auto& it : dq) plan->dq_tiles.push_back(it.t);
 
   if (!(flags & ZL_PLAN_HOST_ONLY)) {
     if (hipGetDevice(&plan->device) != hipSuccess) return fail(ZL_ERR_HIP, "zl_plan_build: hipGetDevice failed");
@@ -270,25 +295,37 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     const size_t b_fwd = align(plan->fwd_tiles.size() * sizeof(zl::Tile));
     const size_t b_bwd = align(plan->bwd_tiles.size() * sizeof(zl::Tile));
     const size_t b_pre = align(plan->pre_tiles.size() * sizeof(zl::Tile));
-    const size_t total = b_segs + b_fwd + b_bwd + b_pre;
+    const size_t b_dq = align(plan->dq_tiles.size() * sizeof(zl::Tile));
+    const size_t b_rng = align(plan->kv_ranges.size() * sizeof(int32_t));
+    const size_t total = b_segs + b_fwd + b_bwd + b_pre + b_dq + b_rng;
     if (hipMalloc(&plan->dev_block, total) != hipSuccess) {
       plan->dev_block = nullptr;
       (void)hipGetLastError();
       return fail(ZL_ERR_NOMEM, "zl_plan_build: hipMalloc of " + std::to_string(total) + " bytes failed");
     }
     char* base = (char*)plan->dev_block;
-    plan->d_segs = (const zl::SegDev*)base;
-    plan->d_fwd = (const zl::Tile*)(base + b_segs);
-    plan->d_bwd = (const zl::Tile*)(base + b_segs + b_fwd);
-    plan->d_pre = (const zl::Tile*)(base + b_segs + b_fwd + b_bwd);
+    size_t off = 0;
+    auto carve = [&](size_t bytes) {
+      char* p = base + off;
+      off += bytes;
+      return (void*)p;
+    };
+    plan->d_segs = (const zl::SegDev*)carve(b_segs);
+    plan->d_fwd = (const zl::Tile*)carve(b_fwd);
+    plan->d_bwd = (const zl::Tile*)carve(b_bwd);
+    plan->d_pre = (const zl::Tile*)carve(b_pre);
+    plan->d_dq = (const zl::Tile*)carve(b_dq);
+    plan->d_ranges = (const int32_t*)carve(b_rng);
     hipError_t e = hipSuccess;
-    e = hipMemcpy((void*)plan->d_segs, plan->segs.data(), plan->segs.size() * sizeof(zl::SegDev), hipMemcpyHostToDevice);
-    if (e == hipSuccess)
-      e = hipMemcpy((void*)plan->d_fwd, plan->fwd_tiles.data(), plan->fwd_tiles.size() * sizeof(zl::Tile), hipMemcpyHostToDevice);
-    if (e == hipSuccess)
-      e = hipMemcpy((void*)plan->d_bwd, plan->bwd_tiles.data(), plan->bwd_tiles.size() * sizeof(zl::Tile), hipMemcpyHostToDevice);
-    if (e == hipSuccess && !plan->pre_tiles.empty())
-      e = hipMemcpy((void*)plan->d_pre, plan->pre_tiles.data(), plan->pre_tiles.size() * sizeof(zl::Tile), hipMemcpyHostToDevice);
+    auto up = [&](const void* dst, const void* src, size_t bytes) {
+      if (e == hipSuccess && bytes) e = hipMemcpy((void*)dst, src, bytes, hipMemcpyHostToDevice);
+    };
+    up(plan->d_segs, plan->segs.data(), plan->segs.size() * sizeof(zl::SegDev));
+    up(plan->d_fwd, plan->fwd_tiles.data(), plan->fwd_tiles.size() * sizeof(zl::Tile));
+    up(plan->d_bwd, plan->bwd_tiles.data(), plan->bwd_tiles.size() * sizeof(zl::Tile));
+    up(plan->d_pre, plan->pre_tiles.data(), plan->pre_tiles.size() * sizeof(zl::Tile));
+    up(plan->d_dq, plan->dq_tiles.data(), plan->dq_tiles.size() * sizeof(zl::Tile));
+    up(plan->d_ranges, plan->kv_ranges.data(), plan->kv_ranges.size() * sizeof(int32_t));
     if (e != hipSuccess) {
       (void)hipFree(plan->dev_block);
       plan->dev_block = nullptr;

@@ -76,11 +76,12 @@ typedef struct {
   int32_t n_groups;       /* KV-split groups */
   int32_t n_parts_max;    /* most parts in one group */
   int64_t fwd_tiles;      /* work items of the forward queue */
-  int64_t bwd_tiles;      /* work items of the backward queue */
+  int64_t bwd_tiles;      /* work items of the backward dK/dV queue */
   double fwd_flops;       /* sum over (segment, head) of 4*Lq*Lkv*d */
   double bwd_flops;       /* 2.5 x fwd_flops */
   int32_t d_head;
   float softmax_scale;
+  int64_t dq_tiles;       /* work items of the backward dQ queue */
 } zl_plan_info_t;
 
 typedef struct {
@@ -108,9 +109,10 @@ typedef struct {
  *   out                   receives the plan; the caller frees it with zl_plan_destroy
  * The host arrays are copied; the plan owns its device tables (allocated on the current
  * device) and nothing else. The forward queue holds one item per (segment, head, block of
- * 128 query rows), the backward queue one per (segment, head, block of 128 key rows); each
- * queue is sorted by decreasing cost (rows x length of the other side), ties kept in
- * (segment, head, block) order.
+ * 128 query rows); the backward has a dK/dV queue with one item per (segment, head, block
+ * of 128 key rows) and a dQ queue with one item per (final segment or ring group, head,
+ * block of 128 query rows). Each queue is sorted by decreasing cost (rows x length of the
+ * other side), ties kept in (segment, head, block) order.
  */
 zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                         const int32_t* seq_heads, int32_t n_seg, const zl_segment* segs,
@@ -123,7 +125,8 @@ zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info);
 zl_status zl_plan_group(const zl_plan* plan, int32_t g, zl_group_info_t* info);
 
 /*
- * Copy a work queue to the host for inspection: which = 0 forward, 1 backward.
+ * Copy a work queue to the host for inspection: which = 0 forward, 1 backward dK/dV,
+ * 2 backward dQ (items of a ring group name its part-0 segment).
  * Each item is 4 int32: segment index, head, first row of the block, rows in the block.
  * Writes min(cap, count) items to out (may be NULL when cap == 0); *count gets the total.
  */
@@ -167,10 +170,11 @@ zl_status zl_lse_merge(int32_t n_parts, int64_t n_rows, int32_t d_head,
  * Backward (the exact backward of §V-A): gradients of f = sum over covered rows of
  * dO . O with respect to Q, K and V, given the final (merged) O and LSE.
  *   q, k, v, d_o   bf16 device tensors; o, lse the forward's final fp32 outputs
- *   dq             fp32 [q_rows][d]: zeroed and accumulated here for every covered row;
- *                  a KV-split group sums its parts
+ *   dq             fp32 [q_rows][d]: overwritten for every covered row; a KV-split group
+ *                  gets the sum over its parts
  *   dk, dv         fp32 [kv_rows][d]: overwritten for every covered row
- *   workspace      device memory of info.ws_bwd bytes (queue counter and row dot products)
+ *   workspace      device memory of info.ws_bwd bytes (queue counters and row dot products),
+ *                  not shared with a concurrent call
  * Rows that no segment covers are left untouched. Pointers must be 16-B aligned.
  */
 zl_status zl_attn_bwd(const zl_plan* plan, const void* q, const void* k, const void* v,

@@ -72,6 +72,34 @@ def test_queue_covers_every_block_once_in_cost_order(name, which):
             assert (a[0], a[1], a[2]) < (b[0], b[1], b[2]), "equal-cost items not in (segment, head, block) order"
 
 
+@pytest.mark.parametrize("name", ["tiny", "mixed", "ring"])
+def test_dq_queue(name):
+    """One dQ item per (final segment or ring group, head, 128 query rows), in decreasing cost
+    (rows x keys of the whole group) order; a ring group's items name its part-0 segment."""
+    pack = W.config(name)
+    p = host_plan(pack)
+    tiles = p.tiles(2)
+    assert p.info["dq_tiles"] == len(tiles)
+    owners = [i for i, s in enumerate(pack.segments) if s[7] <= 0]
+    keys_of = {}
+    for i in owners:
+        s = pack.segments[i]
+        if s[7] < 0:
+            keys_of[i] = s[6] - s[5]
+        else:
+            keys_of[i] = sum(t[6] - t[5] for t in pack.segments if t[7] >= 0 and t[:5] == s[:5])
+    seen = set()
+    for (seg, h, r0, n) in tiles:
+        assert seg in keys_of
+        s = pack.segments[seg]
+        assert s[1] <= h < s[2] and s[3] <= r0 and r0 + n <= s[4] and (r0 - s[3]) % 128 == 0
+        seen.add((seg, h, r0))
+    assert len(seen) == len(tiles) == sum((pack.segments[i][2] - pack.segments[i][1]) *
+                                          -(-(pack.segments[i][4] - pack.segments[i][3]) // 128) for i in owners)
+    costs = [t[3] * keys_of[t[0]] for t in tiles]
+    assert all(a >= b for a, b in zip(costs, costs[1:]))
+
+
 def test_ring_group_layout():
     pack = W.ring()
     p = host_plan(pack)
