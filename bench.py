@@ -75,6 +75,46 @@ def cpu_baseline(pack, ins, budget_s: float = 12.0) -> dict:
                       f"(queries x keys): {desc}; {flops / 1e12:.3f} TFLOP in {t_used:.1f} s"}
 
 
+KERNEL_SOURCES = [os.path.join(ROOT, "coalesced_varlen_attention_amd", "csrc", f)
+                  for f in ("zl_fwd.hip", "zl_bwd.hip", "zl_device.hpp", "zl_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, config: str):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary, if it was taken
+    on the current kernel sources (else None: the counters no longer describe this code)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    ent = rec.get(config, {}).get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent
+
+
+def calibrate_copy(gib: float = 2.0, reps: int = 3) -> int:
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n * 4, "reps": reps}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,7 +123,10 @@ def main() -> int:
     ap.add_argument("--config", default="mixed", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--calibrate-copy", action="store_true", help="run only a 2 GiB device copy (counter scale)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        return calibrate_copy()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding is a design, not a measured path", file=sys.stderr)
@@ -118,44 +161,58 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        if ev:
-            ev[0].record(stream)
+        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        rec(0)
         zl.attn_fwd(plan, q, k, v, o=o, lse=lse, o_part=o_part if has_groups else None,
                     lse_part=lse_part if has_groups else None, workspace=ws_f)
-        if ev:
-            ev[1].record(stream)
+        rec(1)
         if has_groups:
             zl.merge_groups(plan, o_part, lse_part, o, lse)
-        if ev:
-            ev[2].record(stream)
-        zl.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b)
-        if ev:
-            ev[3].record(stream)
+        rec(2)
+        zl.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b, stages=zl.BWD_PRE)
+        rec(3)
+        zl.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b, stages=zl.BWD_DKDV)
+        rec(4)
+        zl.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b, stages=zl.BWD_DQ)
+        rec(5)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    merge_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in events) / args.steps
+    fwd_ms, merge_ms, pre_ms, dkdv_ms, dq_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4), avg(4, 5)
+    bwd_ms = pre_ms + dkdv_ms + dq_ms
     ms_per_step = wall * 1e3 / args.steps
     flops_step = 3.5 * info["fwd_flops"]
     tflops = flops_step / (ms_per_step * 1e-3) / 1e12
-    bwd_tflops = info["bwd_flops"] / (bwd_ms * 1e-3) / 1e12
-    fwd_tflops = info["fwd_flops"] / (fwd_ms * 1e-3) / 1e12
-    # dominant kernel: the backward (71% of the step's flops), timed per launch with events
-    roof = {"bound": "mfma", "kernel": "bwd_kernel<128> (event time of zl_attn_bwd: pre-pass + main)",
-            "achieved": round(bwd_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(bwd_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
-            "fwd": {"kernel": "fwd_kernel<128>", "achieved": round(fwd_tflops, 2),
-                    "frac": round(fwd_tflops / BF16_PEAK_TFLOPS, 4)}}
+    # Per-kernel MFMA work (flops the kernel executes): forward 2 GEMMs (S, PV) = fwd_flops;
+    # dK/dV 4 GEMMs (S, dP, dV, dK) = 2 fwd_flops; dQ 3 GEMMs (S, dP, dQ) = 1.5 fwd_flops.
+    f = info["fwd_flops"]
+    kernels = {
+        "fwd_kernel": {"ms": fwd_ms, "flops": f},
+        "dkdv_kernel": {"ms": dkdv_ms, "flops": 2.0 * f},
+        "dq_kernel": {"ms": dq_ms, "flops": 1.5 * f},
+    }
+    for kname, kv in kernels.items():
+        kv["tflops"] = kv["flops"] / (kv["ms"] * 1e-3) / 1e12
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    dk_ = kernels[dom]
+    roof = {"bound": "mfma", "kernel": f"{dom}<{pack.d}>", "achieved": round(dk_["tflops"], 2),
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(dk_["tflops"] / BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "per_kernel": {n: {"ms": round(kv["ms"], 3), "tflops": round(kv["tflops"], 1),
+                               "frac": round(kv["tflops"] / BF16_PEAK_TFLOPS, 4)} for n, kv in kernels.items()}}
+    traffic = stored_traffic(dom, args.config)
+    if traffic is not None:
+        roof["traffic"] = traffic["bytes_per_launch"]
+        roof["traffic_source"] = traffic["source"]
     line = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -163,6 +220,7 @@ def main() -> int:
                        "fwd_bwd_tflop_per_step": round(flops_step / 1e12, 3),
                        "pct_of_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
                        "fwd_ms": round(fwd_ms, 3), "merge_ms": round(merge_ms, 3), "bwd_ms": round(bwd_ms, 3),
+                       "bwd_pre_ms": round(pre_ms, 3), "bwd_dkdv_ms": round(dkdv_ms, 3), "bwd_dq_ms": round(dq_ms, 3),
                        "plan_build_ms": round(plan_ms, 2), "parallelism": "none (1 GPU)"},
             "roofline": roof}
     if not args.no_cpu_baseline:

@@ -7,7 +7,7 @@ the exact LSE merge of ring parts. This module only marshals arguments: every st
 the computation runs in the HIP kernels behind the C ABI of ``include/zl.h``. PyTorch
 provides device memory and the current stream.
 
-If ``libzl.so`` is missing, importing this package raises: there is no fallback.
+If ``libzl.so`` is missing, the first call raises: there is no fallback.
 """
 from __future__ import annotations
 
@@ -15,12 +15,14 @@ import ctypes
 import os
 from typing import List, Optional, Sequence, Tuple
 
-__all__ = ["Plan", "ZlError", "attn_fwd", "attn_bwd", "lse_merge", "merge_groups", "lib_path", "SEGMENT_FIELDS"]
+__all__ = ["Plan", "ZlError", "attn_fwd", "attn_bwd", "lse_merge", "merge_groups", "lib", "lib_path",
+           "SEGMENT_FIELDS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libzl.so")
 
 ZL_PLAN_HOST_ONLY = 1
+BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 SEGMENT_FIELDS = ("seq", "head_begin", "head_end", "q_begin", "q_end", "kv_begin", "kv_end", "part")
 
 
@@ -64,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "zl_attn_fwd": (I32, [P, P, P, P, P, P, P, P, P, P]),
         "zl_lse_merge": (I32, [I32, I64, I32, P, P, P, P, P]),
         "zl_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, P]),
+        "zl_attn_bwd_stages": (I32, [P, P, P, P, P, P, P, P, P, P, P, U32, P]),
         "zl_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -73,7 +76,15 @@ def _load() -> ctypes.CDLL:
     return lib
 
 
-_lib = _load()
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libzl.so (loaded on first use; raises if it is missing or stale)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
 
 
 def lib_path() -> str:
@@ -82,7 +93,7 @@ def lib_path() -> str:
 
 def _check(status: int) -> None:
     if status != 0:
-        raise ZlError(status, _lib.zl_last_error().decode(errors="replace"))
+        raise ZlError(status, lib().zl_last_error().decode(errors="replace"))
 
 
 def _ptr(t) -> Optional[int]:
@@ -119,17 +130,17 @@ class Plan:
                 setattr(segs[i], name, int(val))
         self._h = ctypes.c_void_p()
         flags = ZL_PLAN_HOST_ONLY if host_only else 0
-        _check(_lib.zl_plan_build(n, ctypes.cast(cu_q, ctypes.c_void_p), ctypes.cast(cu_kv, ctypes.c_void_p),
+        _check(lib().zl_plan_build(n, ctypes.cast(cu_q, ctypes.c_void_p), ctypes.cast(cu_kv, ctypes.c_void_p),
                                   ctypes.cast(hs, ctypes.c_void_p), len(segments), ctypes.cast(segs, ctypes.c_void_p),
                                   int(d), float(scale) if scale else 0.0, flags, ctypes.byref(self._h)))
         info = _PlanInfo()
-        _check(_lib.zl_plan_info(self._h, ctypes.byref(info)))
+        _check(lib().zl_plan_info(self._h, ctypes.byref(info)))
         self.info = {name: getattr(info, name) for name, _ in _PlanInfo._fields_}
         self.d = int(d)
         self.groups: List[dict] = []
         for g in range(info.n_groups):
             gi = _GroupInfo()
-            _check(_lib.zl_plan_group(self._h, g, ctypes.byref(gi)))
+            _check(lib().zl_plan_group(self._h, g, ctypes.byref(gi)))
             self.groups.append({name: getattr(gi, name) for name, _ in _GroupInfo._fields_})
 
     @property
@@ -139,14 +150,14 @@ class Plan:
     def tiles(self, which: int) -> List[Tuple[int, int, int, int]]:
         """Work queue items (segment, head, first row, rows): 0 forward, 1 backward dK/dV, 2 backward dQ."""
         cnt = ctypes.c_int64()
-        _check(_lib.zl_plan_tiles(self._h, which, None, 0, ctypes.byref(cnt)))
+        _check(lib().zl_plan_tiles(self._h, which, None, 0, ctypes.byref(cnt)))
         buf = (ctypes.c_int32 * (4 * cnt.value))()
-        _check(_lib.zl_plan_tiles(self._h, which, ctypes.cast(buf, ctypes.c_void_p), cnt.value, ctypes.byref(cnt)))
+        _check(lib().zl_plan_tiles(self._h, which, ctypes.cast(buf, ctypes.c_void_p), cnt.value, ctypes.byref(cnt)))
         return [tuple(buf[4 * i:4 * i + 4]) for i in range(cnt.value)]
 
     def close(self) -> None:
         if getattr(self, "_h", None) and self._h.value:
-            _lib.zl_plan_destroy(self._h)
+            lib().zl_plan_destroy(self._h)
             self._h = ctypes.c_void_p()
 
     def __del__(self):
@@ -197,7 +208,7 @@ def attn_fwd(plan: Plan, q, k, v, o=None, lse=None, o_part=None, lse_part=None, 
         workspace = torch.empty(info["ws_fwd"], dtype=torch.uint8, device=dev)
     if workspace.numel() < info["ws_fwd"]:
         raise ValueError("workspace too small")
-    _check(_lib.zl_attn_fwd(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+    _check(lib().zl_attn_fwd(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             _ptr(o_part), _ptr(lse_part), workspace.data_ptr(), _stream_handle(stream)))
     return o, lse, o_part, lse_part
 
@@ -211,7 +222,7 @@ def lse_merge(n_parts: int, n_rows: int, d: int, o_part, lse_part, o, lse, strea
     for t, n in ((o_part, n_parts * n_rows * d), (lse_part, n_parts * n_rows), (o, n_rows * d), (lse, n_rows)):
         if not t.is_contiguous() or t.numel() < n:
             raise ValueError("lse_merge: tensor too small or not contiguous")
-    _check(_lib.zl_lse_merge(int(n_parts), int(n_rows), int(d), o_part.data_ptr(), lse_part.data_ptr(),
+    _check(lib().zl_lse_merge(int(n_parts), int(n_rows), int(d), o_part.data_ptr(), lse_part.data_ptr(),
                              o.data_ptr(), lse.data_ptr(), _stream_handle(stream)))
 
 
@@ -224,8 +235,12 @@ def merge_groups(plan: Plan, o_part, lse_part, o, lse, stream=None) -> None:
                   stream)
 
 
-def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Backward of every segment of ``plan`` (``zl_attn_bwd``): returns ``(dq, dk, dv)``."""
+def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None, stream=None,
+             stages: int = BWD_ALL):
+    """Backward of every segment of ``plan`` (``zl_attn_bwd_stages``): returns ``(dq, dk, dv)``.
+
+    ``stages`` selects launches (BWD_PRE, BWD_DKDV, BWD_DQ); DKDV and DQ need a PRE before
+    each of them on the same workspace."""
     import torch
     info, d, dev = plan.info, plan.d, q.device
     _check_tensor(q, "q", torch.bfloat16, info["q_rows"], d, dev)
@@ -247,7 +262,7 @@ def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspa
         workspace = torch.empty(info["ws_bwd"], dtype=torch.uint8, device=dev)
     if workspace.numel() < info["ws_bwd"]:
         raise ValueError("workspace too small")
-    _check(_lib.zl_attn_bwd(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                            _stream_handle(stream)))
+    _check(lib().zl_attn_bwd_stages(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                   workspace.data_ptr(), int(stages), _stream_handle(stream)))
     return dq, dk, dv

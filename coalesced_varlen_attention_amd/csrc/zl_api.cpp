@@ -157,6 +157,13 @@ extern "C" zl_status zl_lse_merge(int32_t n_parts, int64_t n_rows, int32_t d_hea
 extern "C" zl_status zl_attn_bwd(const zl_plan* plan, const void* q, const void* k, const void* v, const float* o,
                                  const float* lse, const void* d_o, float* dq, float* dk, float* dv, void* workspace,
                                  void* stream) {
+  return zl_attn_bwd_stages(plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, ZL_BWD_ALL, stream);
+}
+
+extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, const void* k, const void* v,
+                                        const float* o, const float* lse, const void* d_o, float* dq, float* dk,
+                                        float* dv, void* workspace, uint32_t stages, void* stream) {
+  if (stages == 0 || (stages & ~ZL_BWD_ALL)) return fail(ZL_ERR_INVALID, "zl_attn_bwd: bad stage mask");
   zl_status st = check_runnable(plan, "zl_attn_bwd");
   if (st != ZL_OK) return st;
   if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv || !workspace)
@@ -193,5 +200,5 @@ extern "C" zl_status zl_attn_bwd(const zl_plan* plan, const void* q, const void*
   const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, p.n_tiles);
   const int grid_dq = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu_dq, p.n_dq);
   const int grid_pre = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)plan->n_cu * 8, p.n_pre));
-  return launch_status(zl::launch_bwd(plan->d, p, grid_pre, grid, grid_dq, stream), "zl_attn_bwd");
+  return launch_status(zl::launch_bwd(plan->d, p, grid_pre, grid, grid_dq, stages, stream), "zl_attn_bwd");
 }

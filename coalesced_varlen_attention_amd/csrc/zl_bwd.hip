@@ -475,16 +475,16 @@ int dq_blocks_per_cu(int d) {
   return c;
 }
 
-int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, void* stream) {
+int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (d == 64) {
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(grid_pre), dim3(256), 0, s, p);
-    hipLaunchKernelGGL(dkdv_kernel<64>, dim3(grid), dim3(256), 0, s, p);
-    hipLaunchKernelGGL(dq_kernel<64>, dim3(grid_dq), dim3(256), 0, s, p);
+    if (stages & ZL_BWD_PRE) hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(grid_pre), dim3(256), 0, s, p);
+    if (stages & ZL_BWD_DKDV) hipLaunchKernelGGL(dkdv_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+    if (stages & ZL_BWD_DQ) hipLaunchKernelGGL(dq_kernel<64>, dim3(grid_dq), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid_pre), dim3(256), 0, s, p);
-    hipLaunchKernelGGL(dkdv_kernel<128>, dim3(grid), dim3(256), 0, s, p);
-    hipLaunchKernelGGL(dq_kernel<128>, dim3(grid_dq), dim3(256), 0, s, p);
+    if (stages & ZL_BWD_PRE) hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid_pre), dim3(256), 0, s, p);
+    if (stages & ZL_BWD_DKDV) hipLaunchKernelGGL(dkdv_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+    if (stages & ZL_BWD_DQ) hipLaunchKernelGGL(dq_kernel<128>, dim3(grid_dq), dim3(256), 0, s, p);
   }
   return hipPeekAtLastError() == hipSuccess ? 0 : 1;
 }

@@ -81,7 +81,7 @@ struct BwdParams {
 
 // Kernel launchers (defined next to their kernels). They return the launch status.
 int launch_fwd(int d, const FwdParams& p, int grid, void* stream);
-int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, void* stream);
+int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages, void* stream);
 int launch_merge(int d, int32_t n_parts, int64_t n_rows, const float* o_part, const float* lse_part,
                  float* o, float* lse, int grid, void* stream);
 // Workgroups of each persistent kernel that fit on one compute unit.

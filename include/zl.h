@@ -181,6 +181,23 @@ zl_status zl_attn_bwd(const zl_plan* plan, const void* q, const void* k, const v
                       const float* o, const float* lse, const void* d_o,
                       float* dq, float* dk, float* dv, void* workspace, void* stream);
 
+/* Stages of the backward, for zl_attn_bwd_stages. */
+#define ZL_BWD_PRE 1u   /* D_i = dO_i . O_i for every covered query row; resets both queues */
+#define ZL_BWD_DKDV 2u  /* key-major kernel: dK and dV */
+#define ZL_BWD_DQ 4u    /* query-major kernel: dQ */
+#define ZL_BWD_ALL 7u
+
+/*
+ * The backward split into its three launches, for callers that time or schedule them
+ * separately: `stages` is a non-zero mask of ZL_BWD_* bits, launched in the order PRE, DKDV,
+ * DQ. DKDV and DQ read what PRE left in `workspace`, and each consumes its queue: run PRE
+ * (on the same workspace and inputs) before every DKDV and every DQ. zl_attn_bwd is
+ * zl_attn_bwd_stages(..., ZL_BWD_ALL). Arguments as for zl_attn_bwd.
+ */
+zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, const void* k, const void* v,
+                             const float* o, const float* lse, const void* d_o,
+                             float* dq, float* dk, float* dv, void* workspace, uint32_t stages, void* stream);
+
 /* Thread-local message describing the last failure on this thread ("" if none). */
 const char* zl_last_error(void);
 

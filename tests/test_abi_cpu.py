@@ -28,4 +28,4 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_last_error_is_a_string():
-    assert isinstance(z._lib.zl_last_error(), bytes)
+    assert isinstance(z.lib().zl_last_error(), bytes)

@@ -103,3 +103,14 @@ def test_block_diagonal_separation_bitwise():
     for n in ("dk", "dv"):  # written once per row, no atomics: bitwise too
         assert torch.equal(a[n][q_other].cpu(), b[n][q_other].cpu()), n
     assert not torch.equal(a["o"][200:800].cpu(), b["o"][200:800].cpu())
+
+
+def test_bitwise_reproducible():
+    """No atomics on data: two runs of the same pack give identical bits (ring group included)."""
+    seg = ((0, 0, 2, 0, 300, 0, 200, 0), (0, 0, 2, 0, 300, 200, 500, 1), (1, 0, 3, 0, 129, 0, 129, -1))
+    pack = W.Pack("repro", (300, 129), (500, 129), (2, 3), seg, 128, 19)
+    ins = W.draw(pack)
+    a = H.run_pack(pack, ins)
+    b = H.run_pack(pack, ins)
+    for n in ("o", "lse", "dq", "dk", "dv", "o_part", "lse_part"):
+        assert torch.equal(a[n].cpu(), b[n].cpu()), n

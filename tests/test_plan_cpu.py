@@ -148,7 +148,7 @@ def test_validation_errors():
 
 
 def test_bad_sequence_arrays():
-    lib = z._lib
+    lib = z.lib()
     out = ctypes.c_void_p()
     seg = z._Segment(0, 0, 1, 0, 4, 0, 4, -1)
     cu_bad0 = (ctypes.c_int64 * 2)(1, 5)
@@ -173,7 +173,7 @@ def test_bad_sequence_arrays():
 
 def test_host_only_plan_cannot_run_and_merge_checks():
     p = host_plan(W.tiny())
-    lib = z._lib
+    lib = z.lib()
     assert lib.zl_attn_fwd(p.handle, 16, 16, 16, 16, 16, None, None, 16, None) == ZL_ERR_INVALID
     assert b"host-only" in lib.zl_last_error()
     assert lib.zl_attn_bwd(p.handle, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, None) == ZL_ERR_INVALID
