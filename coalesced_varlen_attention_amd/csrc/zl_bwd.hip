@@ -69,7 +69,7 @@ template <int D>
 struct KvCfg {
   static constexpr int kThreads = 256;
   static constexpr int kBq = kBwdRows;                    // 64 query rows per step
-  static constexpr int kQld = D + 8;                      // Q / dO row stride in LDS
+  static constexpr int kQld = LdsTile<D>::kLd;            // Q / dO row stride in LDS
   static constexpr int kSteps = D / 16;                   // k-steps over d
   static constexpr int kCb = D / 32;                      // 32-wide column blocks over d
   static constexpr int kQChunks = kBq * D / 8 / kThreads; // 16-B chunks per thread (Q or dO)
@@ -117,6 +117,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   const int hi = lane >> 5;
   const int r_in = (lane & 15) >> 2;                         // transposed-read row within 4
   const int c_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // transposed-read column within 32
+  const int prow_b = lds_row(l32);                             // physical row of this lane's operand row
+  const int prow_t = lds_row(4 * hi + r_in);                   // physical row of its transposed reads
   const bf16* __restrict__ gq = (const bf16*)p.q;
   const bf16* __restrict__ gk = (const bf16*)p.k;
   const bf16* __restrict__ gv = (const bf16*)p.v;
@@ -171,8 +173,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
         const int chunk = tid + c * C::kThreads;
         const int r = chunk / C::kRowChunks;
         const int col = (chunk % C::kRowChunks) * 8;
-        *(u32x4*)&q_lds[r * C::kQld + col] = qpre[c];
-        *(u32x4*)&do_lds[r * C::kQld + col] = dopre[c];
+        *(u32x4*)&q_lds[lds_row(r) * C::kQld + col] = qpre[c];
+        *(u32x4*)&do_lds[lds_row(r) * C::kQld + col] = dopre[c];
       }
       if (tid < C::kBq)
         lse_lds[tid] = lpre;
@@ -191,8 +193,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
       for (int mb = 0; mb < 2; ++mb) {
         sacc[mb] = f32x16{};
         dpacc[mb] = f32x16{};
-        const bf16* qa = &q_lds[(mb * 32 + l32) * C::kQld + 8 * hi];
-        const bf16* da = &do_lds[(mb * 32 + l32) * C::kQld + 8 * hi];
+        const bf16* qa = &q_lds[(mb * 32 + prow_b) * C::kQld + 8 * hi];
+        const bf16* da = &do_lds[(mb * 32 + prow_b) * C::kQld + 8 * hi];
 #pragma unroll
         for (int s = 0; s < C::kSteps; ++s) {
           sacc[mb] = mfma32(*(const bf16x8*)(qa + 16 * s), kreg[s], sacc[mb]);
@@ -228,16 +230,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
           dsb[mb * 2 + hs] = to_bf16x8(b);
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per step, in the k order of P's rows.
+      // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per step, in the k order of P's rows
+      // (logical rows +8 are physical rows +2).
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int row = (ks >> 1) * 32 + 16 * (ks & 1) + 4 * hi + r_in;
+        const int row = (ks >> 1) * 32 + 16 * (ks & 1) + prow_t;
 #pragma unroll
         for (int cb = 0; cb < C::kCb; ++cb) {
           const bf16* dp_ = &do_lds[row * C::kQld + cb * 32 + c_in];
           const bf16* qp_ = &q_lds[row * C::kQld + cb * 32 + c_in];
-          const bf16x8 a_do = cat(lds_read_tr(dp_), lds_read_tr(dp_ + 8 * C::kQld));
-          const bf16x8 a_q = cat(lds_read_tr(qp_), lds_read_tr(qp_ + 8 * C::kQld));
+          const bf16x8 a_do = cat(lds_read_tr(dp_), lds_read_tr(dp_ + 2 * C::kQld));
+          const bf16x8 a_q = cat(lds_read_tr(qp_), lds_read_tr(qp_ + 2 * C::kQld));
           dv_acc[cb] = mfma32(a_do, pb[ks], dv_acc[cb]);
           dk_acc[cb] = mfma32(a_q, dsb[ks], dk_acc[cb]);
         }
@@ -271,8 +274,8 @@ template <int D>
 struct DqCfg {
   static constexpr int kThreads = 256;
   static constexpr int kBk = 64;                          // keys per block
-  static constexpr int kKld = D + 16;                     // K row stride (natural and transposed reads)
-  static constexpr int kVld = D + 8;                      // V row stride (natural reads)
+  static constexpr int kKld = LdsTile<D>::kLd;            // K row stride (natural and transposed reads)
+  static constexpr int kVld = LdsTile<D>::kLd;            // V row stride (natural reads)
   static constexpr int kSteps = D / 16;
   static constexpr int kCb = D / 32;
   static constexpr int kChunks = kBk * D / 8 / kThreads;
@@ -305,8 +308,8 @@ __device__ __forceinline__ void dq_store_block(const u32x4 (&kreg)[DqCfg<D>::kCh
     const int chunk = tid + c * C::kThreads;
     const int r = chunk / C::kRowChunks;
     const int col = (chunk % C::kRowChunks) * 8;
-    *(u32x4*)&k_lds[r * C::kKld + col] = kreg[c];
-    *(u32x4*)&v_lds[r * C::kVld + col] = vreg[c];
+    *(u32x4*)&k_lds[lds_row(r) * C::kKld + col] = kreg[c];
+    *(u32x4*)&v_lds[lds_row(r) * C::kVld + col] = vreg[c];
   }
 }
 
@@ -340,6 +343,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
   const int hi = lane >> 5;
   const int r_in = (lane & 15) >> 2;
   const int c_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int prow_b = lds_row(l32);
+  const int prow_t = lds_row(4 * hi + r_in);
   const bf16* __restrict__ gq = (const bf16*)p.q;
   const bf16* __restrict__ gk = (const bf16*)p.k;
   const bf16* __restrict__ gv = (const bf16*)p.v;
@@ -404,8 +409,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 sacc = f32x16{}, dpacc = f32x16{};
-        const bf16* kr = &k_lds[buf][(kb * 32 + l32) * C::kKld + 8 * hi];
-        const bf16* vr = &v_lds[buf][(kb * 32 + l32) * C::kVld + 8 * hi];
+        const bf16* kr = &k_lds[buf][(kb * 32 + prow_b) * C::kKld + 8 * hi];
+        const bf16* vr = &v_lds[buf][(kb * 32 + prow_b) * C::kVld + 8 * hi];
 #pragma unroll
         for (int s = 0; s < C::kSteps; ++s) {
           sacc = mfma32(*(const bf16x8*)(kr + 16 * s), qreg[s], sacc);
@@ -426,11 +431,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
         }
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          const int row = kb * 32 + 16 * hs + 4 * hi + r_in;
+          const int row = kb * 32 + 16 * hs + prow_t;
 #pragma unroll
           for (int cb = 0; cb < C::kCb; ++cb) {
             const bf16* kp = &k_lds[buf][row * C::kKld + cb * 32 + c_in];
-            acc[cb] = mfma32(cat(lds_read_tr(kp), lds_read_tr(kp + 8 * C::kKld)), dsb[hs], acc[cb]);
+            acc[cb] = mfma32(cat(lds_read_tr(kp), lds_read_tr(kp + 2 * C::kKld)), dsb[hs], acc[cb]);
           }
         }
       }

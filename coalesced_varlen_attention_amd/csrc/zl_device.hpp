@@ -61,4 +61,18 @@ __device__ __forceinline__ float half_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS tiles of bf16 rows (d elements each) are stored with a row stride of d + 8 elements and
+// logical row r at physical row lds_row(r). The LDS has 64 banks of 4 bytes. The stride puts
+// consecutive physical rows 16 bytes apart modulo 256, so 16 lanes reading the same 16-byte
+// column of 16 rows hit distinct banks; the row permutation (within each group of 16 rows,
+// r -> 4*(r%4) + r/4) puts the 4 consecutive logical rows of a transposed read 4 physical
+// rows apart, so 32 lanes reading 4 rows x 64 bytes hit distinct banks as well. Both the
+// 16-byte operand reads and the transposed reads are then free of bank conflicts, and every
+// read address stays affine in the loop indices.
+template <int D>
+struct LdsTile {
+  static constexpr int kLd = D + 8;  // row stride in elements
+};
+__device__ __forceinline__ int lds_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
 }  // namespace zl

@@ -23,8 +23,7 @@ template <int D>
 struct FwdCfg {
   static constexpr int kThreads = 256;
   static constexpr int kBk = 64;                              // keys per block
-  static constexpr int kKld = D + 8;                          // K row stride in LDS (elements)
-  static constexpr int kVld = D + 16;                         // V row stride in LDS (elements)
+  static constexpr int kLd = LdsTile<D>::kLd;                 // K and V row stride in LDS (elements)
   static constexpr int kSteps = D / 16;                       // k-steps over d for S^T
   static constexpr int kCb = D / 32;                          // 32-wide column blocks of O^T
   static constexpr int kChunks = kBk * D / 8 / kThreads;      // 16-byte chunks per thread per block
@@ -59,8 +58,8 @@ __device__ __forceinline__ void fwd_store_block(const u32x4 (&kreg)[FwdCfg<D>::k
     const int chunk = tid + c * C::kThreads;
     const int r = chunk / C::kRowChunks;
     const int col = (chunk % C::kRowChunks) * 8;
-    *(u32x4*)&k_lds[r * C::kKld + col] = kreg[c];
-    *(u32x4*)&v_lds[r * C::kVld + col] = vreg[c];
+    *(u32x4*)&k_lds[lds_row(r) * C::kLd + col] = kreg[c];
+    *(u32x4*)&v_lds[lds_row(r) * C::kLd + col] = vreg[c];
   }
 }
 
@@ -69,8 +68,8 @@ __global__ void zero_counter_kernel(int32_t* counter) { *counter = 0; }
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][C::kBk * C::kKld];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][C::kBk * C::kVld];
+  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][C::kBk * C::kLd];
+  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][C::kBk * C::kLd];
   __shared__ int32_t s_item;
 
   const int tid = threadIdx.x;
@@ -78,6 +77,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int r_in = (lane & 15) >> 2;                        // transposed-read row within 4
+  const int c_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // transposed-read column within 32
+  const int prow_b = lds_row(l32);                           // physical row of this lane's operand row
+  const int prow_t = lds_row(4 * hi + r_in);                 // physical row of its transposed reads
   const bf16* __restrict__ gq = (const bf16*)p.q;
   const bf16* __restrict__ gk = (const bf16*)p.k;
   const bf16* __restrict__ gv = (const bf16*)p.v;
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         sacc[kb] = f32x16{};
-        const bf16* kr = &k_lds[buf][(kb * 32 + l32) * C::kKld + 8 * hi];
+        const bf16* kr = &k_lds[buf][(kb * 32 + prow_b) * C::kLd + 8 * hi];
 #pragma unroll
         for (int s = 0; s < C::kSteps; ++s) sacc[kb] = mfma32(*(const bf16x8*)(kr + 16 * s), qreg[s], sacc[kb]);
       }
@@ -149,10 +152,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = half_max(mx);
-      const float m_new = fmaxf(m_run, mx * p.scale_log2);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
+      mx = half_max(mx) * p.scale_log2;
+      // Lazy rescaling: the exponent reference m_run only moves when the block max exceeds it
+      // by more than kSlack (log2 units), so exponentials stay below 2^kSlack and the O and l
+      // rescale runs only when some lane of the wave needs it. The result is the same quantity;
+      // only the reference of the running sums changes.
+      constexpr float kSlack = 8.0f;
+      const bool need = mx > m_run + kSlack;
+      if (__any(need)) {
+        const float m_new = need ? mx : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < C::kCb; ++cb) oacc[cb] *= alpha;
+      }
 
       bf16x8 pb[4];
       float lsum = 0.f;
@@ -163,27 +177,23 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
           f32x8 e;
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            e[u] = fast_exp2(fmaf(sacc[kb][8 * hs + u], p.scale_log2, -m_new));
+            e[u] = fast_exp2(fmaf(sacc[kb][8 * hs + u], p.scale_log2, -m_run));
             lsum += e[u];
           }
           pb[kb * 2 + hs] = to_bf16x8(e);
         }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int cb = 0; cb < C::kCb; ++cb) oacc[cb] *= alpha;
+      l_run += lsum;
 
       // O^T[c][q] += V^T[c][key] P^T[key][q], 16 keys per step. The k order of P^T in this
       // lane is keys {16hs + 4hi + 0..3, 16hs + 8 + 4hi + 0..3} of each 32-key half; the two
-      // transposed reads fetch V rows in that same order.
-      const int r_in = (lane & 15) >> 2;
-      const int c_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      // transposed reads fetch V rows in that same order (logical rows +8 are physical rows +2).
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int row = (ks >> 1) * 32 + 16 * (ks & 1) + 4 * hi + r_in;
+        const int row = (ks >> 1) * 32 + 16 * (ks & 1) + prow_t;
 #pragma unroll
         for (int cb = 0; cb < C::kCb; ++cb) {
-          const bf16* vp = &v_lds[buf][row * C::kVld + cb * 32 + c_in];
-          const bf16x8 a = cat(lds_read_tr(vp), lds_read_tr(vp + 8 * C::kVld));
+          const bf16* vp = &v_lds[buf][row * C::kLd + cb * 32 + c_in];
+          const bf16x8 a = cat(lds_read_tr(vp), lds_read_tr(vp + 2 * C::kLd));
           oacc[cb] = mfma32(a, pb[ks], oacc[cb]);
         }
       }
