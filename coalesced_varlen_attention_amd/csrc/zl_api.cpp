@@ -61,7 +61,7 @@ extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   if (!plan || !info) return fail(ZL_ERR_INVALID, "zl_plan_info: NULL argument");
   std::memset(info, 0, sizeof(*info));
   info->ws_fwd = kCounterBytes;
-  info->ws_bwd = kCounterBytes + align256((size_t)plan->q_rows * sizeof(float));
+  info->ws_bwd = kCounterBytes + 2 * align256((size_t)plan->q_rows * sizeof(float));
   info->q_rows = plan->q_rows;
   info->kv_rows = plan->kv_rows;
   info->part_rows = plan->part_rows;
@@ -184,6 +184,7 @@ extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, cons
   p.counter = (int32_t*)workspace;
   p.dq_counter = (int32_t*)((char*)workspace + 64);
   p.dvec = (float*)((char*)workspace + kCounterBytes);
+  p.lse2 = (float*)((char*)workspace + kCounterBytes + align256((size_t)plan->q_rows * sizeof(float)));
   p.segs = plan->d_segs;
   p.tiles = plan->d_bwd;
   p.n_tiles = (int32_t)plan->bwd_tiles.size();

@@ -7,7 +7,9 @@
 // For a ring part the LSE and O are the merged ones, so P is the global softmax restricted
 // to the part's keys; dQ sums over every part of the group.
 //
-// Pre-pass: D for every covered query row; both queue counters zeroed.
+// Pre-pass: D and LSE log2(e) for every covered query row, stored head-major (row
+//   q_row0 + h * Lq + t of the sequence) so that the key-major kernel reads the 64 rows of a
+//   step as one contiguous 256-byte run; both queue counters zeroed.
 // dK/dV kernel: one item = 128 key rows of one (segment, head); 4 waves x 32 keys. Each wave
 //   keeps its K and V rows in registers as B operands of S = Q K^T and dP = dO V^T (lane = one
 //   key column), so P and dS come out of the MFMA already in the B-operand layout of
@@ -26,7 +28,8 @@ namespace zl {
 namespace {
 
 // ---------------------------------------------------------------------------------------------
-// Pre-pass: D_i = sum_c dO_ic O_ic for every covered query row (16 lanes per row).
+// Pre-pass: D_i = sum_c dO_ic O_ic and LSE_i log2(e) for every covered query row (16 lanes per
+// row), written head-major.
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
@@ -57,7 +60,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
       }
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-      if (sub == 0) p.dvec[row] = acc;
+      if (sub == 0) {
+        const int64_t hm = sg.q_row0 + (int64_t)h * sg.lq + tok;
+        p.dvec[hm] = acc;
+        p.lse2[hm] = p.lse[row] * 1.4426950408889634f;
+      }
     }
   }
 }
@@ -79,7 +86,7 @@ struct KvCfg {
 template <int D>
 __device__ __forceinline__ void kv_prefetch(u32x4 (&qpre)[KvCfg<D>::kQChunks], u32x4 (&dopre)[KvCfg<D>::kQChunks],
                                             float& lpre, const bf16* qbase, const bf16* dobase, int64_t rs,
-                                            int64_t rowbase, int nh, int q0, int nrow, const float* lse,
+                                            int64_t hmbase, int q0, int nrow, const float* lse2,
                                             const float* dvec, int tid) {
   using C = KvCfg<D>;
 #pragma unroll
@@ -91,13 +98,39 @@ __device__ __forceinline__ void kv_prefetch(u32x4 (&qpre)[KvCfg<D>::kQChunks], u
     qpre[c] = *(const u32x4*)(qbase + off);
     dopre[c] = *(const u32x4*)(dobase + off);
   }
-  if (tid < 2 * C::kBq) {
+  if (tid < 2 * C::kBq) {  // head-major rows: 64 consecutive floats per array
     const int r = tid & (C::kBq - 1);
-    const int64_t row = rowbase + (int64_t)(q0 + min(r, nrow - 1)) * nh;
+    const int64_t hm = hmbase + q0 + min(r, nrow - 1);
     if (tid < C::kBq)
-      lpre = r < nrow ? lse[row] * 1.4426950408889634f : INFINITY;  // rows past the end: P = 0
+      lpre = r < nrow ? lse2[hm] : INFINITY;  // rows past the end: P = 0
     else
-      lpre = r < nrow ? dvec[row] : 0.f;
+      lpre = r < nrow ? dvec[hm] : 0.f;
+  }
+}
+
+// P = exp2(S tau log2e - LSE log2e) and dS = P (dP - D) for one 32-row half of a step, rounded
+// to bf16 in the two B-operand halves (rows 8(i/4) + 4hi + i%4; lse and dd point at row 4hi).
+__device__ __forceinline__ void bwd_p_ds(const f32x16& sacc, const f32x16& dpacc, const float* lse,
+                                         const float* dd, bool k_valid, float scale_log2, bf16x8 (&pb)[2],
+                                         bf16x8 (&dsb)[2]) {
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    f32x8 a, b;
+#pragma unroll
+    for (int g2 = 0; g2 < 2; ++g2) {
+      const int g = 2 * hs + g2;
+      const f32x4 L = *(const f32x4*)&lse[8 * g];
+      const f32x4 Dd = *(const f32x4*)&dd[8 * g];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 4 * g + u;
+        const float pe = k_valid ? fast_exp2(fmaf(sacc[i], scale_log2, -L[u])) : 0.f;
+        a[4 * g2 + u] = pe;
+        b[4 * g2 + u] = pe * (dpacc[i] - Dd[u]);
+      }
+    }
+    pb[hs] = to_bf16x8(a);
+    dsb[hs] = to_bf16x8(b);
   }
 }
 
@@ -161,11 +194,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
     const int nqb = (n_q + C::kBq - 1) / C::kBq;
     const bf16* qbase = gq + (sg.q_row0 + (int64_t)sg.q_begin * nh + h) * D;
     const bf16* dobase = gdo + (sg.q_row0 + (int64_t)sg.q_begin * nh + h) * D;
-    const int64_t rowbase = sg.q_row0 + (int64_t)sg.q_begin * nh + h;  // query-side row of local token 0
+    const int64_t hmbase = sg.q_row0 + (int64_t)h * sg.lq + sg.q_begin;  // head-major row of local token 0
 
     u32x4 qpre[C::kQChunks], dopre[C::kQChunks];
     float lpre = 0.f;
-    kv_prefetch<D>(qpre, dopre, lpre, qbase, dobase, rs, rowbase, nh, 0, min(C::kBq, n_q), p.lse, p.dvec, tid);
+    kv_prefetch<D>(qpre, dopre, lpre, qbase, dobase, rs, hmbase, 0, min(C::kBq, n_q), p.lse2, p.dvec, tid);
     for (int qb = 0; qb < nqb; ++qb) {
       // Stage this step's Q, dO, LSE (log2 units) and D in LDS.
 #pragma unroll
@@ -183,68 +216,109 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
       __syncthreads();
       if (qb + 1 < nqb) {
         const int q0n = (qb + 1) * C::kBq;
-        kv_prefetch<D>(qpre, dopre, lpre, qbase, dobase, rs, rowbase, nh, q0n, min(C::kBq, n_q - q0n), p.lse,
+        kv_prefetch<D>(qpre, dopre, lpre, qbase, dobase, rs, hmbase, q0n, min(C::kBq, n_q - q0n), p.lse2,
                        p.dvec, tid);
       }
 
-      // S = Q K^T and dP = dO V^T: two 32-row blocks, lane = this wave's key column.
-      f32x16 sacc[2], dpacc[2];
+      // One step = two 32-row halves mb of the 64 query rows. For each half: S = Q K^T and
+      // dP = dO V^T (lane = this wave's key column; rows 8(i/4) + 4hi + i%4), then
+      // P = exp2(S tau log2e - LSE log2e), dS = P (dP - D), then dV^T += dO^T P and
+      // dK^T += Q^T dS with dO^T and Q^T from transposed reads (k order of P's rows; logical
+      // rows +8 are physical rows +2). The step is software-pipelined in four phases so that
+      // each wave keeps the matrix cores busy while it runs the exponentials of the other
+      // half and waits on LDS:
+      //   A: S, dP of half 0              | LDS: Q, dO operands of half 1
+      //   B: S, dP of half 1              | P, dS of half 0; LDS: transposed operands of half 0
+      //   C: dV, dK of half 0             | P, dS of half 1; LDS: transposed operands of half 1
+      //   D: dV, dK of half 1
+      constexpr int kS = C::kSteps;   // MFMAs per S (or dP) of one half
+      constexpr int kT = 2 * C::kCb;  // MFMAs per dV (or dK) of one half
+      bf16x8 qop0[kS], dop0[kS];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        sacc[mb] = f32x16{};
-        dpacc[mb] = f32x16{};
-        const bf16* qa = &q_lds[(mb * 32 + prow_b) * C::kQld + 8 * hi];
-        const bf16* da = &do_lds[(mb * 32 + prow_b) * C::kQld + 8 * hi];
-#pragma unroll
-        for (int s = 0; s < C::kSteps; ++s) {
-          sacc[mb] = mfma32(*(const bf16x8*)(qa + 16 * s), kreg[s], sacc[mb]);
-          dpacc[mb] = mfma32(*(const bf16x8*)(da + 16 * s), vreg[s], dpacc[mb]);
-        }
+      for (int s = 0; s < kS; ++s) {
+        qop0[s] = *(const bf16x8*)&q_lds[prow_b * C::kQld + 8 * hi + 16 * s];
+        dop0[s] = *(const bf16x8*)&do_lds[prow_b * C::kQld + 8 * hi + 16 * s];
       }
-      // P = exp2(S tau log2e - LSE log2e), dS = P (dP - D); rows 8(i/4) + 4hi + i%4.
-      bf16x8 pb[4], dsb[4];
+      // Phase A.
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 s0 = f32x16{}, dp0 = f32x16{};
+      bf16x8 qop1[kS], dop1[kS];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x16 pv, dsv;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 L = *(const f32x4*)&lse_lds[mb * 32 + 8 * g + 4 * hi];
-          const f32x4 Dd = *(const f32x4*)&dd_lds[mb * 32 + 8 * g + 4 * hi];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = 4 * g + u;
-            const float pe = k_valid ? fast_exp2(fmaf(sacc[mb][i], p.scale_log2, -L[u])) : 0.f;
-            pv[i] = pe;
-            dsv[i] = pe * (dpacc[mb][i] - Dd[u]);
-          }
-        }
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          f32x8 a, b;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            a[u] = pv[8 * hs + u];
-            b[u] = dsv[8 * hs + u];
-          }
-          pb[mb * 2 + hs] = to_bf16x8(a);
-          dsb[mb * 2 + hs] = to_bf16x8(b);
-        }
+      for (int s = 0; s < kS; ++s) {
+        s0 = mfma32(qop0[s], kreg[s], s0);
+        dp0 = mfma32(dop0[s], vreg[s], dp0);
+        qop1[s] = *(const bf16x8*)&q_lds[(32 + prow_b) * C::kQld + 8 * hi + 16 * s];
+        dop1[s] = *(const bf16x8*)&do_lds[(32 + prow_b) * C::kQld + 8 * hi + 16 * s];
       }
-      // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per step, in the k order of P's rows
-      // (logical rows +8 are physical rows +2).
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int row = (ks >> 1) * 32 + 16 * (ks & 1) + prow_t;
+      for (int s = 0; s < kS; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase B.
+      f32x16 s1 = f32x16{}, dp1 = f32x16{};
+#pragma unroll
+      for (int s = 0; s < kS; ++s) {
+        s1 = mfma32(qop1[s], kreg[s], s1);
+        dp1 = mfma32(dop1[s], vreg[s], dp1);
+      }
+      bf16x8 pb[2], dsb[2];
+      bwd_p_ds(s0, dp0, &lse_lds[4 * hi], &dd_lds[4 * hi], k_valid, p.scale_log2, pb, dsb);
+      bf16x8 tdo[kT / 2][2], tq[kT / 2][2];
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
         for (int cb = 0; cb < C::kCb; ++cb) {
+          const int row = 16 * hs + prow_t;
           const bf16* dp_ = &do_lds[row * C::kQld + cb * 32 + c_in];
           const bf16* qp_ = &q_lds[row * C::kQld + cb * 32 + c_in];
-          const bf16x8 a_do = cat(lds_read_tr(dp_), lds_read_tr(dp_ + 2 * C::kQld));
-          const bf16x8 a_q = cat(lds_read_tr(qp_), lds_read_tr(qp_ + 2 * C::kQld));
-          dv_acc[cb] = mfma32(a_do, pb[ks], dv_acc[cb]);
-          dk_acc[cb] = mfma32(a_q, dsb[ks], dk_acc[cb]);
+          tdo[cb][hs] = cat(lds_read_tr(dp_), lds_read_tr(dp_ + 2 * C::kQld));
+          tq[cb][hs] = cat(lds_read_tr(qp_), lds_read_tr(qp_ + 2 * C::kQld));
         }
+#pragma unroll
+      for (int s = 0; s < 2 * kS; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase C.
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int cb = 0; cb < C::kCb; ++cb) {
+          dv_acc[cb] = mfma32(tdo[cb][hs], pb[hs], dv_acc[cb]);
+          dk_acc[cb] = mfma32(tq[cb][hs], dsb[hs], dk_acc[cb]);
+        }
+      bf16x8 pb1[2], dsb1[2];
+      bwd_p_ds(s1, dp1, &lse_lds[32 + 4 * hi], &dd_lds[32 + 4 * hi], k_valid, p.scale_log2, pb1, dsb1);
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int cb = 0; cb < C::kCb; ++cb) {
+          const int row = 32 + 16 * hs + prow_t;
+          const bf16* dp_ = &do_lds[row * C::kQld + cb * 32 + c_in];
+          const bf16* qp_ = &q_lds[row * C::kQld + cb * 32 + c_in];
+          tdo[cb][hs] = cat(lds_read_tr(dp_), lds_read_tr(dp_ + 2 * C::kQld));
+          tq[cb][hs] = cat(lds_read_tr(qp_), lds_read_tr(qp_ + 2 * C::kQld));
+        }
+#pragma unroll
+      for (int s = 0; s < 2 * kT; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase D.
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int cb = 0; cb < C::kCb; ++cb) {
+          dv_acc[cb] = mfma32(tdo[cb][hs], pb1[hs], dv_acc[cb]);
+          dk_acc[cb] = mfma32(tq[cb][hs], dsb1[hs], dk_acc[cb]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     }
 
@@ -373,8 +447,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
       qreg[s] = *(const bf16x8*)(gq + qrow * D + 8 * hi + 16 * s);
       doreg[s] = *(const bf16x8*)(gdo + qrow * D + 8 * hi + 16 * s);
     }
-    const float lse2 = p.lse[qrow] * 1.4426950408889634f;
-    const float dd = p.dvec[qrow];
+    const int64_t hm = sg.q_row0 + (int64_t)h * sg.lq + qtok;
+    const float lse2 = p.lse2[hm];
+    const float dd = p.dvec[hm];
 
     int n_blk = 0;
     for (int r = 0; r < sg.chain_len; ++r) {

@@ -31,8 +31,10 @@ struct alignas(16) SegDev {
   int32_t part;
   int32_t chain_off;  // first (kv_begin, kv_end) pair of this segment's key-range chain
   int32_t chain_len;  // pairs in the chain: 1, or the parts of a ring group (on part 0)
+  int32_t lq;         // query tokens of the sequence (head-major row = q_row0 + h * lq + t)
+  int32_t pad[3];
 };
-static_assert(sizeof(SegDev) == 64, "SegDev must stay 64 bytes");
+static_assert(sizeof(SegDev) == 80, "SegDev must stay 80 bytes");
 
 // One work item: segment index, head, first row (token) of the block, rows in the block.
 struct alignas(16) Tile {
@@ -64,7 +66,8 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
-  float* dvec;  // per query row: sum_c dO * O (workspace)
+  float* dvec;  // per query row: sum_c dO * O, head-major rows (workspace)
+  float* lse2;  // per query row: LSE * log2(e), head-major rows (workspace)
   const SegDev* segs;
   const Tile* tiles;
   int32_t n_tiles;

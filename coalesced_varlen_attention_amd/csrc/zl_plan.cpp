@@ -208,6 +208,7 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     d.q_row0 = qoff[g.seq];
     d.kv_row0 = kvoff[g.seq];
     d.nh = seq_heads[g.seq];
+    d.lq = (int32_t)lq[g.seq];
     d.q_begin = g.q_begin;
     d.q_end = g.q_end;
     d.kv_begin = g.kv_begin;
