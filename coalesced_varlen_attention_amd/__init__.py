@@ -62,6 +62,7 @@ def _load() -> ctypes.CDLL:
         "zl_plan_info": (I32, [P, ctypes.POINTER(_PlanInfo)]),
         "zl_plan_group": (I32, [P, I32, ctypes.POINTER(_GroupInfo)]),
         "zl_plan_tiles": (I32, [P, I32, P, I64, ctypes.POINTER(I64)]),
+        "zl_plan_queues": (I32, [P, I32, P, I32, ctypes.POINTER(I32)]),
         "zl_plan_destroy": (None, [P]),
         "zl_attn_fwd": (I32, [P, P, P, P, P, P, P, P, P, P]),
         "zl_lse_merge": (I32, [I32, I64, I32, P, P, P, P, P]),
@@ -154,6 +155,13 @@ class Plan:
         buf = (ctypes.c_int32 * (4 * cnt.value))()
         _check(lib().zl_plan_tiles(self._h, which, ctypes.cast(buf, ctypes.c_void_p), cnt.value, ctypes.byref(cnt)))
         return [tuple(buf[4 * i:4 * i + 4]) for i in range(cnt.value)]
+
+    def queues(self, which: int) -> List[int]:
+        """Queue boundaries of a work list: items bounds[k]:bounds[k+1] of tiles(which) form queue k."""
+        n = ctypes.c_int32()
+        buf = (ctypes.c_int32 * 64)()
+        _check(lib().zl_plan_queues(self._h, which, ctypes.cast(buf, ctypes.c_void_p), 64, ctypes.byref(n)))
+        return list(buf[: n.value + 1])
 
     def close(self) -> None:
         if getattr(self, "_h", None) and self._h.value:

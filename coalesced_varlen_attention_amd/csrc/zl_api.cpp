@@ -26,7 +26,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr size_t kCounterBytes = 256;
+// Queue counters at the head of each workspace: forward kQueues, backward 2 x kQueues, each
+// kCounterStride ints apart.
+constexpr size_t kCounterBytes = 2 * zl::kQueues * zl::kCounterStride * sizeof(int32_t);
 
 zl_status check_runnable(const zl_plan* plan, const char* who) {
   if (!plan) return fail(ZL_ERR_INVALID, std::string(who) + ": plan is NULL");
@@ -102,6 +104,17 @@ extern "C" zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* 
   return ZL_OK;
 }
 
+extern "C" zl_status zl_plan_queues(const zl_plan* plan, int32_t which, int32_t* bounds, int32_t cap,
+                                    int32_t* n_queues) {
+  if (!plan || !n_queues) return fail(ZL_ERR_INVALID, "zl_plan_queues: NULL argument");
+  if (which < 0 || which > 2) return fail(ZL_ERR_INVALID, "zl_plan_queues: which must be 0, 1 or 2");
+  const auto& b = which == 0 ? plan->fwd_bounds : which == 1 ? plan->bwd_bounds : plan->dq_bounds;
+  *n_queues = zl::kQueues;
+  if (cap < 0 || (cap > 0 && !bounds)) return fail(ZL_ERR_INVALID, "zl_plan_queues: bad output buffer");
+  for (int32_t i = 0; i < std::min<int32_t>(cap, (int32_t)b.size()); ++i) bounds[i] = b[i];
+  return ZL_OK;
+}
+
 extern "C" zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void* k, const void* v, float* o,
                                  float* lse, float* o_part, float* lse_part, void* workspace, void* stream) {
   zl_status st = check_runnable(plan, "zl_attn_fwd");
@@ -123,13 +136,11 @@ extern "C" zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void*
   p.o_part = o_part;
   p.lse_part = lse_part;
   p.segs = plan->d_segs;
-  p.tiles = plan->d_fwd;
-  p.n_tiles = (int32_t)plan->fwd_tiles.size();
-  p.counter = (int32_t*)workspace;
+  p.queue = {plan->d_fwd, plan->d_bounds, (int32_t*)workspace};
   p.scale_log2 = plan->scale * 1.4426950408889634f;
   const int per_cu = zl::fwd_blocks_per_cu(plan->d);
   if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_fwd: forward kernel cannot be resident");
-  const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, p.n_tiles);
+  const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, (int64_t)plan->fwd_tiles.size());
   return launch_status(zl::launch_fwd(plan->d, p, grid, stream), "zl_attn_fwd");
 }
 
@@ -181,25 +192,22 @@ extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, cons
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.counter = (int32_t*)workspace;
-  p.dq_counter = (int32_t*)((char*)workspace + 64);
+  p.kvq = {plan->d_bwd, plan->d_bounds + (zl::kQueues + 1), (int32_t*)workspace};
+  p.dqq = {plan->d_dq, plan->d_bounds + 2 * (zl::kQueues + 1),
+           (int32_t*)workspace + zl::kQueues * zl::kCounterStride};
   p.dvec = (float*)((char*)workspace + kCounterBytes);
   p.lse2 = (float*)((char*)workspace + kCounterBytes + align256((size_t)plan->q_rows * sizeof(float)));
   p.segs = plan->d_segs;
-  p.tiles = plan->d_bwd;
-  p.n_tiles = (int32_t)plan->bwd_tiles.size();
   p.pre_tiles = plan->d_pre;
   p.n_pre = (int32_t)plan->pre_tiles.size();
-  p.dq_tiles = plan->d_dq;
-  p.n_dq = (int32_t)plan->dq_tiles.size();
   p.kv_ranges = plan->d_ranges;
   p.scale = plan->scale;
   p.scale_log2 = plan->scale * 1.4426950408889634f;
   const int per_cu = zl::bwd_blocks_per_cu(plan->d);
   const int per_cu_dq = zl::dq_blocks_per_cu(plan->d);
   if (per_cu < 1 || per_cu_dq < 1) return fail(ZL_ERR_HIP, "zl_attn_bwd: backward kernels cannot be resident");
-  const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, p.n_tiles);
-  const int grid_dq = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu_dq, p.n_dq);
+  const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, (int64_t)plan->bwd_tiles.size());
+  const int grid_dq = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu_dq, (int64_t)plan->dq_tiles.size());
   const int grid_pre = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)plan->n_cu * 8, p.n_pre));
   return launch_status(zl::launch_bwd(plan->d, p, grid_pre, grid, grid_dq, stages, stream), "zl_attn_bwd");
 }

@@ -33,9 +33,9 @@ namespace {
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    *p.counter = 0;
-    *p.dq_counter = 0;
+  if (blockIdx.x == 0 && threadIdx.x < kQueues) {
+    p.kvq.counters[threadIdx.x * kCounterStride] = 0;
+    p.dqq.counters[threadIdx.x * kCounterStride] = 0;
   }
   constexpr int kPer = D / 16;  // elements per lane
   const int sub = threadIdx.x & 15;
@@ -157,12 +157,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   const bf16* __restrict__ gv = (const bf16*)p.v;
   const bf16* __restrict__ gdo = (const bf16*)p.d_o;
 
+  const int home = blockIdx.x % kQueues;
+  int drained = 0;
   for (;;) {
-    if (tid == 0) s_item = atomicAdd(p.counter, 1);
+    if (tid == 0) s_item = take_item(p.kvq, home, drained);
     __syncthreads();
     const int item = s_item;
-    if (item >= p.n_tiles) break;
-    const Tile tile = p.tiles[item];
+    if (item < 0) break;
+    const Tile tile = p.kvq.items[item];
     const SegDev sg = p.segs[tile.seg];
     const int nh = sg.nh;
     const int h = tile.head;
@@ -424,12 +426,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
   const bf16* __restrict__ gv = (const bf16*)p.v;
   const bf16* __restrict__ gdo = (const bf16*)p.d_o;
 
+  const int home = blockIdx.x % kQueues;
+  int drained = 0;
   for (;;) {
-    if (tid == 0) s_item = atomicAdd(p.dq_counter, 1);
+    if (tid == 0) s_item = take_item(p.dqq, home, drained);
     __syncthreads();
     const int item = s_item;
-    if (item >= p.n_dq) break;
-    const Tile tile = p.dq_tiles[item];
+    if (item < 0) break;
+    const Tile tile = p.dqq.items[item];
     const SegDev sg = p.segs[tile.seg];
     const int nh = sg.nh;
     const int h = tile.head;

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "zl_internal.h"
+
 namespace zl {
 
 typedef __bf16 bf16;
@@ -74,5 +76,18 @@ struct LdsTile {
   static constexpr int kLd = D + 8;  // row stride in elements
 };
 __device__ __forceinline__ int lds_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Next work item for a workgroup (called by one thread): its own XCD's queue first, then the
+// others in order. `drained` counts the queues found empty and only grows, so every
+// workgroup stops after at most (its items + kQueues) atomics. Returns -1 when all are empty.
+__device__ __forceinline__ int take_item(const Queues& q, int home, int& drained) {
+  while (drained < kQueues) {
+    const int k = (home + drained) & (kQueues - 1);
+    const int idx = q.bounds[k] + atomicAdd(&q.counters[k * kCounterStride], 1);
+    if (idx < q.bounds[k + 1]) return idx;
+    ++drained;
+  }
+  return -1;
+}
 
 }  // namespace zl

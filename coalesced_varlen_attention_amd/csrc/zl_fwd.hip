@@ -1,4 +1,5 @@
-// Forward kernel: persistent, cost-ordered queue of (segment, head, 128 query rows) items.
+// Forward kernel: persistent, per-XCD cost-ordered queues of (segment, head, 128 query rows)
+// items.
 //
 // Computes, per item, softmax attention of 128 query rows against the segment's key rows
 // (dense bidirectional attention of one sequence, Zellige page §II-A; segments never read
@@ -63,7 +64,7 @@ __device__ __forceinline__ void fwd_store_block(const u32x4 (&kreg)[FwdCfg<D>::k
   }
 }
 
-__global__ void zero_counter_kernel(int32_t* counter) { *counter = 0; }
+__global__ void zero_counters_kernel(int32_t* counters) { counters[threadIdx.x * kCounterStride] = 0; }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
@@ -85,12 +86,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   const bf16* __restrict__ gk = (const bf16*)p.k;
   const bf16* __restrict__ gv = (const bf16*)p.v;
 
+  const int home = blockIdx.x % kQueues;
+  int drained = 0;
   for (;;) {
-    if (tid == 0) s_item = atomicAdd(p.counter, 1);
+    if (tid == 0) s_item = take_item(p.queue, home, drained);
     __syncthreads();
     const int item = s_item;
-    if (item >= p.n_tiles) break;
-    const Tile tile = p.tiles[item];
+    if (item < 0) break;
+    const Tile tile = p.queue.items[item];
     const SegDev sg = p.segs[tile.seg];
     const int nh = sg.nh;
     const int h = tile.head;
@@ -250,7 +253,7 @@ int fwd_blocks_per_cu(int d) { return d == 64 ? blocks_per_cu_impl<64>() : block
 
 int launch_fwd(int d, const FwdParams& p, int grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(1), 0, s, p.counter);
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(kQueues), 0, s, p.queue.counters);
   if (d == 64)
     hipLaunchKernelGGL(fwd_kernel<64>, dim3(grid), dim3(256), 0, s, p);
   else

@@ -19,6 +19,10 @@ constexpr int kBwdKeys = 128;
 constexpr int kBwdRows = 64;
 // Rows (token, head pairs) per item of the backward pre-pass.
 constexpr int kPreRows = 256;
+// Work queues per launch: one per XCD. Workgroup b starts on queue b % kQueues (the XCD the
+// hardware dispatches it to) and steals from the others once its own queue is empty.
+constexpr int kQueues = 8;
+constexpr int kCounterStride = 16;  // ints between queue counters (64 bytes)
 
 // A segment as the kernels see it. Rows are (token, head) pairs of d contiguous values.
 struct alignas(16) SegDev {
@@ -41,6 +45,14 @@ struct alignas(16) Tile {
   int32_t seg, head, row0, nrows;
 };
 
+// A set of kQueues work queues: items stored queue by queue, bounds[k]..bounds[k+1] for
+// queue k, and one counter per queue (kCounterStride ints apart) in the caller's workspace.
+struct Queues {
+  const Tile* items;
+  const int32_t* bounds;
+  int32_t* counters;
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -50,9 +62,7 @@ struct FwdParams {
   float* o_part;
   float* lse_part;
   const SegDev* segs;
-  const Tile* tiles;
-  int32_t n_tiles;
-  int32_t* counter;
+  Queues queue;
   float scale_log2;  // softmax scale times log2(e)
 };
 
@@ -69,15 +79,11 @@ struct BwdParams {
   float* dvec;  // per query row: sum_c dO * O, head-major rows (workspace)
   float* lse2;  // per query row: LSE * log2(e), head-major rows (workspace)
   const SegDev* segs;
-  const Tile* tiles;
-  int32_t n_tiles;
+  Queues kvq;             // dK/dV queues
+  Queues dqq;             // dQ queues
   const Tile* pre_tiles;  // (segment, head_begin, first token, tokens) per pre-pass item
   int32_t n_pre;
-  const Tile* dq_tiles;   // dQ queue
-  int32_t n_dq;
   const int32_t* kv_ranges;  // (kv_begin, kv_end) pairs of the key-range chains
-  int32_t* counter;     // dK/dV queue counter
-  int32_t* dq_counter;  // dQ queue counter
   float scale;       // softmax scale
   float scale_log2;  // softmax scale times log2(e)
 };
@@ -107,7 +113,8 @@ struct zl_plan {
   int32_t n_parts_max = 0;
   double fwd_flops = 0.0;
   std::vector<zl::SegDev> segs;
-  std::vector<zl::Tile> fwd_tiles, bwd_tiles, pre_tiles, dq_tiles;
+  std::vector<zl::Tile> fwd_tiles, bwd_tiles, pre_tiles, dq_tiles;  // queue by queue
+  std::vector<int32_t> fwd_bounds, bwd_bounds, dq_bounds;            // kQueues + 1 each
   std::vector<int32_t> kv_ranges;
   std::vector<zl_group_info_t> groups;
   // device copies (one allocation, carved into the three tables)
@@ -118,4 +125,5 @@ struct zl_plan {
   const zl::Tile* d_pre = nullptr;
   const zl::Tile* d_dq = nullptr;
   const int32_t* d_ranges = nullptr;
+  const int32_t* d_bounds = nullptr;  // fwd, bwd, dq bounds, kQueues + 1 each
 };

@@ -64,6 +64,59 @@ bool find_overlap(std::vector<Rect>& rs, bool same_group_ok, int* a, int* b) {
   return false;
 }
 
+struct Item {
+  zl::Tile t;
+  int64_t cost;
+};
+
+// Split the items (in (segment, head, block) order) into chunks of consecutive items of one
+// unit with bounded total cost, assign the chunks to the kQueues queues by decreasing chunk
+// cost to the least-loaded queue, and emit each queue sorted by decreasing item cost (stable).
+void distribute(const std::vector<Item>& items, const std::vector<int64_t>& unit, std::vector<zl::Tile>* out,
+                std::vector<int32_t>* bounds) {
+  int64_t total = 0, biggest = 0;
+  for (const Item& it : items) {
+    total += it.cost;
+    biggest = std::max(biggest, it.cost);
+  }
+  const int64_t cap = std::max<int64_t>(biggest, total / (zl::kQueues * 16) + 1);
+  struct Chunk {
+    size_t begin, end;
+    int64_t cost;
+  };
+  std::vector<Chunk> chunks;
+  for (size_t i = 0; i < items.size();) {
+    Chunk c{i, i, 0};
+    while (c.end < items.size() && unit[c.end] == unit[i] && (c.end == i || c.cost + items[c.end].cost <= cap)) {
+      c.cost += items[c.end].cost;
+      ++c.end;
+    }
+    chunks.push_back(c);
+    i = c.end;
+  }
+  std::vector<size_t> order(chunks.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) { return chunks[a].cost > chunks[b].cost; });
+  std::vector<int64_t> load(zl::kQueues, 0);
+  std::vector<std::vector<size_t>> members(zl::kQueues);
+  for (size_t ci : order) {
+    const int q = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[q] += chunks[ci].cost;
+    members[q].push_back(ci);
+  }
+  out->clear();
+  bounds->assign(1, 0);
+  for (int q = 0; q < zl::kQueues; ++q) {
+    std::sort(members[q].begin(), members[q].end());  // back to (segment, head, block) order
+    std::vector<Item> mine;
+    for (size_t ci : members[q])
+      for (size_t k = chunks[ci].begin; k < chunks[ci].end; ++k) mine.push_back(items[k]);
+    std::stable_sort(mine.begin(), mine.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
+    for (const Item& it : mine) out->push_back(it.t);
+    bounds->push_back((int32_t)out->size());
+  }
+}
+
 }  // namespace
 
 extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int64_t* cu_kv,
@@ -245,12 +298,12 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     d.chain_len = (int32_t)members.size();
   }
 
-  // Work queues, sorted by decreasing cost with a stable tie order.
-  struct Item {
-    zl::Tile t;
-    int64_t cost;
-  };
+  // Work queues. Items of one (segment, head) that share K/V (forward, dQ) or Q/dO (dK/dV)
+  // are grouped into chunks of bounded cost; chunks go to the kQueues per-XCD queues by
+  // longest-processing-time-first, so that each head's data is mostly read through one XCD's
+  // L2; each queue is then sorted by decreasing item cost with a stable tie order.
   std::vector<Item> fwd, bwd, dq;
+  std::vector<int64_t> fwd_unit, bwd_unit, dq_unit;  // (segment, head) unit of each item
   for (int i = 0; i < n_seg; ++i) {
     const zl_segment& g = segs[i];
     const int64_t nq = g.q_end - g.q_begin, nk = g.kv_end - g.kv_begin;
@@ -258,14 +311,20 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     for (int c = 0; c < plan->segs[i].chain_len; ++c)
       chain_keys += plan->kv_ranges[2 * (plan->segs[i].chain_off + c) + 1] - plan->kv_ranges[2 * (plan->segs[i].chain_off + c)];
     for (int h = g.head_begin; h < g.head_end; ++h) {
+      const int64_t unit = (int64_t)i * 65536 + h;
       for (int64_t r = g.q_begin; r < g.q_end; r += zl::kFwdRows) {
         const int32_t n = (int32_t)std::min<int64_t>(zl::kFwdRows, g.q_end - r);
         fwd.push_back({{i, h, (int32_t)r, n}, (int64_t)n * nk});
-        if (g.part <= 0) dq.push_back({{i, h, (int32_t)r, n}, (int64_t)n * chain_keys});
+        fwd_unit.push_back(unit);
+        if (g.part <= 0) {
+          dq.push_back({{i, h, (int32_t)r, n}, (int64_t)n * chain_keys});
+          dq_unit.push_back(unit);
+        }
       }
       for (int64_t r = g.kv_begin; r < g.kv_end; r += zl::kBwdKeys) {
         const int32_t n = (int32_t)std::min<int64_t>(zl::kBwdKeys, g.kv_end - r);
         bwd.push_back({{i, h, (int32_t)r, n}, (int64_t)n * nq});
+        bwd_unit.push_back(unit);
       }
     }
     // Backward pre-pass rows: once per output row set (a ring group does it on part 0).
@@ -278,13 +337,9 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   }
   if (fwd.size() > (size_t)INT32_MAX || bwd.size() > (size_t)INT32_MAX || plan->pre_tiles.size() > (size_t)INT32_MAX)
     return fail(ZL_ERR_INVALID, "zl_plan_build: too many work items");
-  auto by_cost = [](const Item& a, const Item& b) { return a.cost > b.cost; };
-  std::stable_sort(fwd.begin(), fwd.end(), by_cost);
-  std::stable_sort(bwd.begin(), bwd.end(), by_cost);
-  std::stable_sort(dq.begin(), dq.end(), by_cost);
-  for (auto& it : fwd) plan->fwd_tiles.push_back(it.t);
-  for (auto& it : bwd) plan->bwd_tiles.push_back(it.t);
-  for (auto& it : dq) plan->dq_tiles.push_back(it.t);
+  distribute(fwd, fwd_unit, &plan->fwd_tiles, &plan->fwd_bounds);
+  distribute(bwd, bwd_unit, &plan->bwd_tiles, &plan->bwd_bounds);
+  distribute(dq, dq_unit, &plan->dq_tiles, &plan->dq_bounds);
 
   if (!(flags & ZL_PLAN_HOST_ONLY)) {
     if (hipGetDevice(&plan->device) != hipSuccess) return fail(ZL_ERR_HIP, "zl_plan_build: hipGetDevice failed");
@@ -298,7 +353,8 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     const size_t b_pre = align(plan->pre_tiles.size() * sizeof(zl::Tile));
     const size_t b_dq = align(plan->dq_tiles.size() * sizeof(zl::Tile));
     const size_t b_rng = align(plan->kv_ranges.size() * sizeof(int32_t));
-    const size_t total = b_segs + b_fwd + b_bwd + b_pre + b_dq + b_rng;
+    const size_t b_bnd = align(3 * (zl::kQueues + 1) * sizeof(int32_t));
+    const size_t total = b_segs + b_fwd + b_bwd + b_pre + b_dq + b_rng + b_bnd;
     if (hipMalloc(&plan->dev_block, total) != hipSuccess) {
       plan->dev_block = nullptr;
       (void)hipGetLastError();
@@ -317,6 +373,7 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     plan->d_pre = (const zl::Tile*)carve(b_pre);
     plan->d_dq = (const zl::Tile*)carve(b_dq);
     plan->d_ranges = (const int32_t*)carve(b_rng);
+    plan->d_bounds = (const int32_t*)carve(b_bnd);
     hipError_t e = hipSuccess;
     auto up = [&](const void* dst, const void* src, size_t bytes) {
       if (e == hipSuccess && bytes) e = hipMemcpy((void*)dst, src, bytes, hipMemcpyHostToDevice);
@@ -327,6 +384,10 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     up(plan->d_pre, plan->pre_tiles.data(), plan->pre_tiles.size() * sizeof(zl::Tile));
     up(plan->d_dq, plan->dq_tiles.data(), plan->dq_tiles.size() * sizeof(zl::Tile));
     up(plan->d_ranges, plan->kv_ranges.data(), plan->kv_ranges.size() * sizeof(int32_t));
+    std::vector<int32_t> all_bounds;
+    for (const auto* b : {&plan->fwd_bounds, &plan->bwd_bounds, &plan->dq_bounds})
+      all_bounds.insert(all_bounds.end(), b->begin(), b->end());
+    up(plan->d_bounds, all_bounds.data(), all_bounds.size() * sizeof(int32_t));
     if (e != hipSuccess) {
       (void)hipFree(plan->dev_block);
       plan->dev_block = nullptr;

@@ -111,8 +111,10 @@ typedef struct {
  * device) and nothing else. The forward queue holds one item per (segment, head, block of
  * 128 query rows); the backward has a dK/dV queue with one item per (segment, head, block
  * of 128 key rows) and a dQ queue with one item per (final segment or ring group, head,
- * block of 128 query rows). Each queue is sorted by decreasing cost (rows x length of the
- * other side), ties kept in (segment, head, block) order.
+ * block of 128 query rows). Each is split into one queue per XCD (zl_plan_queues): chunks of
+ * consecutive items of one (segment, head) go to the least-loaded queue, largest first, and
+ * each queue is sorted by decreasing cost (rows x length of the other side), ties kept in
+ * (segment, head, block) order. A workgroup drains its own XCD's queue, then the others.
  */
 zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                         const int32_t* seq_heads, int32_t n_seg, const zl_segment* segs,
@@ -132,6 +134,13 @@ zl_status zl_plan_group(const zl_plan* plan, int32_t g, zl_group_info_t* info);
  */
 zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* out, int64_t cap, int64_t* count);
 
+/*
+ * Queue boundaries of a work list (which as for zl_plan_tiles): items bounds[k]..bounds[k+1]
+ * of zl_plan_tiles' order form queue k. Writes min(cap, n_queues + 1) ints; *n_queues gets
+ * the queue count.
+ */
+zl_status zl_plan_queues(const zl_plan* plan, int32_t which, int32_t* bounds, int32_t cap, int32_t* n_queues);
+
 /* Free a plan and its device tables. NULL is ignored. */
 void zl_plan_destroy(zl_plan* plan);
 
@@ -143,7 +152,7 @@ void zl_plan_destroy(zl_plan* plan);
  *   o_part,     fp32 partial slab, [part_rows][d] and [part_rows]; may be NULL only if the
  *   lse_part    plan has no KV-split group
  *   workspace   device memory of info.ws_fwd bytes, 256-B aligned, not shared with a
- *               concurrent call (it holds the queue counter)
+ *               concurrent call (it holds the queue counters)
  *   stream      hipStream_t, NULL for the default stream
  * Rows that no segment covers are left untouched. Pointers must be 16-B aligned.
  */

@@ -47,12 +47,32 @@ def test_mixed_pack_metric_flops():
     assert p.info["q_rows"] * 128 * 4 > 2 ** 31
 
 
+def _per_queue_cost_order(tiles, costs, bounds):
+    """Within each queue: decreasing cost, equal costs in (segment, head, block) order."""
+    for q in range(len(bounds) - 1):
+        lo, hi = bounds[q], bounds[q + 1]
+        for i in range(lo, hi - 1):
+            assert costs[i] >= costs[i + 1], f"queue {q} not in decreasing cost order"
+            if costs[i] == costs[i + 1]:
+                assert tiles[i][:3] < tiles[i + 1][:3], "equal-cost items not in (segment, head, block) order"
+
+
+def _balanced(costs, bounds, tol=0.15):
+    loads = [sum(costs[bounds[q]:bounds[q + 1]]) for q in range(len(bounds) - 1)]
+    mean = sum(loads) / len(loads)
+    biggest = max(costs) if costs else 0
+    assert max(loads) <= mean * (1 + tol) + biggest, f"queue loads {loads}"
+
+
 @pytest.mark.parametrize("which", [0, 1])
-@pytest.mark.parametrize("name", ["tiny", "mixed", "ring"])
+@pytest.mark.parametrize("name", ["tiny", "mixed", "ring", "long"])
 def test_queue_covers_every_block_once_in_cost_order(name, which):
     pack = W.config(name)
     p = host_plan(pack)
     tiles = p.tiles(which)
+    bounds = p.queues(which)
+    assert len(bounds) == 9 and bounds[0] == 0 and bounds[-1] == len(tiles)
+    assert all(a <= b for a, b in zip(bounds, bounds[1:]))
     block = 128
     seen = set()
     for (seg, h, r0, n) in tiles:
@@ -66,10 +86,22 @@ def test_queue_covers_every_block_once_in_cost_order(name, which):
     assert len(seen) == expected
     other = lambda t: (pack.segments[t[0]][6] - pack.segments[t[0]][5]) if which == 0 else (pack.segments[t[0]][4] - pack.segments[t[0]][3])
     costs = [t[3] * other(t) for t in tiles]
-    assert all(a >= b for a, b in zip(costs, costs[1:])), "queue not in decreasing cost order"
-    for a, b, ca, cb in zip(tiles, tiles[1:], costs, costs[1:]):
-        if ca == cb:
-            assert (a[0], a[1], a[2]) < (b[0], b[1], b[2]), "equal-cost items not in (segment, head, block) order"
+    _per_queue_cost_order(tiles, costs, bounds)
+    _balanced(costs, bounds)
+
+
+def test_queue_keeps_heads_together():
+    """Chunks of one (segment, head) stay together: the mixed pack's forward items of a head
+    land in few queues, so a head's K/V is read through few L2s."""
+    pack = W.mixed()
+    p = host_plan(pack)
+    tiles, bounds = p.tiles(0), p.queues(0)
+    where = {}
+    for q in range(8):
+        for (seg, h, r0, n) in tiles[bounds[q]:bounds[q + 1]]:
+            where.setdefault((seg, h), set()).add(q)
+    spread = sum(len(v) for v in where.values()) / len(where)
+    assert spread < 1.5, spread
 
 
 @pytest.mark.parametrize("name", ["tiny", "mixed", "ring"])
@@ -97,7 +129,10 @@ def test_dq_queue(name):
     assert len(seen) == len(tiles) == sum((pack.segments[i][2] - pack.segments[i][1]) *
                                           -(-(pack.segments[i][4] - pack.segments[i][3]) // 128) for i in owners)
     costs = [t[3] * keys_of[t[0]] for t in tiles]
-    assert all(a >= b for a, b in zip(costs, costs[1:]))
+    bounds = p.queues(2)
+    assert bounds[-1] == len(tiles)
+    _per_queue_cost_order(tiles, costs, bounds)
+    _balanced(costs, bounds)
 
 
 def test_ring_group_layout():
