@@ -42,6 +42,15 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ZL_LDS i16x4*)(p));
   return __builtin_bit_cast(bf16x4, r);
 }
+// The same at an LDS address.
+__device__ __forceinline__ bf16x4 lds_read_tr(uint32_t a) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ZL_LDS i16x4*)a);
+  return __builtin_bit_cast(bf16x4, r);
+}
+__device__ __forceinline__ bf16x4 lds_read_tr(ZL_LDS const char* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ZL_LDS i16x4*)p);
+  return __builtin_bit_cast(bf16x4, r);
+}
 
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);

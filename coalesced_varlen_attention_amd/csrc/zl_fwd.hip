@@ -11,9 +11,30 @@
 // registers as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so every lane owns
 // one query row of the score tile: the running max and sum are per-lane values that only
 // combine with the partner lane l^32. The exponentiated scores, rounded to bf16, are already
-// in the B-operand layout of O^T = V^T P^T; V^T comes from a natural [key][d] LDS tile
-// through transposed LDS reads. K and V blocks are double-buffered in LDS and the next
-// block's global loads are in flight while the current block is computed.
+// in the B-operand layout of O^T = V^T P^T; V^T comes from LDS through transposed reads.
+//
+// Software pipeline. On gfx950 the matrix cores and the vector ALU overlap when one wave
+// interleaves both kinds of instruction; a wave in a pure softmax phase does not hide behind
+// another wave's MFMAs. Step t of an item therefore runs, as two interleaved regions,
+//   region 1: the MFMAs of O += P(t-1) V(t-1), with the exponentials of block t in place;
+//   region 2: rounding of those exponentials to bf16 P(t), with the MFMAs of S(t+1) = K(t+1) Q^T
+//             in the freed registers, the row sums of P(t) and the row max of S(t+1),
+// so the vector work of one block runs under the matrix work of its neighbours and the
+// registers of S and P are reused in place. K and V blocks reach LDS by direct global-to-LDS
+// loads (no staging registers) issued at the start of a step for use in the next one: K(t+2)
+// and V(t) into the buffers step t-1 finished reading.
+//
+// LDS layouts (64 banks of 4 bytes; 16 lanes per cycle for 16-byte reads, 32 lanes for the
+// 8-byte transposed reads):
+//   K: rows in groups of 1 KB (4 rows of d = 128, 8 of d = 64) with a 64-byte gap between
+//      groups; 16-byte chunk c of row r sits at position c ^ g(r), g(r) in 0..3. The 16 rows
+//      read together fall on 16 distinct bank groups, and since g only flips the two low
+//      chunk bits the read address of every k-step is one of two per-lane bases plus a
+//      constant.
+//   V: column-block major, [d/32][64 keys][32 values]: the 4 consecutive keys x 64 bytes of a
+//      transposed read are 256 contiguous bytes, and every address is affine.
+// Both layouts are what a global-to-LDS load can write: each wave instruction fills 1 KB of
+// contiguous LDS, lane l the 16 bytes at offset 16 l, and each lane picks its source chunk.
 #include "zl_device.hpp"
 #include "zl_internal.h"
 
@@ -23,54 +44,378 @@ namespace {
 template <int D>
 struct FwdCfg {
   static constexpr int kThreads = 256;
-  static constexpr int kBk = 64;                              // keys per block
-  static constexpr int kLd = LdsTile<D>::kLd;                 // K and V row stride in LDS (elements)
-  static constexpr int kSteps = D / 16;                       // k-steps over d for S^T
-  static constexpr int kCb = D / 32;                          // 32-wide column blocks of O^T
-  static constexpr int kChunks = kBk * D / 8 / kThreads;      // 16-byte chunks per thread per block
-  static constexpr int kRowChunks = D / 8;                    // 16-byte chunks per row
+  static constexpr int kBk = 64;                          // keys per block
+  static constexpr int kKb = kBk / 32;                    // 32x32 S^T tiles per block
+  static constexpr int kKs = kBk / 16;                    // 16-key steps of O^T += V^T P^T
+  static constexpr int kSteps = D / 16;                   // k-steps over d for S^T
+  static constexpr int kCb = D / 32;                      // 32-wide column blocks of O^T
+  static constexpr int kRowBytes = 2 * D;                 // one K or V row in bf16
+  static constexpr int kRowChunks = D / 8;                // 16-byte chunks per row
+  static constexpr int kGroupRows = 1024 / kRowBytes;     // K rows per 1 KB group
+  static constexpr int kGroupPitch = 1024 + 64;           // bytes between K row groups
+  static constexpr int kKBytes = kBk / kGroupRows * kGroupPitch;
+  static constexpr int kKbStride = 32 / kGroupRows * kGroupPitch;  // bytes between 32-row K tiles
+  static constexpr int kVBytes = kBk * kRowBytes;
+  static constexpr int kVCbStride = kBk * 64;             // bytes between V column blocks
+  static constexpr int kKDma = kBk / kGroupRows / 4;      // K loads per thread per block
+  static constexpr int kVDma = kVBytes / 1024 / 4;        // V loads per thread per block
+  static_assert(kKDma >= 1 && kVDma >= 1, "every wave loads part of each block");
+  static constexpr float kSlack = 8.0f;                   // lazy-rescale slack, log2 units
+  static constexpr int kAhead = 2;                        // MFMAs between an operand read and its use
 };
 
-// Global -> registers for one block of 64 key rows of K and V (16-byte chunks, rows clamped
-// to the last valid key), and registers -> LDS.
+// Per-lane constants and per-item pointers shared by the pipeline steps.
 template <int D>
-__device__ __forceinline__ void fwd_load_block(u32x4 (&kreg)[FwdCfg<D>::kChunks], u32x4 (&vreg)[FwdCfg<D>::kChunks],
-                                               const bf16* kbase, const bf16* vbase, int64_t rs, int j, int n_kv,
-                                               int tid) {
+struct FwdCtx {
+  const bf16* kbase;  // key row (kv_begin, head h)
+  const bf16* vbase;
+  int64_t rs;         // elements between consecutive tokens
+  int n_kv, n_blk;
+  int koff0, koff1;   // K read bases for even / odd k-steps (bytes)
+  int voff;           // V transposed-read base (bytes)
+  int64_t blk_bytes;                    // bytes between consecutive key blocks
+  uint32_t row_bytes;                   // bytes between consecutive key rows (tokens)
+  uint32_t koff_dma;                    // this lane's byte offset of K load 0 in a full block
+  uint32_t voff_dma;                    // ... of V load 0
+  int64_t k_dma_step;                   // bytes between the rows of consecutive K loads
+  int dma_krow, dma_kcol;               // this lane's row within its K load group, byte column
+  int dma_vrow, dma_vcol;               // this lane's key within the block, byte column (load 0)
+  int wave;
+  float scale_log2;
+};
+
+template <int D>
+struct FwdState {
+  f32x16 oacc[FwdCfg<D>::kCb];
+  bf16x8 q[FwdCfg<D>::kSteps];
+  float m_run;  // exponent reference, log2 units
+  float l_run;  // this lane's share of the running sum
+  float mx;     // row max of the pending score block, log2 units
+};
+
+// Direct global -> LDS load of 16 bytes per lane: lane l reads base + off (off per lane) and
+// its bytes land at lds_base + 16 l (base and lds_base are the same for the whole wave).
+// Issued as inline assembly so that the compiler does not order later LDS reads of other
+// buffers behind it; completion is awaited explicitly (dma_wait) before the workgroup barrier
+// that publishes the buffer.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_base, const char* base, uint32_t off) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+}
+
+// Global -> LDS load of K block blk. Lane offsets are relative to the block's first key row;
+// in a partial last block, rows past the end of the segment read its last row.
+template <int D>
+__device__ __forceinline__ void dma_k(const FwdCtx<D>& cx, uint32_t k_lds, int blk) {
   using C = FwdCfg<D>;
+  const char* base = (const char*)cx.kbase + (int64_t)blk * cx.blk_bytes;
+  if ((blk + 1) * C::kBk <= cx.n_kv) {
 #pragma unroll
-  for (int c = 0; c < C::kChunks; ++c) {
-    const int chunk = tid + c * C::kThreads;
-    const int r = chunk / C::kRowChunks;
-    const int col = (chunk % C::kRowChunks) * 8;
-    const int key = min(j * C::kBk + r, n_kv - 1);
-    kreg[c] = *(const u32x4*)(kbase + (int64_t)key * rs + col);
-    vreg[c] = *(const u32x4*)(vbase + (int64_t)key * rs + col);
+    for (int i = 0; i < C::kKDma; ++i)
+      lds_dma16(k_lds + (i * 4 + cx.wave) * C::kGroupPitch, base + i * cx.k_dma_step, cx.koff_dma);
+  } else {
+    const int last = cx.n_kv - 1 - blk * C::kBk;
+#pragma unroll
+    for (int i = 0; i < C::kKDma; ++i) {
+      const int row = min((i * 4 + cx.wave) * C::kGroupRows + cx.dma_krow, last);
+      lds_dma16(k_lds + (i * 4 + cx.wave) * C::kGroupPitch, base, (uint32_t)row * cx.row_bytes + cx.dma_kcol);
+    }
   }
 }
 
+// Each 1 KB of the V tile is 16 keys x 64 bytes of one column block; load i of wave w fills
+// the (4i + w)-th such piece: column block (4i + w) / (kBk / 16), key group (4i + w) % (kBk / 16).
 template <int D>
-__device__ __forceinline__ void fwd_store_block(const u32x4 (&kreg)[FwdCfg<D>::kChunks],
-                                                const u32x4 (&vreg)[FwdCfg<D>::kChunks], bf16* k_lds, bf16* v_lds,
-                                                int tid) {
+__device__ __forceinline__ void dma_v(const FwdCtx<D>& cx, uint32_t v_lds, int blk) {
   using C = FwdCfg<D>;
+  const char* base = (const char*)cx.vbase + (int64_t)blk * cx.blk_bytes;
+  if ((blk + 1) * C::kBk <= cx.n_kv) {
 #pragma unroll
-  for (int c = 0; c < C::kChunks; ++c) {
-    const int chunk = tid + c * C::kThreads;
-    const int r = chunk / C::kRowChunks;
-    const int col = (chunk % C::kRowChunks) * 8;
-    *(u32x4*)&k_lds[lds_row(r) * C::kLd + col] = kreg[c];
-    *(u32x4*)&v_lds[lds_row(r) * C::kLd + col] = vreg[c];
+    for (int i = 0; i < C::kVDma; ++i)
+      lds_dma16(v_lds + (i * 4 + cx.wave) * 1024, base + 64 * (4 / (C::kBk / 16)) * i, cx.voff_dma);
+  } else {
+    const int row = min(cx.dma_vrow, cx.n_kv - 1 - blk * C::kBk);
+#pragma unroll
+    for (int i = 0; i < C::kVDma; ++i)
+      lds_dma16(v_lds + (i * 4 + cx.wave) * 1024, base,
+                (uint32_t)row * cx.row_bytes + cx.dma_vcol + 64 * (4 / (C::kBk / 16)) * i);
   }
 }
 
 __global__ void zero_counters_kernel(int32_t* counters) { counters[threadIdx.x * kCounterStride] = 0; }
 
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// S^T[key][q] of one block: kKb tiles of 32 keys, each a chain of k-steps over d.
+template <int D>
+__device__ __forceinline__ void score_block(const FwdCtx<D>& cx, uint32_t k_lds, const bf16x8 (&q)[FwdCfg<D>::kSteps],
+                                            f32x16 (&s)[FwdCfg<D>::kKb]) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int kb = 0; kb < C::kKb; ++kb) {
+    s[kb] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) {
+      const uint32_t kp = k_lds + kb * C::kKbStride + (st & 1 ? cx.koff1 : cx.koff0) + 64 * (st >> 1);
+      s[kb] = mfma32(*(ZL_LDS const bf16x8*)kp, q[st], s[kb]);
+    }
+  }
+}
+
+// O^T[c][q] += V^T[c][key] P^T[key][q], 16 keys per step. The k order of P^T in this lane is
+// keys {16ks + 4hi + 0..3, 16ks + 8 + 4hi + 0..3}; the two transposed reads fetch V rows in
+// that same order.
+template <int D>
+__device__ __forceinline__ void value_block(const FwdCtx<D>& cx, uint32_t v_lds, const bf16x8 (&pb)[FwdCfg<D>::kKs],
+                                            f32x16 (&oacc)[FwdCfg<D>::kCb]) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int ks = 0; ks < C::kKs; ++ks)
+#pragma unroll
+    for (int cb = 0; cb < C::kCb; ++cb) {
+      const uint32_t vp = v_lds + cb * C::kVCbStride + ks * 1024 + cx.voff;
+      const bf16x8 a = cat(lds_read_tr(vp), lds_read_tr(vp + 512));
+      oacc[cb] = mfma32(a, pb[ks], oacc[cb]);
+    }
+}
+
+// Keys at or past `valid` in a score block get -inf.
+template <int KB>
+__device__ __forceinline__ void mask_block(f32x16 (&s)[KB], int valid, int hi) {
+  const int vr = valid - 4 * hi;  // compare lane-independent key offsets against one value
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (kb * 32 + 8 * (i / 4) + (i % 4) >= vr) s[kb][i] = -INFINITY;
+}
+
+template <int KB>
+__device__ __forceinline__ float block_max(const f32x16 (&s)[KB]) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+  return mx;
+}
+
+// In place: S -> exp2(S * scale_log2 - m).
+template <int KB>
+__device__ __forceinline__ void block_exp(f32x16 (&s)[KB], float scale_log2, float m) {
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], scale_log2, -m));
+}
+
+// Exponentials -> bf16 P in the B-operand layout (P^T k-steps of 16 keys). Returns this
+// lane's sum of the rounded values (bf16 pair dot products with 1): the same weights that the
+// P V product uses.
+template <int KB>
+__device__ __forceinline__ float block_round(const f32x16 (&e)[KB], bf16x8 (&pb)[2 * KB]) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float lsum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      f32x8 v;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = e[kb][8 * hs + u];
+      const bf16x8 r = to_bf16x8(v);
+      pb[2 * kb + hs] = r;
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(r, r, 0, 1), one, lsum, false);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(r, r, 2, 3), one, lsum, false);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(r, r, 4, 5), one, lsum, false);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(r, r, 6, 7), one, lsum, false);
+    }
+  return lsum;
+}
+
+// Operand reads at a per-lane base plus a constant (the constant folds into the instruction).
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand(ZL_LDS const char* vb, int m) {
+  using C = FwdCfg<D>;
+  ZL_LDS const char* vp = vb + (m % C::kCb) * C::kVCbStride + (m / C::kCb) * 1024;
+  return cat(lds_read_tr(vp), lds_read_tr(vp + 512));
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 k_operand(ZL_LDS const char* kb0, ZL_LDS const char* kb1, int m) {
+  using C = FwdCfg<D>;
+  const int st = m % C::kSteps;
+  return *(ZL_LDS const bf16x8*)((st & 1 ? kb1 : kb0) + (m / C::kSteps) * C::kKbStride + 64 * (st >> 1));
+}
+
+// Region 1 of a step, written in issue order: each P(t-1) V(t-1) MFMA (operands read two
+// MFMAs ahead) is followed by its share of the in-place exponentials of S(t).
+template <int D>
+__device__ __forceinline__ void pv_exp_interleaved(const FwdCtx<D>& cx, uint32_t v_lds, const bf16x8 (&pb)[FwdCfg<D>::kKs],
+                                                   f32x16 (&oacc)[FwdCfg<D>::kCb], f32x16 (&sc)[FwdCfg<D>::kKb],
+                                                   float m_ref) {
+  using C = FwdCfg<D>;
+  constexpr int kM = C::kKs * C::kCb;
+  constexpr int kAhead = C::kAhead;
+  constexpr int kPer = 16 * C::kKb / kM;  // exponentials per MFMA
+  static_assert(kPer * kM == 16 * C::kKb, "exponentials must divide evenly over the MFMAs");
+  ZL_LDS const char* vb = (ZL_LDS const char*)(v_lds + cx.voff);
+  bf16x8 a[kM];
+#pragma unroll
+  for (int m = 0; m < kAhead; ++m) a[m] = v_operand<D>(vb, m);
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    if (m + kAhead < kM) a[m + kAhead] = v_operand<D>(vb, m + kAhead);
+    oacc[m % C::kCb] = mfma32(a[m], pb[m / C::kCb], oacc[m % C::kCb]);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = m * kPer + u;
+      sc[e / 16][e % 16] = fast_exp2(fmaf(sc[e / 16][e % 16], cx.scale_log2, -m_ref));
+    }
+  }
+}
+
+// Region 2 of a step, written in issue order: the exponentials become bf16 P(t) (tile 0 before
+// its score chain starts, tile 1 during it); the S(t+1) MFMAs (operands read two MFMAs ahead)
+// accumulate into the freed registers; the row sum of P(t) and the row max of the finished
+// tile 0 fill the slots of the later MFMAs; the max of tile 1 follows the last MFMA.
+template <int D>
+__device__ __forceinline__ void round_score_interleaved(const FwdCtx<D>& cx, uint32_t k_lds,
+                                                        const bf16x8 (&q)[FwdCfg<D>::kSteps],
+                                                        f32x16 (&sc)[2], bf16x8 (&pb)[4], float& lsum,
+                                                        float& mx) {
+  using C = FwdCfg<D>;
+  static_assert(C::kKb == 2, "two score tiles per block");
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  auto half = [](const f32x16& t, int hs) {
+    f32x8 v;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = t[8 * hs + u];
+    return to_bf16x8(v);
+  };
+  pb[0] = half(sc[0], 0);
+  pb[1] = half(sc[0], 1);
+  constexpr int kM = 2 * C::kSteps;
+  constexpr int kAhead = C::kAhead;
+  float ls0 = 0.f, ls1 = 0.f, mx0 = -INFINITY, mx1 = -INFINITY;
+  ZL_LDS const char* kb0 = (ZL_LDS const char*)(k_lds + cx.koff0);
+  ZL_LDS const char* kb1 = (ZL_LDS const char*)(k_lds + cx.koff1);
+  bf16x8 ko[kM];
+#pragma unroll
+  for (int m = 0; m < kAhead; ++m) ko[m] = k_operand<D>(kb0, kb1, m);
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    if (m + kAhead < kM) ko[m + kAhead] = k_operand<D>(kb0, kb1, m + kAhead);
+    const int kb = m / C::kSteps;
+    const int st = m % C::kSteps;
+    sc[kb] = mfma32(ko[m], q[st], st == 0 ? f32x16{} : sc[kb]);
+    if (m == 0) pb[2] = half(sc[1], 0);
+    if (m == 1) pb[3] = half(sc[1], 1);
+    // 16 row-sum dot products spread over the slots after the rounding.
+    if (m >= 2) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (2 + (j * (kM - 2)) / 16 == m) {
+          const bf16x8 r = pb[j / 4];
+          const bf16x2 pr = __builtin_shufflevector(r, r, 0, 1);
+          const bf16x2 pr1 = __builtin_shufflevector(r, r, 2, 3);
+          const bf16x2 pr2 = __builtin_shufflevector(r, r, 4, 5);
+          const bf16x2 pr3 = __builtin_shufflevector(r, r, 6, 7);
+          const bf16x2 sel = (j % 4) == 0 ? pr : (j % 4) == 1 ? pr1 : (j % 4) == 2 ? pr2 : pr3;
+          if (j & 1)
+            ls1 = __builtin_amdgcn_fdot2_f32_bf16(sel, one, ls1, false);
+          else
+            ls0 = __builtin_amdgcn_fdot2_f32_bf16(sel, one, ls0, false);
+        }
+    }
+    // Row max of tile 0 over the slots of tile 1's chain (two values per slot).
+    if (kb == 1) {
+#pragma unroll
+      for (int u = 0; u < 16 / C::kSteps; ++u) {
+        const int i = st * (16 / C::kSteps) + u;
+        mx0 = fmaxf(mx0, sc[0][i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx1 = fmaxf(mx1, sc[1][i]);
+  lsum = ls0 + ls1;
+  mx = fmaxf(mx0, mx1);
+}
+
+// One pipeline step t of an item (see the file comment). kPrev: block t-1 exists (P(t-1) is in
+// `pb`, V(t-1) in LDS); kNext: block t+1 exists (K(t+1) in LDS). On entry `sc` holds S(t) and
+// st.mx its row max; on return `pb` holds P(t), `sc` S(t+1) and st.mx its row max. The two
+// register sets are reused in place, so steps need no copies:
+//   region 1: the P(t-1) V(t-1) MFMAs, with the exponentials of S(t) computed in place;
+//   region 2: rounding of those exponentials into `pb` (free once region 1 has issued its
+//             MFMAs), with the S(t+1) MFMAs accumulating into `sc`, then its row max.
+template <int D, bool kPrev, bool kNext>
+__device__ __forceinline__ void fwd_step(const FwdCtx<D>& cx, FwdState<D>& st, int t, uint32_t k_dma, uint32_t v_dma,
+                                         uint32_t k_rd, uint32_t v_rd, f32x16 (&sc)[FwdCfg<D>::kKb],
+                                         bf16x8 (&pb)[FwdCfg<D>::kKs], int hi) {
+  using C = FwdCfg<D>;
+  if (kNext && t + 2 < cx.n_blk) dma_k<D>(cx, k_dma, t + 2);
+  dma_v<D>(cx, v_dma, t);
+
+  // Lazy rescaling: the exponent reference only moves when the block max exceeds it by more
+  // than kSlack, so exponentials stay below 2^kSlack. P(t) uses the new reference; the
+  // accumulators move to it after the pending P(t-1) V(t-1) product (which belongs to the old
+  // one) has been added, and only when some lane of the wave needs it. The result is the same
+  // quantity; only the reference changes.
+  const bool need = st.mx > st.m_run + C::kSlack;
+  const bool rescale = __any(need);
+  float alpha = 1.f;
+  if (rescale) {
+    const float m_new = need ? st.mx : st.m_run;
+    alpha = fast_exp2(st.m_run - m_new);
+    st.m_run = m_new;
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  if (kPrev)
+    pv_exp_interleaved<D>(cx, v_rd, pb, st.oacc, sc, st.m_run);
+  else
+    block_exp(sc, cx.scale_log2, st.m_run);
+#pragma unroll
+  for (int kb = 0; kb < C::kKb; ++kb) asm volatile("" : "+v"(sc[kb]));  // keep the exponentials here
+  __builtin_amdgcn_sched_barrier(0);
+  if (rescale) {
+    st.l_run *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < C::kCb; ++cb) st.oacc[cb] *= alpha;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float lsum, mxn = 0.f;
+  if (kNext)
+    round_score_interleaved<D>(cx, k_rd, st.q, sc, pb, lsum, mxn);
+  else
+    lsum = block_round(sc, pb);
+  asm volatile("" : "+v"(lsum), "+v"(mxn));
+  __builtin_amdgcn_sched_barrier(0);
+  st.l_run += lsum;
+  if (kNext) {
+    const int valid = cx.n_kv - (t + 1) * C::kBk;
+    if (valid < C::kBk) {
+      mask_block(sc, valid, hi);
+      mxn = block_max(sc);
+    }
+    st.mx = half_max(mxn) * cx.scale_log2;
+  }
+  dma_wait();
+  __syncthreads();
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][C::kBk * C::kLd];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][C::kBk * C::kLd];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::kVBytes + 2 * C::kKBytes];
+  // LDS byte addresses of the double-buffered V and K blocks.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(ZL_LDS char*)smem;
+  const uint32_t v_lds0 = lds0, v_lds1 = lds0 + C::kVBytes;
+  const uint32_t k_lds0 = lds0 + 2 * C::kVBytes, k_lds1 = k_lds0 + C::kKBytes;
   __shared__ int32_t s_item;
 
   const int tid = threadIdx.x;
@@ -78,13 +423,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int r_in = (lane & 15) >> 2;                        // transposed-read row within 4
-  const int c_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // transposed-read column within 32
-  const int prow_b = lds_row(l32);                           // physical row of this lane's operand row
-  const int prow_t = lds_row(4 * hi + r_in);                 // physical row of its transposed reads
   const bf16* __restrict__ gq = (const bf16*)p.q;
-  const bf16* __restrict__ gk = (const bf16*)p.k;
-  const bf16* __restrict__ gv = (const bf16*)p.v;
+
+  FwdCtx<D> cx;
+  cx.wave = __builtin_amdgcn_readfirstlane(wave);
+  cx.scale_log2 = p.scale_log2;
+  {
+    const int g = (l32 / (C::kGroupRows / 4)) & 3;
+    const int row = (l32 / C::kGroupRows) * C::kGroupPitch + (l32 % C::kGroupRows) * C::kRowBytes;
+    cx.koff0 = row + 16 * (hi ^ g);
+    cx.koff1 = row + 16 * ((2 + hi) ^ g);
+    const int r_in = (lane & 15) >> 2;
+    const int c_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    cx.voff = (4 * hi + r_in) * 64 + 2 * c_in;
+    constexpr int kGroups = C::kBk / 16;
+    cx.dma_krow = lane / C::kRowChunks;
+    cx.dma_kcol = 16 * ((lane % C::kRowChunks) ^ ((lane >> 4) & 3));
+    cx.dma_vrow = (wave % kGroups) * 16 + lane / 4;
+    cx.dma_vcol = 64 * (wave / kGroups) + 16 * (lane & 3);
+  }
 
   const int home = blockIdx.x % kQueues;
   int drained = 0;
@@ -97,116 +454,63 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
     const SegDev sg = p.segs[tile.seg];
     const int nh = sg.nh;
     const int h = tile.head;
-    const int64_t rs = (int64_t)nh * D;  // elements between consecutive tokens
+    cx.rs = (int64_t)nh * D;
+    cx.row_bytes = (uint32_t)(cx.rs * 2);
+    cx.blk_bytes = (int64_t)C::kBk * cx.rs * 2;
+    cx.koff_dma = (uint32_t)(wave * C::kGroupRows + cx.dma_krow) * cx.row_bytes + cx.dma_kcol;
+    cx.voff_dma = (uint32_t)cx.dma_vrow * cx.row_bytes + cx.dma_vcol;
+    cx.k_dma_step = (int64_t)4 * C::kGroupRows * cx.rs * 2;
+    cx.n_kv = sg.kv_end - sg.kv_begin;
+    cx.n_blk = (cx.n_kv + C::kBk - 1) / C::kBk;
+    cx.kbase = (const bf16*)p.k + (sg.kv_row0 + (int64_t)sg.kv_begin * nh + h) * D;
+    cx.vbase = (const bf16*)p.v + (sg.kv_row0 + (int64_t)sg.kv_begin * nh + h) * D;
+    const int n = cx.n_blk;
 
-    // This lane's query row (clamped to the last valid row; results of clamped rows are dropped).
+    // Prologue: K(0), K(1) into LDS; this lane's query row into registers (clamped to the
+    // last valid row; results of clamped rows are dropped); S(0) and its row max.
+    dma_k<D>(cx, k_lds0, 0);
+    if (n > 1) dma_k<D>(cx, k_lds1, 1);
     const int qi = wave * 32 + l32;
     const bool q_valid = qi < tile.nrows;
     const int qtok = tile.row0 + (q_valid ? qi : tile.nrows - 1);
-    bf16x8 qreg[C::kSteps];
+    FwdState<D> st;
     {
       const bf16* qp = gq + (sg.q_row0 + (int64_t)qtok * nh + h) * D + 8 * hi;
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) qreg[s] = *(const bf16x8*)(qp + 16 * s);
+      for (int s = 0; s < C::kSteps; ++s) st.q[s] = *(const bf16x8*)(qp + 16 * s);
     }
-
-    const int n_kv = sg.kv_end - sg.kv_begin;
-    const int n_blk = (n_kv + C::kBk - 1) / C::kBk;
-    const bf16* kbase = gk + (sg.kv_row0 + (int64_t)sg.kv_begin * nh + h) * D;
-    const bf16* vbase = gv + (sg.kv_row0 + (int64_t)sg.kv_begin * nh + h) * D;
-
-    u32x4 kreg[C::kChunks], vreg[C::kChunks];
-    f32x16 oacc[C::kCb];
 #pragma unroll
-    for (int cb = 0; cb < C::kCb; ++cb) oacc[cb] = f32x16{};
-    float m_run = -INFINITY;  // running max of scaled scores, log2 units
-    float l_run = 0.f;        // this lane's share of the running sum
-
-    fwd_load_block<D>(kreg, vreg, kbase, vbase, rs, 0, n_kv, tid);
-    fwd_store_block<D>(kreg, vreg, k_lds[0], v_lds[0], tid);
+    for (int cb = 0; cb < C::kCb; ++cb) st.oacc[cb] = f32x16{};
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+    f32x16 sc[C::kKb];
+    bf16x8 pb[C::kKs];
+    dma_wait();
     __syncthreads();
+    score_block<D>(cx, k_lds0, st.q, sc);
+    if (cx.n_kv < C::kBk) mask_block(sc, cx.n_kv, hi);
+    st.mx = half_max(block_max(sc)) * cx.scale_log2;
+    __syncthreads();  // every wave has read K(0) before step 0 refills its buffer
 
-    for (int j = 0; j < n_blk; ++j) {
-      const int buf = j & 1;
-      if (j + 1 < n_blk) fwd_load_block<D>(kreg, vreg, kbase, vbase, rs, j + 1, n_kv, tid);
-
-      // S^T[key][q] for the block's 64 keys, as two 32x32 tiles.
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-        const bf16* kr = &k_lds[buf][(kb * 32 + prow_b) * C::kLd + 8 * hi];
-#pragma unroll
-        for (int s = 0; s < C::kSteps; ++s) sacc[kb] = mfma32(*(const bf16x8*)(kr + 16 * s), qreg[s], sacc[kb]);
+    // Step t reads K(t+1) from k_lds[(t+1)&1] and V(t-1) from v_lds[(t-1)&1], and refills
+    // k_lds[t&1] with K(t+2) and v_lds[t&1] with V(t).
+    if (n == 1) {
+      fwd_step<D, false, false>(cx, st, 0, k_lds0, v_lds0, k_lds1, v_lds1, sc, pb, hi);
+    } else {
+      fwd_step<D, false, true>(cx, st, 0, k_lds0, v_lds0, k_lds1, v_lds1, sc, pb, hi);
+      for (int t = 1; t < n - 1; ++t) {
+        const bool odd = t & 1;
+        fwd_step<D, true, true>(cx, st, t, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, odd ? k_lds0 : k_lds1,
+                                odd ? v_lds0 : v_lds1, sc, pb, hi);
       }
-      // Keys past the end of the segment (last block only) get -inf.
-      const int valid = n_kv - j * C::kBk;
-      if (valid < C::kBk) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
-            if (key >= valid) sacc[kb][i] = -INFINITY;
-          }
-      }
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = half_max(mx) * p.scale_log2;
-      // Lazy rescaling: the exponent reference m_run only moves when the block max exceeds it
-      // by more than kSlack (log2 units), so exponentials stay below 2^kSlack and the O and l
-      // rescale runs only when some lane of the wave needs it. The result is the same quantity;
-      // only the reference of the running sums changes.
-      constexpr float kSlack = 8.0f;
-      const bool need = mx > m_run + kSlack;
-      if (__any(need)) {
-        const float m_new = need ? mx : m_run;
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < C::kCb; ++cb) oacc[cb] *= alpha;
-      }
-
-      bf16x8 pb[4];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          f32x8 e;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            e[u] = fast_exp2(fmaf(sacc[kb][8 * hs + u], p.scale_log2, -m_run));
-            lsum += e[u];
-          }
-          pb[kb * 2 + hs] = to_bf16x8(e);
-        }
-      l_run += lsum;
-
-      // O^T[c][q] += V^T[c][key] P^T[key][q], 16 keys per step. The k order of P^T in this
-      // lane is keys {16hs + 4hi + 0..3, 16hs + 8 + 4hi + 0..3} of each 32-key half; the two
-      // transposed reads fetch V rows in that same order (logical rows +8 are physical rows +2).
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int row = (ks >> 1) * 32 + 16 * (ks & 1) + prow_t;
-#pragma unroll
-        for (int cb = 0; cb < C::kCb; ++cb) {
-          const bf16* vp = &v_lds[buf][row * C::kLd + cb * 32 + c_in];
-          const bf16x8 a = cat(lds_read_tr(vp), lds_read_tr(vp + 2 * C::kLd));
-          oacc[cb] = mfma32(a, pb[ks], oacc[cb]);
-        }
-      }
-
-      if (j + 1 < n_blk) fwd_store_block<D>(kreg, vreg, k_lds[buf ^ 1], v_lds[buf ^ 1], tid);
-      __syncthreads();
+      const bool odd = (n - 1) & 1;
+      fwd_step<D, true, false>(cx, st, n - 1, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, odd ? k_lds0 : k_lds1,
+                               odd ? v_lds0 : v_lds1, sc, pb, hi);
     }
+    value_block<D>(cx, ((n - 1) & 1) ? v_lds1 : v_lds0, pb, st.oacc);  // P(n-1) V(n-1)
 
     // Epilogue: O = O_acc / l, LSE = ln(2) * (m + log2 l), natural log.
-    const float l_tot = half_sum(l_run);
+    const float l_tot = half_sum(st.l_run);
     if (q_valid) {
       const float inv = 1.0f / l_tot;
       float* orow;
@@ -226,11 +530,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int c = cb * 32 + 8 * g + 4 * hi;
-          f32x4 val = {oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv, oacc[cb][4 * g + 2] * inv,
-                       oacc[cb][4 * g + 3] * inv};
+          f32x4 val = {st.oacc[cb][4 * g] * inv, st.oacc[cb][4 * g + 1] * inv, st.oacc[cb][4 * g + 2] * inv,
+                       st.oacc[cb][4 * g + 3] * inv};
           *(f32x4*)(orow + c) = val;
         }
-      if (hi == 0) lse_out[lrow] = 0.69314718055994531f * (m_run + __log2f(l_tot));
+      if (hi == 0) lse_out[lrow] = 0.69314718055994531f * (st.m_run + __log2f(l_tot));
     }
     __syncthreads();
   }
