@@ -23,6 +23,10 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
                 "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
 HOST_FLAGS = ["-x", "c++", "-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__"]
+# Per-file device flags. The backward kernels keep MFMA results in arch VGPRs (the vector
+# code reads every score and gradient element; the accumulator-register form costs one move
+# per element).
+EXTRA_DEVICE_FLAGS = {"zl_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -39,7 +43,10 @@ def _hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
     rocm_inc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
-    flags = DEVICE_FLAGS if src.endswith(".hip") else HOST_FLAGS + ["-I", rocm_inc]
+    if src.endswith(".hip"):
+        flags = DEVICE_FLAGS + EXTRA_DEVICE_FLAGS.get(os.path.basename(src), [])
+    else:
+        flags = HOST_FLAGS + ["-I", rocm_inc]
     cmd = [_hipcc(), *flags, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)

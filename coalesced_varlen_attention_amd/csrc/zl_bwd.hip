@@ -13,8 +13,10 @@
 // dK/dV kernel: one item = 128 key rows of one (segment, head); 4 waves x 32 keys. Each wave
 //   keeps its K and V rows in registers as B operands of S = Q K^T and dP = dO V^T (lane = one
 //   key column), so P and dS come out of the MFMA already in the B-operand layout of
-//   dV^T = dO^T P and dK^T = Q^T dS; dO^T and Q^T are read from natural LDS tiles with
-//   transposed LDS reads. dK and dV accumulate in registers and are written once.
+//   dV^T = dO^T P and dK^T = Q^T dS; dO^T and Q^T are read from the same LDS tiles with
+//   transposed LDS reads. The 64-row Q and dO tiles of a step reach LDS by direct global-to-LDS
+//   loads, double-buffered and issued one step ahead, so a step costs one barrier. dK and dV
+//   accumulate in registers and are written once.
 // dQ kernel: one item = 128 query rows of one (segment or ring group, head); 4 waves x 32
 //   query rows, the forward's shape: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers
 //   (lane = one query row, whose LSE and D are then per-lane scalars), and
@@ -76,42 +78,89 @@ template <int D>
 struct KvCfg {
   static constexpr int kThreads = 256;
   static constexpr int kBq = kBwdRows;                    // 64 query rows per step
-  static constexpr int kQld = LdsTile<D>::kLd;            // Q / dO row stride in LDS
   static constexpr int kSteps = D / 16;                   // k-steps over d
   static constexpr int kCb = D / 32;                      // 32-wide column blocks over d
-  static constexpr int kQChunks = kBq * D / 8 / kThreads; // 16-B chunks per thread (Q or dO)
-  static constexpr int kRowChunks = D / 8;
+  static constexpr int kRowChunks = D / 8;                // 16-byte chunks per row
+  // Q and dO tiles of kBq rows: rows in 1 KB groups with a 16-byte gap; 16-byte chunk c of
+  // row r at position c ^ x(r) (x below). With 64 banks of 4 bytes this keeps both read kinds
+  // free of bank conflicts: 16 consecutive rows read at one chunk (16-byte operand reads) fall
+  // on 16 distinct 16-byte bank groups, and 4 consecutive rows x 64 bytes (transposed reads)
+  // on 4 distinct 64-byte groups. Every group is one 1 KB global-to-LDS load of one wave.
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kGroupRows = 1024 / kRowBytes;     // 4 (d = 128) or 8 (d = 64)
+  static constexpr int kPitch = 1024 + 16;
+  static constexpr int kTileBytes = kBq / kGroupRows * kPitch;
+  static constexpr int kDma = kBq / kGroupRows / 4;       // loads per thread per tile
+  static constexpr int kStageBytes = 2 * kTileBytes + 2 * kBq * 4;  // Q, dO, LSE, D
+  static constexpr int kSub = kSteps / 4;                 // k-steps per operand base
 };
 
+// Chunk swizzle of row r (r % 8 matters only).
 template <int D>
-__device__ __forceinline__ void kv_prefetch(u32x4 (&qpre)[KvCfg<D>::kQChunks], u32x4 (&dopre)[KvCfg<D>::kQChunks],
-                                            float& lpre, const bf16* qbase, const bf16* dobase, int64_t rs,
-                                            int64_t hmbase, int q0, int nrow, const float* lse2,
-                                            const float* dvec, int tid) {
+__device__ __forceinline__ int qt_x(int r) {
+  if (D == 128) return 4 * (r & 3);
+  const int w = r & 7;
+  return 4 * ((w >> 1) & 1) + 2 * ((w >> 2) & 1);
+}
+
+// Byte offset of row r within a tile.
+template <int D>
+__device__ __forceinline__ int qt_row(int r) {
   using C = KvCfg<D>;
+  return (r / C::kGroupRows) * C::kPitch + (r % C::kGroupRows) * C::kRowBytes;
+}
+
+// Per-item state of the key-major kernel's Q / dO loads.
+struct KvDma {
+  const char* qbase;    // row of local query 0 of the segment (Q)
+  const char* dobase;   // ... (dO)
+  int64_t rs_bytes;     // bytes between consecutive query tokens
+  uint32_t lane_off;    // this lane's byte offset within a full step (row in group, chunk)
+  int lane_row;         // this lane's row within its load group
+  int lane_col;         // this lane's byte column
+  int n_q;
+};
+
+// Global -> LDS loads of the Q and dO rows of step qb into one stage; rows past the end of
+// the segment read its last row (their probabilities are forced to 0 through LSE = +inf).
+template <int D>
+__device__ __forceinline__ void kv_dma(const KvDma& dm, uint32_t stage, int qb, int wave) {
+  using C = KvCfg<D>;
+  const int q0 = qb * C::kBq;
+  if (q0 + C::kBq <= dm.n_q) {
 #pragma unroll
-  for (int c = 0; c < C::kQChunks; ++c) {
-    const int chunk = tid + c * C::kThreads;
-    const int r = chunk / C::kRowChunks;
-    const int col = (chunk % C::kRowChunks) * 8;
-    const int64_t off = (int64_t)(q0 + min(r, nrow - 1)) * rs + col;
-    qpre[c] = *(const u32x4*)(qbase + off);
-    dopre[c] = *(const u32x4*)(dobase + off);
+    for (int i = 0; i < C::kDma; ++i) {
+      const int grp = i * 4 + wave;
+      const int64_t off = (int64_t)(q0 + grp * C::kGroupRows) * dm.rs_bytes;
+      lds_dma16(stage + grp * C::kPitch, dm.qbase + off, dm.lane_off);
+      lds_dma16(stage + C::kTileBytes + grp * C::kPitch, dm.dobase + off, dm.lane_off);
+    }
+  } else {
+    const int64_t off0 = (int64_t)q0 * dm.rs_bytes;
+#pragma unroll
+    for (int i = 0; i < C::kDma; ++i) {
+      const int grp = i * 4 + wave;
+      const int row = min(grp * C::kGroupRows + dm.lane_row, dm.n_q - 1 - q0);
+      const uint32_t off = (uint32_t)row * (uint32_t)dm.rs_bytes + dm.lane_col;
+      lds_dma16(stage + grp * C::kPitch, dm.qbase + off0, off);
+      lds_dma16(stage + C::kTileBytes + grp * C::kPitch, dm.dobase + off0, off);
+    }
   }
-  if (tid < 2 * C::kBq) {  // head-major rows: 64 consecutive floats per array
-    const int r = tid & (C::kBq - 1);
-    const int64_t hm = hmbase + q0 + min(r, nrow - 1);
-    if (tid < C::kBq)
-      lpre = r < nrow ? lse2[hm] : INFINITY;  // rows past the end: P = 0
-    else
-      lpre = r < nrow ? dvec[hm] : 0.f;
-  }
+}
+
+// LSE log2(e) (+inf past the end: P = 0) and D of the step's rows, one value per thread.
+__device__ __forceinline__ float kv_rowval(const float* lse2, const float* dvec, int64_t hmbase, int qb, int n_q,
+                                           int tid) {
+  const int r = tid & (kBwdRows - 1);
+  const int q = qb * kBwdRows + r;
+  if (tid < kBwdRows) return q < n_q ? lse2[hmbase + q] : INFINITY;
+  return q < n_q ? dvec[hmbase + q] : 0.f;
 }
 
 // P = exp2(S tau log2e - LSE log2e) and dS = P (dP - D) for one 32-row half of a step, rounded
 // to bf16 in the two B-operand halves (rows 8(i/4) + 4hi + i%4; lse and dd point at row 4hi).
-__device__ __forceinline__ void bwd_p_ds(const f32x16& sacc, const f32x16& dpacc, const float* lse,
-                                         const float* dd, bool k_valid, float scale_log2, bf16x8 (&pb)[2],
+__device__ __forceinline__ void bwd_p_ds(const f32x16& sacc, const f32x16& dpacc, ZL_LDS const float* lse,
+                                         ZL_LDS const float* dd, bool k_valid, float scale_log2, bf16x8 (&pb)[2],
                                          bf16x8 (&dsb)[2]) {
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs) {
@@ -119,8 +168,8 @@ __device__ __forceinline__ void bwd_p_ds(const f32x16& sacc, const f32x16& dpacc
 #pragma unroll
     for (int g2 = 0; g2 < 2; ++g2) {
       const int g = 2 * hs + g2;
-      const f32x4 L = *(const f32x4*)&lse[8 * g];
-      const f32x4 Dd = *(const f32x4*)&dd[8 * g];
+      const f32x4 L = *(ZL_LDS const f32x4*)&lse[8 * g];
+      const f32x4 Dd = *(ZL_LDS const f32x4*)&dd[8 * g];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = 4 * g + u;
@@ -134,28 +183,153 @@ __device__ __forceinline__ void bwd_p_ds(const f32x16& sacc, const f32x16& dpacc
   }
 }
 
+// Operand reads of the key-major kernel (offsets in bytes within a stage's tile).
+template <int D>
+__device__ __forceinline__ bf16x8 kv_row_op(ZL_LDS const char* tile, const int (&rbase)[4], int mb, int st) {
+  using C = KvCfg<D>;
+  constexpr int kHalf = 32 / C::kGroupRows * C::kPitch;
+  return *(ZL_LDS const bf16x8*)(tile + mb * kHalf + rbase[st / C::kSub] + 32 * (st % C::kSub));
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 kv_tr_op(ZL_LDS const char* tile, const int (&tbase)[KvCfg<D>::kCb], int mb, int hs,
+                                           int cb) {
+  using C = KvCfg<D>;
+  const int r0 = 32 * mb + 16 * hs;
+  return cat(lds_read_tr(tile + r0 / C::kGroupRows * C::kPitch + tbase[cb]),
+             lds_read_tr(tile + (r0 + 8) / C::kGroupRows * C::kPitch + tbase[cb]));
+}
+
+// S and dP of one 32-row half (16 MFMAs, S and dP alternating), operands two MFMAs ahead;
+// with kValu, the P / dS of the other half (element m per MFMA, rounded per 8) in the slots.
+template <int D, bool kValu>
+__device__ __forceinline__ void kv_scores(ZL_LDS const char* qt, ZL_LDS const char* dot, const int (&rbase)[4], int mb,
+                                          const bf16x8 (&kreg)[KvCfg<D>::kSteps],
+                                          const bf16x8 (&vreg)[KvCfg<D>::kSteps], f32x16& sacc, f32x16& dpacc,
+                                          const f32x16& s_o, const f32x16& dp_o, const float (&lse_o)[16],
+                                          const float (&dd_o)[16], float scale_log2, bf16x8 (&pb)[2],
+                                          bf16x8 (&dsb)[2]) {
+  using C = KvCfg<D>;
+  constexpr int kM = 2 * C::kSteps;
+  bf16x8 op[kM];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) op[m] = kv_row_op<D>(m & 1 ? dot : qt, rbase, mb, m >> 1);
+  f32x8 pe, ds;
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    if (m + 2 < kM) op[m + 2] = kv_row_op<D>((m + 2) & 1 ? dot : qt, rbase, mb, (m + 2) >> 1);
+    if (m & 1)
+      dpacc = mfma32(op[m], vreg[m >> 1], m == 1 ? f32x16{} : dpacc);
+    else
+      sacc = mfma32(op[m], kreg[m >> 1], m == 0 ? f32x16{} : sacc);
+    if (kValu) {
+#pragma unroll
+      for (int u = 0; u < 16 / kM; ++u) {
+        const int e = m * (16 / kM) + u;
+        const float pv = fast_exp2(fmaf(s_o[e], scale_log2, -lse_o[e]));
+        pe[e % 8] = pv;
+        ds[e % 8] = pv * (dp_o[e] - dd_o[e]);
+        if (e % 8 == 7) {
+          pb[e / 8] = to_bf16x8(pe);
+          dsb[e / 8] = to_bf16x8(ds);
+        }
+      }
+    }
+  }
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS of one half (16 MFMAs, alternating), transposed operands
+// two MFMAs ahead; with kValu, the P / dS of the other half in the slots.
+template <int D, bool kValu>
+__device__ __forceinline__ void kv_grads(ZL_LDS const char* qt, ZL_LDS const char* dot,
+                                         const int (&tbase)[KvCfg<D>::kCb], int mb, const bf16x8 (&pb)[2],
+                                         const bf16x8 (&dsb)[2], f32x16 (&dv_acc)[KvCfg<D>::kCb],
+                                         f32x16 (&dk_acc)[KvCfg<D>::kCb], const f32x16& s_o, const f32x16& dp_o,
+                                         const float (&lse_o)[16], const float (&dd_o)[16], float scale_log2,
+                                         bf16x8 (&pb_o)[2], bf16x8 (&dsb_o)[2]) {
+  using C = KvCfg<D>;
+  constexpr int kM = 4 * C::kCb;  // (hs, cb) x {dV, dK}
+  bf16x8 op[kM];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) op[m] = kv_tr_op<D>(m & 1 ? qt : dot, tbase, mb, (m >> 1) / C::kCb, (m >> 1) % C::kCb);
+  f32x8 pe, ds;
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    if (m + 2 < kM)
+      op[m + 2] = kv_tr_op<D>((m + 2) & 1 ? qt : dot, tbase, mb, ((m + 2) >> 1) / C::kCb, ((m + 2) >> 1) % C::kCb);
+    const int hs = (m >> 1) / C::kCb, cb = (m >> 1) % C::kCb;
+    if (m & 1)
+      dk_acc[cb] = mfma32(op[m], dsb[hs], dk_acc[cb]);
+    else
+      dv_acc[cb] = mfma32(op[m], pb[hs], dv_acc[cb]);
+    if (kValu) {
+#pragma unroll
+      for (int u = 0; u < 16 / kM; ++u) {
+        const int e = m * (16 / kM) + u;
+        const float pv = fast_exp2(fmaf(s_o[e], scale_log2, -lse_o[e]));
+        pe[e % 8] = pv;
+        ds[e % 8] = pv * (dp_o[e] - dd_o[e]);
+        if (e % 8 == 7) {
+          pb_o[e / 8] = to_bf16x8(pe);
+          dsb_o[e / 8] = to_bf16x8(ds);
+        }
+      }
+    }
+  }
+}
+
+// LSE log2(e) and D of the rows 8(e/4) + 4hi + e%4 of half mb.
+__device__ __forceinline__ void kv_rowvals(ZL_LDS const float* lse_s, ZL_LDS const float* dd_s, int mb, int hi,
+                                           float (&lse)[16], float (&dd)[16]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 L = *(ZL_LDS const f32x4*)&lse_s[32 * mb + 8 * g + 4 * hi];
+    const f32x4 Dd = *(ZL_LDS const f32x4*)&dd_s[32 * mb + 8 * g + 4 * hi];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      lse[4 * g + u] = L[u];
+      dd[4 * g + u] = Dd[u];
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   using C = KvCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 q_lds[C::kBq * C::kQld];
-  __shared__ __attribute__((aligned(16))) bf16 do_lds[C::kBq * C::kQld];
-  __shared__ __attribute__((aligned(16))) float lse_lds[C::kBq];
-  __shared__ __attribute__((aligned(16))) float dd_lds[C::kBq];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
   __shared__ int32_t s_item;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(ZL_LDS char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int r_in = (lane & 15) >> 2;                         // transposed-read row within 4
-  const int c_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // transposed-read column within 32
-  const int prow_b = lds_row(l32);                             // physical row of this lane's operand row
-  const int prow_t = lds_row(4 * hi + r_in);                   // physical row of its transposed reads
-  const bf16* __restrict__ gq = (const bf16*)p.q;
   const bf16* __restrict__ gk = (const bf16*)p.k;
   const bf16* __restrict__ gv = (const bf16*)p.v;
-  const bf16* __restrict__ gdo = (const bf16*)p.d_o;
+
+  // Per-lane LDS read offsets (bytes within a tile).
+  // Operand reads of row l32 (+32 per half), k-step s: rbase[s / kSub] + 32 (s % kSub).
+  int rbase[4];
+  {
+    const int x = qt_x<D>(l32);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rbase[k] = qt_row<D>(l32) + 16 * hi + 32 * C::kSub * (k ^ (x / (2 * C::kSub)));
+  }
+  // Transposed reads: lane (r_in, c_in) of rows R + 4hi + r_in, column block cb: tbase[cb] plus
+  // the offset of row R (a multiple of 8).
+  int tbase[C::kCb];
+  {
+    const int r_in = (lane & 15) >> 2;
+    const int c_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int r = 4 * hi + r_in;
+#pragma unroll
+    for (int cb = 0; cb < C::kCb; ++cb)
+      tbase[cb] = qt_row<D>(r) + 16 * ((4 * cb + (c_in >> 3)) ^ qt_x<D>(r)) + 2 * (c_in & 7);
+  }
+  const int dma_row = lane / C::kRowChunks;
+  const int dma_col = 16 * ((lane % C::kRowChunks) ^ qt_x<D>(dma_row));
 
   const int home = blockIdx.x % kQueues;
   int drained = 0;
@@ -168,8 +342,22 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
     const SegDev sg = p.segs[tile.seg];
     const int nh = sg.nh;
     const int h = tile.head;
-    const int64_t rs = (int64_t)nh * D;
     const int nk = tile.nrows;
+
+    KvDma dm;
+    dm.n_q = sg.q_end - sg.q_begin;
+    dm.rs_bytes = (int64_t)nh * D * 2;
+    dm.qbase = (const char*)p.q + (sg.q_row0 + (int64_t)sg.q_begin * nh + h) * D * 2;
+    dm.dobase = (const char*)p.d_o + (sg.q_row0 + (int64_t)sg.q_begin * nh + h) * D * 2;
+    dm.lane_row = dma_row;
+    dm.lane_col = dma_col;
+    dm.lane_off = (uint32_t)dma_row * (uint32_t)dm.rs_bytes + dma_col;
+    const int nqb = (dm.n_q + C::kBq - 1) / C::kBq;
+    const int64_t hmbase = sg.q_row0 + (int64_t)h * sg.lq + sg.q_begin;  // head-major row of local token 0
+
+    // Step 0's rows into stage 0 while this wave's keys load.
+    kv_dma<D>(dm, lds0, 0, wave_u);
+    const float rv0 = tid < 2 * C::kBq ? kv_rowval(p.lse2, p.dvec, hmbase, 0, dm.n_q, tid) : 0.f;
 
     // This wave's 32 keys in registers (B operands, lane = key column); clamped past the end.
     const int key_local = wave * 32 + l32;
@@ -184,143 +372,58 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
         vreg[s] = *(const bf16x8*)(gv + off + 16 * s);
       }
     }
-
     f32x16 dk_acc[C::kCb], dv_acc[C::kCb];
 #pragma unroll
     for (int cb = 0; cb < C::kCb; ++cb) {
       dk_acc[cb] = f32x16{};
       dv_acc[cb] = f32x16{};
     }
+    if (tid < 2 * C::kBq) *(ZL_LDS float*)(lds0 + 2 * C::kTileBytes + 4 * tid) = rv0;
+    dma_wait();
+    __syncthreads();
 
-    const int n_q = sg.q_end - sg.q_begin;
-    const int nqb = (n_q + C::kBq - 1) / C::kBq;
-    const bf16* qbase = gq + (sg.q_row0 + (int64_t)sg.q_begin * nh + h) * D;
-    const bf16* dobase = gdo + (sg.q_row0 + (int64_t)sg.q_begin * nh + h) * D;
-    const int64_t hmbase = sg.q_row0 + (int64_t)h * sg.lq + sg.q_begin;  // head-major row of local token 0
-
-    u32x4 qpre[C::kQChunks], dopre[C::kQChunks];
-    float lpre = 0.f;
-    kv_prefetch<D>(qpre, dopre, lpre, qbase, dobase, rs, hmbase, 0, min(C::kBq, n_q), p.lse2, p.dvec, tid);
     for (int qb = 0; qb < nqb; ++qb) {
-      // Stage this step's Q, dO, LSE (log2 units) and D in LDS.
-#pragma unroll
-      for (int c = 0; c < C::kQChunks; ++c) {
-        const int chunk = tid + c * C::kThreads;
-        const int r = chunk / C::kRowChunks;
-        const int col = (chunk % C::kRowChunks) * 8;
-        *(u32x4*)&q_lds[lds_row(r) * C::kQld + col] = qpre[c];
-        *(u32x4*)&do_lds[lds_row(r) * C::kQld + col] = dopre[c];
-      }
-      if (tid < C::kBq)
-        lse_lds[tid] = lpre;
-      else if (tid < 2 * C::kBq)
-        dd_lds[tid - C::kBq] = lpre;
-      __syncthreads();
+      const uint32_t cur = lds0 + (qb & 1) * C::kStageBytes;
+      const uint32_t nxt = lds0 + ((qb + 1) & 1) * C::kStageBytes;
+      // The next step's rows go to the other stage (read in the previous step, which every
+      // wave has finished); its LSE and D are stored at the end of this step.
+      float rvn = 0.f;
       if (qb + 1 < nqb) {
-        const int q0n = (qb + 1) * C::kBq;
-        kv_prefetch<D>(qpre, dopre, lpre, qbase, dobase, rs, hmbase, q0n, min(C::kBq, n_q - q0n), p.lse2,
-                       p.dvec, tid);
+        kv_dma<D>(dm, nxt, qb + 1, wave_u);
+        if (tid < 2 * C::kBq) rvn = kv_rowval(p.lse2, p.dvec, hmbase, qb + 1, dm.n_q, tid);
       }
+      ZL_LDS const char* qt = (ZL_LDS const char*)cur;
+      ZL_LDS const char* dot = (ZL_LDS const char*)(cur + C::kTileBytes);
+      ZL_LDS const float* lse_s = (ZL_LDS const float*)(cur + 2 * C::kTileBytes);
+      ZL_LDS const float* dd_s = lse_s + C::kBq;
+      constexpr int kHalf = 32 / C::kGroupRows * C::kPitch;  // bytes between the two 32-row halves
 
       // One step = two 32-row halves mb of the 64 query rows. For each half: S = Q K^T and
       // dP = dO V^T (lane = this wave's key column; rows 8(i/4) + 4hi + i%4), then
       // P = exp2(S tau log2e - LSE log2e), dS = P (dP - D), then dV^T += dO^T P and
-      // dK^T += Q^T dS with dO^T and Q^T from transposed reads (k order of P's rows; logical
-      // rows +8 are physical rows +2). The step is software-pipelined in four phases so that
-      // each wave keeps the matrix cores busy while it runs the exponentials of the other
-      // half and waits on LDS:
-      //   A: S, dP of half 0              | LDS: Q, dO operands of half 1
-      //   B: S, dP of half 1              | P, dS of half 0; LDS: transposed operands of half 0
-      //   C: dV, dK of half 0             | P, dS of half 1; LDS: transposed operands of half 1
+      // dK^T += Q^T dS with dO^T and Q^T from transposed reads (k order of P's rows). Keys past
+      // the end of the item need no mask: their P and dS only reach their own dK and dV
+      // columns, which are not written. The step runs in four phases, each written in issue
+      // order, so that the vector work of one half runs under the MFMAs of the other:
+      //   A: S, dP of half 0
+      //   B: S, dP of half 1              | P, dS of half 0
+      //   C: dV, dK of half 0             | P, dS of half 1
       //   D: dV, dK of half 1
-      constexpr int kS = C::kSteps;   // MFMAs per S (or dP) of one half
-      constexpr int kT = 2 * C::kCb;  // MFMAs per dV (or dK) of one half
-      bf16x8 qop0[kS], dop0[kS];
-#pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        qop0[s] = *(const bf16x8*)&q_lds[prow_b * C::kQld + 8 * hi + 16 * s];
-        dop0[s] = *(const bf16x8*)&do_lds[prow_b * C::kQld + 8 * hi + 16 * s];
-      }
-      // Phase A.
+      f32x16 s0, dp0, s1, dp1;
+      bf16x8 pb0[2], dsb0[2], pb1[2], dsb1[2];
+      float lse0[16], dd0[16], lse1[16], dd1[16];
+      kv_rowvals(lse_s, dd_s, 0, hi, lse0, dd0);
+      kv_scores<D, false>(qt, dot, rbase, 0, kreg, vreg, s0, dp0, s1, dp1, lse0, dd0, p.scale_log2, pb1, dsb1);
+      kv_rowvals(lse_s, dd_s, 1, hi, lse1, dd1);
       __builtin_amdgcn_sched_barrier(0);
-      f32x16 s0 = f32x16{}, dp0 = f32x16{};
-      bf16x8 qop1[kS], dop1[kS];
-#pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        s0 = mfma32(qop0[s], kreg[s], s0);
-        dp0 = mfma32(dop0[s], vreg[s], dp0);
-        qop1[s] = *(const bf16x8*)&q_lds[(32 + prow_b) * C::kQld + 8 * hi + 16 * s];
-        dop1[s] = *(const bf16x8*)&do_lds[(32 + prow_b) * C::kQld + 8 * hi + 16 * s];
-      }
-#pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-      }
+      kv_scores<D, true>(qt, dot, rbase, 1, kreg, vreg, s1, dp1, s0, dp0, lse0, dd0, p.scale_log2, pb0, dsb0);
       __builtin_amdgcn_sched_barrier(0);
-      // Phase B.
-      f32x16 s1 = f32x16{}, dp1 = f32x16{};
-#pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        s1 = mfma32(qop1[s], kreg[s], s1);
-        dp1 = mfma32(dop1[s], vreg[s], dp1);
-      }
-      bf16x8 pb[2], dsb[2];
-      bwd_p_ds(s0, dp0, &lse_lds[4 * hi], &dd_lds[4 * hi], k_valid, p.scale_log2, pb, dsb);
-      bf16x8 tdo[kT / 2][2], tq[kT / 2][2];
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-        for (int cb = 0; cb < C::kCb; ++cb) {
-          const int row = 16 * hs + prow_t;
-          const bf16* dp_ = &do_lds[row * C::kQld + cb * 32 + c_in];
-          const bf16* qp_ = &q_lds[row * C::kQld + cb * 32 + c_in];
-          tdo[cb][hs] = cat(lds_read_tr(dp_), lds_read_tr(dp_ + 2 * C::kQld));
-          tq[cb][hs] = cat(lds_read_tr(qp_), lds_read_tr(qp_ + 2 * C::kQld));
-        }
-#pragma unroll
-      for (int s = 0; s < 2 * kS; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads
-      }
+      kv_grads<D, true>(qt, dot, tbase, 0, pb0, dsb0, dv_acc, dk_acc, s1, dp1, lse1, dd1, p.scale_log2, pb1, dsb1);
       __builtin_amdgcn_sched_barrier(0);
-      // Phase C.
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-        for (int cb = 0; cb < C::kCb; ++cb) {
-          dv_acc[cb] = mfma32(tdo[cb][hs], pb[hs], dv_acc[cb]);
-          dk_acc[cb] = mfma32(tq[cb][hs], dsb[hs], dk_acc[cb]);
-        }
-      bf16x8 pb1[2], dsb1[2];
-      bwd_p_ds(s1, dp1, &lse_lds[32 + 4 * hi], &dd_lds[32 + 4 * hi], k_valid, p.scale_log2, pb1, dsb1);
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-        for (int cb = 0; cb < C::kCb; ++cb) {
-          const int row = 32 + 16 * hs + prow_t;
-          const bf16* dp_ = &do_lds[row * C::kQld + cb * 32 + c_in];
-          const bf16* qp_ = &q_lds[row * C::kQld + cb * 32 + c_in];
-          tdo[cb][hs] = cat(lds_read_tr(dp_), lds_read_tr(dp_ + 2 * C::kQld));
-          tq[cb][hs] = cat(lds_read_tr(qp_), lds_read_tr(qp_ + 2 * C::kQld));
-        }
-#pragma unroll
-      for (int s = 0; s < 2 * kT; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads
-      }
+      kv_grads<D, false>(qt, dot, tbase, 1, pb1, dsb1, dv_acc, dk_acc, s1, dp1, lse1, dd1, p.scale_log2, pb0, dsb0);
       __builtin_amdgcn_sched_barrier(0);
-      // Phase D.
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-        for (int cb = 0; cb < C::kCb; ++cb) {
-          dv_acc[cb] = mfma32(tdo[cb][hs], pb1[hs], dv_acc[cb]);
-          dk_acc[cb] = mfma32(tq[cb][hs], dsb1[hs], dk_acc[cb]);
-        }
-      __builtin_amdgcn_sched_barrier(0);
+      if (qb + 1 < nqb && tid < 2 * C::kBq) *(ZL_LDS float*)(nxt + 2 * C::kTileBytes + 4 * tid) = rvn;
+      dma_wait();
       __syncthreads();
     }
 

@@ -86,6 +86,18 @@ struct LdsTile {
 };
 __device__ __forceinline__ int lds_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// Direct global -> LDS load of 16 bytes per lane: lane l reads base + off (off per lane) and
+// its bytes land at lds_base + 16 l (base and lds_base are the same for the whole wave).
+// Issued as inline assembly so that the compiler does not order later LDS reads of other
+// buffers behind it; completion is awaited explicitly (dma_wait) before the workgroup barrier
+// that publishes the buffer.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_base, const char* base, uint32_t off) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+}
+
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Next work item for a workgroup (called by one thread): its own XCD's queue first, then the
 // others in order. `drained` counts the queues found empty and only grows, so every
 // workgroup stops after at most (its items + kQueues) atomics. Returns -1 when all are empty.

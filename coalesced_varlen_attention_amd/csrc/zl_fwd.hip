@@ -93,16 +93,6 @@ struct FwdState {
   float mx;     // row max of the pending score block, log2 units
 };
 
-// Direct global -> LDS load of 16 bytes per lane: lane l reads base + off (off per lane) and
-// its bytes land at lds_base + 16 l (base and lds_base are the same for the whole wave).
-// Issued as inline assembly so that the compiler does not order later LDS reads of other
-// buffers behind it; completion is awaited explicitly (dma_wait) before the workgroup barrier
-// that publishes the buffer.
-__device__ __forceinline__ void lds_dma16(uint32_t lds_base, const char* base, uint32_t off) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
-}
-
 // Global -> LDS load of K block blk. Lane offsets are relative to the block's first key row;
 // in a partial last block, rows past the end of the segment read its last row.
 template <int D>
@@ -143,8 +133,6 @@ __device__ __forceinline__ void dma_v(const FwdCtx<D>& cx, uint32_t v_lds, int b
 }
 
 __global__ void zero_counters_kernel(int32_t* counters) { counters[threadIdx.x * kCounterStride] = 0; }
-
-__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // S^T[key][q] of one block: kKb tiles of 32 keys, each a chain of k-steps over d.
 template <int D>
