@@ -76,7 +76,8 @@ def cpu_baseline(pack, ins, budget_s: float = 12.0) -> dict:
 
 
 KERNEL_SOURCES = [os.path.join(ROOT, "coalesced_varlen_attention_amd", "csrc", f)
-                  for f in ("zl_fwd.hip", "zl_bwd.hip", "zl_device.hpp", "zl_internal.h")]
+                  for f in ("zl_fwd.hip", "zl_bwd.hip", "zl_device.hpp", "zl_internal.h")] + [
+    os.path.join(ROOT, "coalesced_varlen_attention_amd", "build.py")]  # compile flags shape the kernels too
 
 
 def kernel_source_hash() -> str:
