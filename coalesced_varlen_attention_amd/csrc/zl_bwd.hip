@@ -20,7 +20,9 @@
 // dQ kernel: one item = 128 query rows of one (segment or ring group, head); 4 waves x 32
 //   query rows, the forward's shape: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers
 //   (lane = one query row, whose LSE and D are then per-lane scalars), and
-//   dQ^T += K^T dS^T with K^T from transposed LDS reads. dQ is written once: no atomics.
+//   dQ^T += K^T dS^T with K^T from transposed LDS reads. K and V blocks reach LDS by direct
+//   global-to-LDS loads in the key-major kernel's layout, one block ahead. dQ is written
+//   once: no atomics.
 //   Computing dQ in its own query-major pass costs S and dP a second time, but fp32 atomics
 //   into dQ from every key block were measured to cost more than the whole key-major pass.
 #include "zl_device.hpp"
@@ -452,43 +454,38 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
 template <int D>
 struct DqCfg {
   static constexpr int kThreads = 256;
-  static constexpr int kBk = 64;                          // keys per block
-  static constexpr int kKld = LdsTile<D>::kLd;            // K row stride (natural and transposed reads)
-  static constexpr int kVld = LdsTile<D>::kLd;            // V row stride (natural reads)
+  static constexpr int kBk = kBwdRows;                    // keys per block (64)
   static constexpr int kSteps = D / 16;
   static constexpr int kCb = D / 32;
-  static constexpr int kChunks = kBk * D / 8 / kThreads;
-  static constexpr int kRowChunks = D / 8;
+  // K and V blocks use the key-major kernel's tile layout (64 rows, both read kinds free of
+  // bank conflicts): K is read by rows (S^T = K Q^T) and transposed (dQ^T = K^T dS^T), V by rows.
+  static constexpr int kTileBytes = KvCfg<D>::kTileBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes;
 };
 
+// Global -> LDS loads of one key block: rows [0, 64) after `kblk` / `vblk` (the block's first
+// key row), rows at or past `rows` read row rows - 1.
 template <int D>
-__device__ __forceinline__ void dq_load_block(u32x4 (&kreg)[DqCfg<D>::kChunks], u32x4 (&vreg)[DqCfg<D>::kChunks],
-                                              const bf16* kbase, const bf16* vbase, int64_t rs, int key0, int n_kv,
-                                              int tid) {
-  using C = DqCfg<D>;
+__device__ __forceinline__ void dq_dma(uint32_t stage, const char* kblk, const char* vblk, int64_t rs_bytes, int rows,
+                                       uint32_t lane_off, int lane_row, int lane_col, int wave) {
+  using L = KvCfg<D>;
+  if (rows >= L::kBq) {
 #pragma unroll
-  for (int c = 0; c < C::kChunks; ++c) {
-    const int chunk = tid + c * C::kThreads;
-    const int r = chunk / C::kRowChunks;
-    const int col = (chunk % C::kRowChunks) * 8;
-    const int key = min(key0 + r, n_kv - 1);
-    kreg[c] = *(const u32x4*)(kbase + (int64_t)key * rs + col);
-    vreg[c] = *(const u32x4*)(vbase + (int64_t)key * rs + col);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void dq_store_block(const u32x4 (&kreg)[DqCfg<D>::kChunks],
-                                               const u32x4 (&vreg)[DqCfg<D>::kChunks], bf16* k_lds, bf16* v_lds,
-                                               int tid) {
-  using C = DqCfg<D>;
+    for (int i = 0; i < L::kDma; ++i) {
+      const int grp = i * 4 + wave;
+      const int64_t off = (int64_t)grp * L::kGroupRows * rs_bytes;
+      lds_dma16(stage + grp * L::kPitch, kblk + off, lane_off);
+      lds_dma16(stage + L::kTileBytes + grp * L::kPitch, vblk + off, lane_off);
+    }
+  } else {
 #pragma unroll
-  for (int c = 0; c < C::kChunks; ++c) {
-    const int chunk = tid + c * C::kThreads;
-    const int r = chunk / C::kRowChunks;
-    const int col = (chunk % C::kRowChunks) * 8;
-    *(u32x4*)&k_lds[lds_row(r) * C::kKld + col] = kreg[c];
-    *(u32x4*)&v_lds[lds_row(r) * C::kVld + col] = vreg[c];
+    for (int i = 0; i < L::kDma; ++i) {
+      const int grp = i * 4 + wave;
+      const int row = min(grp * L::kGroupRows + lane_row, rows - 1);
+      const uint32_t off = (uint32_t)row * (uint32_t)rs_bytes + lane_col;
+      lds_dma16(stage + grp * L::kPitch, kblk, off);
+      lds_dma16(stage + L::kTileBytes + grp * L::kPitch, vblk, off);
+    }
   }
 }
 
@@ -508,26 +505,113 @@ __device__ __forceinline__ void chain_block(const int32_t* ranges, int off, int 
   }
 }
 
+// dS^T = exp2(S^T tau log2e - LSE log2e) (dP^T - D) of element e of a tile (lane = query row).
+__device__ __forceinline__ float dq_ds(float s, float dp, float scale_log2, float lse2, float dd) {
+  return fast_exp2(fmaf(s, scale_log2, -lse2)) * (dp - dd);
+}
+
+// S^T and dP^T of one 32-key half of a block (16 MFMAs, alternating), operands two MFMAs ahead;
+// with kValu, the dS^T of the other half (one element per MFMA, rounded per 8) in the slots.
+template <int D, bool kValu>
+__device__ __forceinline__ void dq_scores(ZL_LDS const char* kt, ZL_LDS const char* vt, const int (&rbase)[4], int kb,
+                                          const bf16x8 (&qreg)[DqCfg<D>::kSteps],
+                                          const bf16x8 (&doreg)[DqCfg<D>::kSteps], f32x16& sacc, f32x16& dpacc,
+                                          const f32x16& s_o, const f32x16& dp_o, float scale_log2, float lse2, float dd,
+                                          bf16x8 (&dsb)[2]) {
+  using C = DqCfg<D>;
+  constexpr int kM = 2 * C::kSteps;
+  bf16x8 op[kM];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) op[m] = kv_row_op<D>(m & 1 ? vt : kt, rbase, kb, m >> 1);
+  f32x8 x;
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    if (m + 2 < kM) op[m + 2] = kv_row_op<D>((m + 2) & 1 ? vt : kt, rbase, kb, (m + 2) >> 1);
+    if (m & 1)
+      dpacc = mfma32(op[m], doreg[m >> 1], m == 1 ? f32x16{} : dpacc);
+    else
+      sacc = mfma32(op[m], qreg[m >> 1], m == 0 ? f32x16{} : sacc);
+    if (kValu) {
+#pragma unroll
+      for (int u = 0; u < 16 / kM; ++u) {
+        const int e = m * (16 / kM) + u;
+        x[e % 8] = dq_ds(s_o[e], dp_o[e], scale_log2, lse2, dd);
+        if (e % 8 == 7) dsb[e / 8] = to_bf16x8(x);
+      }
+    }
+  }
+}
+
+// dQ^T += K^T dS^T of one half (2 x kCb MFMAs), transposed operands two MFMAs ahead; with
+// kValu, the dS^T of the other half in the slots.
+template <int D, bool kValu>
+__device__ __forceinline__ void dq_grads(ZL_LDS const char* kt, const int (&tbase)[DqCfg<D>::kCb], int kb,
+                                         const bf16x8 (&dsb)[2], f32x16 (&acc)[DqCfg<D>::kCb], const f32x16& s_o,
+                                         const f32x16& dp_o, float scale_log2, float lse2, float dd,
+                                         bf16x8 (&dsb_o)[2]) {
+  using C = DqCfg<D>;
+  constexpr int kM = 2 * C::kCb;
+  bf16x8 op[kM];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) op[m] = kv_tr_op<D>(kt, tbase, kb, m / C::kCb, m % C::kCb);
+  f32x8 x;
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    if (m + 2 < kM) op[m + 2] = kv_tr_op<D>(kt, tbase, kb, (m + 2) / C::kCb, (m + 2) % C::kCb);
+    acc[m % C::kCb] = mfma32(op[m], dsb[m / C::kCb], acc[m % C::kCb]);
+    if (kValu) {
+#pragma unroll
+      for (int u = 0; u < 16 / kM; ++u) {
+        const int e = m * (16 / kM) + u;
+        x[e % 8] = dq_ds(s_o[e], dp_o[e], scale_log2, lse2, dd);
+        if (e % 8 == 7) dsb_o[e / 8] = to_bf16x8(x);
+      }
+    }
+  }
+}
+
+// Keys at or past vr (lane-independent offsets 8(i/4) + i%4) get S = -inf, hence P = 0.
+__device__ __forceinline__ void dq_mask(f32x16& s, int vr) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (8 * (i / 4) + (i % 4) >= vr) s[i] = -INFINITY;
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][C::kBk * C::kKld];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][C::kBk * C::kVld];
+  using L = KvCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
   __shared__ int32_t s_item;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(ZL_LDS char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int r_in = (lane & 15) >> 2;
-  const int c_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int prow_b = lds_row(l32);
-  const int prow_t = lds_row(4 * hi + r_in);
   const bf16* __restrict__ gq = (const bf16*)p.q;
-  const bf16* __restrict__ gk = (const bf16*)p.k;
-  const bf16* __restrict__ gv = (const bf16*)p.v;
   const bf16* __restrict__ gdo = (const bf16*)p.d_o;
+
+  // Per-lane LDS read offsets within a tile (as in the key-major kernel).
+  int rbase[4];
+  {
+    const int x = qt_x<D>(l32);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rbase[k] = qt_row<D>(l32) + 16 * hi + 32 * L::kSub * (k ^ (x / (2 * L::kSub)));
+  }
+  int tbase[C::kCb];
+  {
+    const int r_in = (lane & 15) >> 2;
+    const int c_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int r = 4 * hi + r_in;
+#pragma unroll
+    for (int cb = 0; cb < C::kCb; ++cb)
+      tbase[cb] = qt_row<D>(r) + 16 * ((4 * cb + (c_in >> 3)) ^ qt_x<D>(r)) + 2 * (c_in & 7);
+  }
+  const int dma_row = lane / L::kRowChunks;
+  const int dma_col = 16 * ((lane % L::kRowChunks) ^ qt_x<D>(dma_row));
 
   const int home = blockIdx.x % kQueues;
   int drained = 0;
@@ -540,7 +624,22 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
     const SegDev sg = p.segs[tile.seg];
     const int nh = sg.nh;
     const int h = tile.head;
-    const int64_t rs = (int64_t)nh * D;
+    const int64_t rs_bytes = (int64_t)nh * D * 2;
+    const uint32_t lane_off = (uint32_t)dma_row * (uint32_t)rs_bytes + dma_col;
+    const char* kseq = (const char*)p.k + (sg.kv_row0 + h) * D * 2;
+    const char* vseq = (const char*)p.v + (sg.kv_row0 + h) * D * 2;
+
+    int n_blk = 0;
+    for (int r = 0; r < sg.chain_len; ++r) {
+      const int len = p.kv_ranges[2 * (sg.chain_off + r) + 1] - p.kv_ranges[2 * (sg.chain_off + r)];
+      n_blk += (len + C::kBk - 1) / C::kBk;
+    }
+    int kv0, n_kv, key0;
+    chain_block(p.kv_ranges, sg.chain_off, sg.chain_len, 0, C::kBk, &kv0, &n_kv, &key0);
+    {
+      const int64_t off = (int64_t)(kv0 + key0) * rs_bytes;
+      dq_dma<D>(lds0, kseq + off, vseq + off, rs_bytes, n_kv - key0, lane_off, dma_row, dma_col, wave_u);
+    }
 
     // This lane's query row (clamped; results of clamped rows are dropped), with its Q and dO
     // as B operands (k = d) and its LSE (log2 units) and D as scalars.
@@ -558,70 +657,43 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
     const float lse2 = p.lse2[hm];
     const float dd = p.dvec[hm];
 
-    int n_blk = 0;
-    for (int r = 0; r < sg.chain_len; ++r) {
-      const int len = p.kv_ranges[2 * (sg.chain_off + r) + 1] - p.kv_ranges[2 * (sg.chain_off + r)];
-      n_blk += (len + C::kBk - 1) / C::kBk;
-    }
-    const bf16* kseq = gk + (sg.kv_row0 + h) * D;
-    const bf16* vseq = gv + (sg.kv_row0 + h) * D;
-
     f32x16 acc[C::kCb];
 #pragma unroll
     for (int cb = 0; cb < C::kCb; ++cb) acc[cb] = f32x16{};
-
-    u32x4 kreg[C::kChunks], vreg[C::kChunks];
-    int kv0, n_kv, key0;
-    chain_block(p.kv_ranges, sg.chain_off, sg.chain_len, 0, C::kBk, &kv0, &n_kv, &key0);
-    dq_load_block<D>(kreg, vreg, kseq + (int64_t)kv0 * rs, vseq + (int64_t)kv0 * rs, rs, key0, n_kv, tid);
-    dq_store_block<D>(kreg, vreg, k_lds[0], v_lds[0], tid);
+    dma_wait();
     __syncthreads();
 
     for (int j = 0; j < n_blk; ++j) {
-      const int buf = j & 1;
+      const uint32_t cur = lds0 + (j & 1) * C::kStageBytes;
       const int valid = n_kv - key0;  // keys of this block inside its range
       if (j + 1 < n_blk) {
         chain_block(p.kv_ranges, sg.chain_off, sg.chain_len, j + 1, C::kBk, &kv0, &n_kv, &key0);
-        dq_load_block<D>(kreg, vreg, kseq + (int64_t)kv0 * rs, vseq + (int64_t)kv0 * rs, rs, key0, n_kv, tid);
+        const int64_t off = (int64_t)(kv0 + key0) * rs_bytes;
+        dq_dma<D>(lds0 + ((j + 1) & 1) * C::kStageBytes, kseq + off, vseq + off, rs_bytes, n_kv - key0, lane_off,
+                  dma_row, dma_col, wave_u);
       }
+      ZL_LDS const char* kt = (ZL_LDS const char*)cur;
+      ZL_LDS const char* vt = (ZL_LDS const char*)(cur + C::kTileBytes);
 
       // Per 32-key half kb: S^T = K Q^T and dP^T = V dO^T, then
       // dS^T = P^T (dP^T - D) with P^T = exp2(S^T tau log2e - LSE log2e) (keys past the range: 0),
-      // then dQ^T[c][q] += K^T[c][key] dS^T[key][q] in the k order of dS^T's rows.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
-        const bf16* kr = &k_lds[buf][(kb * 32 + prow_b) * C::kKld + 8 * hi];
-        const bf16* vr = &v_lds[buf][(kb * 32 + prow_b) * C::kVld + 8 * hi];
-#pragma unroll
-        for (int s = 0; s < C::kSteps; ++s) {
-          sacc = mfma32(*(const bf16x8*)(kr + 16 * s), qreg[s], sacc);
-          dpacc = mfma32(*(const bf16x8*)(vr + 16 * s), doreg[s], dpacc);
-        }
-        bf16x8 dsb[2];
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          f32x8 x;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int i = 8 * hs + u;
-            const int key = kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
-            const float pe = key < valid ? fast_exp2(fmaf(sacc[i], p.scale_log2, -lse2)) : 0.f;
-            x[u] = pe * (dpacc[i] - dd);
-          }
-          dsb[hs] = to_bf16x8(x);
-        }
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const int row = kb * 32 + 16 * hs + prow_t;
-#pragma unroll
-          for (int cb = 0; cb < C::kCb; ++cb) {
-            const bf16* kp = &k_lds[buf][row * C::kKld + cb * 32 + c_in];
-            acc[cb] = mfma32(cat(lds_read_tr(kp), lds_read_tr(kp + 2 * C::kKld)), dsb[hs], acc[cb]);
-          }
-        }
-      }
-      if (j + 1 < n_blk) dq_store_block<D>(kreg, vreg, k_lds[buf ^ 1], v_lds[buf ^ 1], tid);
+      // then dQ^T[c][q] += K^T[c][key] dS^T[key][q] in the k order of dS^T's rows. Four phases,
+      // each in issue order, so that the vector work of one half runs under the MFMAs of the
+      // other: A: S, dP of half 0 | B: S, dP of half 1 with dS of half 0 |
+      // C: dQ of half 0 with dS of half 1 | D: dQ of half 1.
+      f32x16 s0, dp0, s1, dp1;
+      bf16x8 dsb0[2], dsb1[2];
+      dq_scores<D, false>(kt, vt, rbase, 0, qreg, doreg, s0, dp0, s1, dp1, p.scale_log2, lse2, dd, dsb1);
+      if (valid < C::kBk) dq_mask(s0, valid - 4 * hi);
+      __builtin_amdgcn_sched_barrier(0);
+      dq_scores<D, true>(kt, vt, rbase, 1, qreg, doreg, s1, dp1, s0, dp0, p.scale_log2, lse2, dd, dsb0);
+      if (valid < C::kBk) dq_mask(s1, valid - 32 - 4 * hi);
+      __builtin_amdgcn_sched_barrier(0);
+      dq_grads<D, true>(kt, tbase, 0, dsb0, acc, s1, dp1, p.scale_log2, lse2, dd, dsb1);
+      __builtin_amdgcn_sched_barrier(0);
+      dq_grads<D, false>(kt, tbase, 1, dsb1, acc, s1, dp1, p.scale_log2, lse2, dd, dsb0);
+      __builtin_amdgcn_sched_barrier(0);
+      dma_wait();
       __syncthreads();
     }
 
