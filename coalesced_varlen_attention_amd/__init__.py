@@ -65,6 +65,7 @@ def _load() -> ctypes.CDLL:
         "zl_plan_queues": (I32, [P, I32, P, I32, ctypes.POINTER(I32)]),
         "zl_plan_destroy": (None, [P]),
         "zl_attn_fwd": (I32, [P, P, P, P, P, P, P, P, P, P]),
+        "zl_attn_fwd_accumulate": (I32, [P, P, P, P, P, P, P, P]),
         "zl_lse_merge": (I32, [I32, I64, I32, P, P, P, P, P]),
         "zl_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, P]),
         "zl_attn_bwd_stages": (I32, [P, P, P, P, P, P, P, P, P, P, P, U32, P]),
@@ -219,6 +220,27 @@ def attn_fwd(plan: Plan, q, k, v, o=None, lse=None, o_part=None, lse_part=None, 
     _check(lib().zl_attn_fwd(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             _ptr(o_part), _ptr(lse_part), workspace.data_ptr(), _stream_handle(stream)))
     return o, lse, o_part, lse_part
+
+
+def attn_fwd_accumulate(plan: Plan, q, k, v, o, lse, workspace=None, stream=None):
+    """Forward with a running merge (``zl_attn_fwd_accumulate``): every ring part of ``plan``
+    folds its result into ``o``/``lse`` at its group's rows (set ``lse`` to -inf there before
+    a group's first block); ``part == -1`` segments are written as in ``attn_fwd``. The plan
+    may hold at most one part per group. Returns ``(o, lse)``."""
+    import torch
+    info, d, dev = plan.info, plan.d, q.device
+    _check_tensor(q, "q", torch.bfloat16, info["q_rows"], d, dev)
+    _check_tensor(k, "k", torch.bfloat16, info["kv_rows"], d, dev)
+    _check_tensor(v, "v", torch.bfloat16, info["kv_rows"], d, dev)
+    _check_tensor(o, "o", torch.float32, info["q_rows"], d, dev)
+    _check_tensor(lse, "lse", torch.float32, info["q_rows"], 1, dev)
+    if workspace is None:
+        workspace = torch.empty(info["ws_fwd"], dtype=torch.uint8, device=dev)
+    if workspace.numel() < info["ws_fwd"]:
+        raise ValueError("workspace too small")
+    _check(lib().zl_attn_fwd_accumulate(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        lse.data_ptr(), workspace.data_ptr(), _stream_handle(stream)))
+    return o, lse
 
 
 def lse_merge(n_parts: int, n_rows: int, d: int, o_part, lse_part, o, lse, stream=None) -> None:

@@ -144,6 +144,38 @@ extern "C" zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void*
   return launch_status(zl::launch_fwd(plan->d, p, grid, stream), "zl_attn_fwd");
 }
 
+extern "C" zl_status zl_attn_fwd_accumulate(const zl_plan* plan, const void* q, const void* k, const void* v,
+                                            float* o, float* lse, void* workspace, void* stream) {
+  if (!plan) return fail(ZL_ERR_INVALID, "zl_attn_fwd_accumulate: plan is NULL");
+  for (const zl_group_info_t& g : plan->groups)
+    if (g.n_parts > 1)
+      return fail(ZL_ERR_INVALID,
+                  "zl_attn_fwd_accumulate: a group has " + std::to_string(g.n_parts) +
+                      " parts in this plan; two parts of one group would fold into the same rows at once");
+  zl_status st = check_runnable(plan, "zl_attn_fwd_accumulate");
+  if (st != ZL_OK) return st;
+  if (!q || !k || !v) return fail(ZL_ERR_INVALID, "zl_attn_fwd_accumulate: q, k or v is NULL");
+  if (!workspace) return fail(ZL_ERR_INVALID, "zl_attn_fwd_accumulate: workspace is NULL");
+  if (!o || !lse) return fail(ZL_ERR_INVALID, "zl_attn_fwd_accumulate: o or lse is NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(workspace, 16) ||
+      !aligned(lse, 4))
+    return fail(ZL_ERR_INVALID, "zl_attn_fwd_accumulate: q/k/v/o/workspace must be 16-byte aligned, lse 4-byte");
+  zl::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.segs = plan->d_segs;
+  p.queue = {plan->d_fwd, plan->d_bounds, (int32_t*)workspace};
+  p.scale_log2 = plan->scale * 1.4426950408889634f;
+  p.accumulate = 1;
+  const int per_cu = zl::fwd_blocks_per_cu(plan->d);
+  if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_fwd_accumulate: forward kernel cannot be resident");
+  const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, (int64_t)plan->fwd_tiles.size());
+  return launch_status(zl::launch_fwd(plan->d, p, grid, stream), "zl_attn_fwd_accumulate");
+}
+
 extern "C" zl_status zl_lse_merge(int32_t n_parts, int64_t n_rows, int32_t d_head, const float* o_part,
                                   const float* lse_part, float* o, float* lse, void* stream) {
   if (d_head != 64 && d_head != 128)

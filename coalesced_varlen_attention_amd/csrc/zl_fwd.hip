@@ -497,14 +497,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
     }
     value_block<D>(cx, ((n - 1) & 1) ? v_lds1 : v_lds0, pb, st.oacc);  // P(n-1) V(n-1)
 
-    // Epilogue: O = O_acc / l, LSE = ln(2) * (m + log2 l), natural log.
+    // Epilogue: O = O_acc / l, LSE = ln(2) * (m + log2 l), natural log. A ring part writes
+    // its normalised partial to the slab, or in accumulate mode folds it into the running
+    // O and LSE of its rows (exact merge of two normalised results, §II-B):
+    //   LSE' = M + ln(e^{LSE - M} + e^{LSE_b - M}),  O' = e^{LSE - LSE'} O + e^{LSE_b - LSE'} O_b.
+    // Rows whose running LSE is -inf take the part as it is (their O is not read).
     const float l_tot = half_sum(st.l_run);
     if (q_valid) {
       const float inv = 1.0f / l_tot;
+      const float lse_b = 0.69314718055994531f * (st.m_run + __log2f(l_tot));
+      const bool fold = sg.part >= 0 && p.accumulate;
       float* orow;
       int64_t lrow;
       float* lse_out;
-      if (sg.part < 0) {
+      if (sg.part < 0 || fold) {
         lrow = sg.q_row0 + (int64_t)qtok * nh + h;
         orow = p.o + lrow * D;
         lse_out = p.lse;
@@ -513,16 +519,27 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
         orow = p.o_part + lrow * D;
         lse_out = p.lse_part;
       }
+      float w_old = 0.f, w_new = inv, lse_new = lse_b;
+      if (fold) {
+        const float lse_a = lse_out[lrow];
+        if (lse_a != -INFINITY) {
+          const float mx = fmaxf(lse_a, lse_b);
+          lse_new = mx + logf(expf(lse_a - mx) + expf(lse_b - mx));
+          w_old = expf(lse_a - lse_new);
+          w_new = expf(lse_b - lse_new) * inv;
+        }
+      }
 #pragma unroll
       for (int cb = 0; cb < C::kCb; ++cb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int c = cb * 32 + 8 * g + 4 * hi;
-          f32x4 val = {st.oacc[cb][4 * g] * inv, st.oacc[cb][4 * g + 1] * inv, st.oacc[cb][4 * g + 2] * inv,
-                       st.oacc[cb][4 * g + 3] * inv};
+          f32x4 val = {st.oacc[cb][4 * g] * w_new, st.oacc[cb][4 * g + 1] * w_new, st.oacc[cb][4 * g + 2] * w_new,
+                       st.oacc[cb][4 * g + 3] * w_new};
+          if (w_old != 0.f) val += *(const f32x4*)(orow + c) * w_old;
           *(f32x4*)(orow + c) = val;
         }
-      if (hi == 0) lse_out[lrow] = 0.69314718055994531f * (st.m_run + __log2f(l_tot));
+      if (hi == 0) lse_out[lrow] = lse_new;
     }
     __syncthreads();
   }

@@ -64,6 +64,7 @@ struct FwdParams {
   const SegDev* segs;
   Queues queue;
   float scale_log2;  // softmax scale times log2(e)
+  int32_t accumulate;  // ring parts fold into o/lse (running merge) instead of the slab
 };
 
 struct BwdParams {

@@ -161,6 +161,28 @@ zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void* k, const v
                       void* workspace, void* stream);
 
 /*
+ * Forward with a running merge (ring accumulation, §II-B: the output is accumulated block by
+ * block as key/value blocks arrive). Like zl_attn_fwd, except that every ring part folds its
+ * normalised partial result O_b, LSE_b into the running result held in o and lse at the
+ * group's rows (o_row of zl_plan_group), with no partial slab:
+ *   LSE' = M + ln(exp(LSE - M) + exp(LSE_b - M)),  M = max(LSE, LSE_b)
+ *   O'   = exp(LSE - LSE') * O + exp(LSE_b - LSE') * O_b
+ * Before a group's first block the caller sets its rows of lse to -inf; such rows take the
+ * part as it is and their o is not read. Folding the parts of a group one call at a time, in
+ * any order, gives the exact merge of zl_lse_merge (up to rounding).
+ *   q, k, v     bf16 device tensors in the packed layout
+ *   o, lse      fp32 running results (in/out for ring parts; output for part == -1 segments)
+ *   workspace   device memory of info.ws_fwd bytes, 256-B aligned, not shared with a
+ *               concurrent call
+ *   stream      hipStream_t, NULL for the default stream
+ * A plan used here may hold at most one part of each group (ZL_ERR_INVALID otherwise): two
+ * parts of a group would fold into the same rows at once. Calls that fold into the same rows
+ * must be ordered (one stream, or events). Pointers must be 16-B aligned.
+ */
+zl_status zl_attn_fwd_accumulate(const zl_plan* plan, const void* q, const void* k, const void* v,
+                                 float* o, float* lse, void* workspace, void* stream);
+
+/*
  * Exact merge of n_parts normalised partial results over disjoint key blocks (ring
  * accumulation, §II-B): for every row r,
  *   LSE[r] = M + ln sum_b exp(lse_part[b][r] - M),  M = max_b lse_part[b][r]

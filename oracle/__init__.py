@@ -5,7 +5,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 never imports it. Every function states the passage of the Zellige page it follows.
 """
 from .attention import (PackLayout, default_scale, head_backward, head_forward, head_probs,
-                        head_scores, lse_merge, pack_backward, pack_forward)
+                        head_scores, lse_merge, pack_backward, pack_forward, running_merge)
 
 __all__ = ["PackLayout", "default_scale", "head_backward", "head_forward", "head_probs",
-           "head_scores", "lse_merge", "pack_backward", "pack_forward"]
+           "head_scores", "lse_merge", "pack_backward", "pack_forward", "running_merge"]

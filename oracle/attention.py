@@ -167,6 +167,33 @@ def lse_merge(o_parts: np.ndarray, lse_parts: np.ndarray) -> Tuple[np.ndarray, n
     return o, lse
 
 
+def running_merge(o_acc: np.ndarray, lse_acc: np.ndarray, o_b: np.ndarray,
+                  lse_b: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Fold one more normalised partial into a running (O, LSE) pair (ring, §II-B).
+
+    The ring step that receives key block b updates the accumulated result in place:
+    ``LSE' = ln(exp LSE + exp LSE_b)`` and ``O' = exp(LSE - LSE') O + exp(LSE_b - LSE') O_b``.
+    A side with LSE = -inf carries no keys and has weight 0, so folding a part into the
+    empty pair ``(anything, -inf)`` returns the part. Rows: ``o_*`` is ``[rows, d]``, ``lse_*`` is
+    ``[rows]``.
+    """
+    o_acc = np.asarray(o_acc, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    lse_acc = np.asarray(lse_acc, dtype=np.float64)
+    lse_b = np.asarray(lse_b, dtype=np.float64)
+    m = np.maximum(lse_acc, lse_b)
+    live = np.isfinite(m)
+    m_safe = np.where(live, m, 0.0)
+    ea = np.where(np.isfinite(lse_acc), np.exp(lse_acc - m_safe), 0.0)
+    eb = np.where(np.isfinite(lse_b), np.exp(lse_b - m_safe), 0.0)
+    tot = np.where(live, ea + eb, 1.0)
+    lse = np.where(live, m_safe + np.log(tot), -np.inf)
+    # a side of weight 0 is not read at all: its O may hold anything, NaN included
+    wa, wb = (ea / tot)[:, None], (eb / tot)[:, None]
+    o = np.where(wa > 0, wa * o_acc, 0.0) + np.where(wb > 0, wb * o_b, 0.0)
+    return o, lse
+
+
 class PackLayout:
     """Row layout of a packed batch: sequence s stores its tokens as ``[tokens, heads_s, d]``.
 

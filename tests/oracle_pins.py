@@ -235,6 +235,39 @@ def pin_merge_empty_parts():
     assert np.all(mo == 0.0) and np.all(np.isneginf(ml))
 
 
+def pin_running_merge():
+    """Folding the parts one at a time, in any order, into the empty pair equals the batch
+    merge and unsplit attention; folding into the empty pair returns the part unchanged,
+    whatever O the empty pair holds; folding an empty part changes nothing."""
+    r = _rng(23)
+    q, k, v = r.normal(size=(7, 5)), r.normal(size=(31, 5)), r.normal(size=(31, 5))
+    o, lse = A.head_forward(q, k, v, 0.7)
+    cuts = [0, 3, 4, 19, 31]
+    parts = [A.head_forward(q, k[a:b], v[a:b], 0.7) for a, b in zip(cuts[:-1], cuts[1:])]
+    for order in ([0, 1, 2, 3], [3, 1, 0, 2], [2, 3, 1, 0]):
+        acc_o = np.full((7, 5), np.nan)
+        acc_l = np.full(7, -np.inf)
+        for i in order:
+            acc_o, acc_l = A.running_merge(acc_o, acc_l, *parts[i])
+        _close(acc_o, o, 1e-13, f"running merge O, order {order}")
+        _close(acc_l, lse, 1e-13, f"running merge LSE, order {order}")
+    bo, bl = A.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    _close(acc_o, bo, 1e-13, "running vs batch merge O")
+    _close(acc_l, bl, 1e-13, "running vs batch merge LSE")
+    # first fold: the part itself, bit for bit
+    fo, fl = A.running_merge(np.full((7, 5), np.nan), np.full(7, -np.inf), *parts[2])
+    assert np.array_equal(fo, parts[2][0]) and np.array_equal(fl, parts[2][1])
+    # an empty part (LSE = -inf) leaves the running pair as it is
+    eo, el = A.running_merge(parts[1][0], parts[1][1], np.full((7, 5), np.nan), np.full(7, -np.inf))
+    assert np.array_equal(eo, parts[1][0]) and np.array_equal(el, parts[1][1])
+    # two equal LSEs: the mean of the two outputs and LSE + ln 2
+    a_o, b_o = r.normal(size=(3, 2)), r.normal(size=(3, 2))
+    l = r.normal(size=3)
+    mo, ml = A.running_merge(a_o, l, b_o, l)
+    _close(mo, 0.5 * (a_o + b_o), 1e-15, "equal-weight fold O")
+    _close(ml, l + np.log(2.0), 1e-15, "equal-weight fold LSE")
+
+
 # ---------------------------------------------------------------- pack-level
 
 def _rand_pack_inputs(r, seq_q, seq_kv, heads, d):
@@ -364,5 +397,6 @@ def pin_pack_layout():
 ALL_PINS = [pin_brute_force_forward, pin_zero_query, pin_single_key, pin_two_keys_scalar, pin_constant_v,
             pin_dominant_key, pin_zero_upstream, pin_probs_rows_sum_to_one, pin_key_permutation,
             pin_lse_bounds, pin_gradient_sums, pin_merge_equals_unsplit, pin_merge_empty_parts,
+            pin_running_merge,
             pin_block_diagonal_separation, pin_head_and_query_slices, pin_pack_kv_split_equals_whole,
             pin_finite_differences, pin_pack_layout]

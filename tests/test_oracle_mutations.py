@@ -87,6 +87,25 @@ def merge_wrong_shift(o_parts, lse_parts):
     return (w[:, :, None] * o_parts).sum(axis=0), lse - 1e-3
 
 
+def running_merge_weights_swapped(o_acc, lse_acc, o_b, lse_b):
+    m = np.maximum(lse_acc, lse_b)
+    ea = np.where(np.isfinite(lse_acc), np.exp(lse_acc - m), 0.0)
+    eb = np.where(np.isfinite(lse_b), np.exp(lse_b - m), 0.0)
+    tot = ea + eb
+    o = np.nan_to_num((eb / tot)[:, None] * np.nan_to_num(o_acc)) + np.nan_to_num((ea / tot)[:, None] * o_b)
+    return o, m + np.log(tot)
+
+
+def running_merge_lse_max_only(o_acc, lse_acc, o_b, lse_b):
+    m = np.maximum(lse_acc, lse_b)
+    ea = np.where(np.isfinite(lse_acc), np.exp(lse_acc - m), 0.0)
+    eb = np.where(np.isfinite(lse_b), np.exp(lse_b - m), 0.0)
+    tot = ea + eb
+    wa, wb = (ea / tot)[:, None], (eb / tot)[:, None]
+    o = np.where(wa > 0, wa * o_acc, 0.0) + np.where(wb > 0, wb * o_b, 0.0)
+    return o, m
+
+
 class _WrongHeadLayout(A.PackLayout):
     """Reads K/V of the neighbouring head: a wrong index in the row layout."""
 
@@ -128,6 +147,8 @@ MUTANTS = {
     "p_without_lse": ("head_backward", _bwd_variant("p_without_lse")),
     "merge_unnormalised": ("lse_merge", merge_unnormalised),
     "merge_wrong_shift": ("lse_merge", merge_wrong_shift),
+    "running_merge_weights_swapped": ("running_merge", running_merge_weights_swapped),
+    "running_merge_lse_is_max": ("running_merge", running_merge_lse_max_only),
     "kv_rows_of_wrong_head": ("PackLayout", _WrongHeadLayout),
     "token_head_strides_swapped": ("PackLayout", _TransposedLayout),
     "parts_overwrite_dq": ("pack_backward", pack_backward_overwrites_parts),

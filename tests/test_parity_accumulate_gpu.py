@@ -1,0 +1,91 @@
+"""Running-merge forward (zl_attn_fwd_accumulate) vs the fp64 oracle.
+
+Ring accumulation: each call folds one key/value block of a query chunk into the running
+(O, LSE) at the chunk's rows. After the last block, in any order, the rows must hold
+attention over the whole key range, element by element within the usual tolerance; after
+the first block they must hold that block's own result. Covers d_head 64 and 128, blocks of
+one key and of ragged lengths, two ring groups folded in the same calls, and whole segments
+written in the same launch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_harness as H
+
+pytestmark = [pytest.mark.gpu, H.requires_gpu]
+
+SEQ_Q = (150, 77, 100)
+SEQ_KV = (333, 77, 300)
+HEADS = (3, 3, 2)
+BLOCKS0 = ((0, 1), (1, 64), (64, 200), (200, 333))  # sequence 0: queries [0,150), 3 heads
+BLOCKS2 = ((0, 150), (150, 300))                    # sequence 2: queries [20,100), 2 heads
+WHOLE1 = (1, 0, 3, 0, 77, 0, 77, -1)
+
+
+def _oracle(d, segs, ins):
+    q, k, v = (H.f64(ins[n]) for n in ("q", "k", "v"))
+    scale = 1.0 / np.sqrt(d)
+    return oracle.pack_forward(SEQ_Q, SEQ_KV, HEADS, segs, d, scale, q, k, v)
+
+
+def _rows(lay, s, q0, q1, h0, h1):
+    return np.concatenate([lay.q_index(s, q0, q1, h) for h in range(h0, h1)])
+
+
+@pytest.mark.parametrize("d,order", [(64, (2, 0, 3, 1)), (128, (0, 1, 2, 3)), (128, (3, 2, 1, 0))])
+def test_ring_blocks_folded_one_call_at_a_time(d, order):
+    z = H.zl()
+    dev = torch.device("cuda:0")
+    pack = W.Pack(f"acc{d}", SEQ_Q, SEQ_KV, HEADS, (WHOLE1,), d, 31 + d)
+    ins = W.draw(pack)
+    q, k, v = (ins[n].to(dev) for n in ("q", "k", "v"))
+    lay = oracle.PackLayout(SEQ_Q, SEQ_KV, HEADS)
+    rows0 = _rows(lay, 0, 0, 150, 0, 3)
+    rows2 = _rows(lay, 2, 20, 100, 0, 2)
+    n_q = int(lay.q_off[-1])
+    o = torch.full((n_q, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((n_q,), float("nan"), dtype=torch.float32, device=dev)
+    lse[torch.as_tensor(np.concatenate([rows0, rows2]), device=dev)] = float("-inf")
+    print(f"[case] accumulate d={d} order={order}", flush=True)
+    for i, b in enumerate(order):
+        segs = [(0, 0, 3, 0, 150, BLOCKS0[b][0], BLOCKS0[b][1], 0)]
+        if i < len(BLOCKS2):
+            segs.append((2, 0, 2, 20, 100, BLOCKS2[i][0], BLOCKS2[i][1], 0))
+        if i == 0:
+            segs.append(WHOLE1)
+        plan = z.Plan(SEQ_Q, SEQ_KV, HEADS, tuple(segs), d)
+        z.attn_fwd_accumulate(plan, q, k, v, o, lse)
+        if i == 0:
+            torch.cuda.synchronize()
+            first = _oracle(d, [(0, 0, 3, 0, 150, BLOCKS0[b][0], BLOCKS0[b][1], -1)], ins)
+            H.assert_close("first block O", H.f64(o)[rows0], first["o"][rows0])
+            H.assert_close("first block LSE", H.f64(lse)[rows0], first["lse"][rows0])
+    torch.cuda.synchronize()
+    ref = _oracle(d, [(0, 0, 3, 0, 150, 0, 333, -1), WHOLE1, (2, 0, 2, 20, 100, 0, 300, -1)], ins)
+    go, gl = H.f64(o), H.f64(lse)
+    cov = ~np.isnan(ref["lse"])
+    assert cov.sum() == len(rows0) + len(rows2) + 77 * 3
+    H.assert_close("O", go[cov], ref["o"][cov])
+    H.assert_close("LSE", gl[cov], ref["lse"][cov])
+    assert np.isnan(go[~cov]).all() and np.isnan(gl[~cov]).all(), "rows no segment covers were written"
+
+
+def test_whole_segments_match_plain_forward_bit_for_bit():
+    """With no ring part in the plan the running-merge forward is the plain forward."""
+    z = H.zl()
+    dev = torch.device("cuda:0")
+    pack = W.tiny()
+    ins = W.draw(pack)
+    q, k, v = (ins[n].to(dev) for n in ("q", "k", "v"))
+    plan = H.make_plan(pack)
+    n_q = plan.info["q_rows"]
+    print("[case] accumulate vs plain forward, tiny pack", flush=True)
+    o1, l1, _, _ = z.attn_fwd(plan, q, k, v)
+    o2 = torch.zeros((n_q, pack.d), dtype=torch.float32, device=dev)
+    l2 = torch.zeros((n_q,), dtype=torch.float32, device=dev)
+    z.attn_fwd_accumulate(plan, q, k, v, o2, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -224,3 +224,15 @@ def test_scale_override():
     pack = W.tiny()
     p = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, 0.3, host_only=True)
     assert abs(p.info["softmax_scale"] - 0.3) < 1e-7
+
+
+def test_accumulate_rejects_two_parts_of_one_group():
+    lib = z.lib()
+    seg = ((0, 0, 2, 0, 40, 0, 30, 0), (0, 0, 2, 0, 40, 30, 70, 1))
+    p = z.Plan((40,), (70,), (2,), seg, 64, host_only=True)
+    assert lib.zl_attn_fwd_accumulate(p.handle, 16, 16, 16, 16, 16, 16, None) == ZL_ERR_INVALID
+    assert b"parts" in lib.zl_last_error()
+    one = z.Plan((40,), (70,), (2,), ((0, 0, 2, 0, 40, 30, 70, 0),), 64, host_only=True)
+    assert lib.zl_attn_fwd_accumulate(one.handle, 16, 16, 16, 16, 16, 16, None) == ZL_ERR_INVALID
+    assert b"host-only" in lib.zl_last_error()
+    assert lib.zl_attn_fwd_accumulate(None, 16, 16, 16, 16, 16, 16, None) == ZL_ERR_INVALID
