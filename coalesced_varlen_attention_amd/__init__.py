@@ -48,7 +48,9 @@ class _PlanInfo(ctypes.Structure):
 
 class _GroupInfo(ctypes.Structure):
     _fields_ = [("n_parts", ctypes.c_int32), ("seq", ctypes.c_int32), ("n_rows", ctypes.c_int64),
-                ("o_row", ctypes.c_int64), ("part_row", ctypes.c_int64)]
+                ("o_row", ctypes.c_int64), ("part_row", ctypes.c_int64), ("head_begin", ctypes.c_int32),
+                ("head_end", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("q_begin", ctypes.c_int32),
+                ("q_end", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -67,6 +69,7 @@ def _load() -> ctypes.CDLL:
         "zl_attn_fwd": (I32, [P, P, P, P, P, P, P, P, P, P]),
         "zl_attn_fwd_accumulate": (I32, [P, P, P, P, P, P, P, P]),
         "zl_lse_merge": (I32, [I32, I64, I32, P, P, P, P, P]),
+        "zl_plan_merge": (I32, [P, P, P, P, P, P]),
         "zl_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, P]),
         "zl_attn_bwd_stages": (I32, [P, P, P, P, P, P, P, P, P, P, P, U32, P]),
         "zl_last_error": (ctypes.c_char_p, []),
@@ -257,12 +260,19 @@ def lse_merge(n_parts: int, n_rows: int, d: int, o_part, lse_part, o, lse, strea
 
 
 def merge_groups(plan: Plan, o_part, lse_part, o, lse, stream=None) -> None:
-    """Merge every ring group of ``plan`` into its final rows of ``o`` and ``lse``."""
-    d = plan.d
-    for g in plan.groups:
-        r0, n, p0, np_ = g["o_row"], g["n_rows"], g["part_row"], g["n_parts"]
-        lse_merge(np_, n, d, o_part[p0:p0 + np_ * n], lse_part[p0:p0 + np_ * n], o[r0:r0 + n], lse[r0:r0 + n],
-                  stream)
+    """Merge every ring group of ``plan`` into its rows of ``o`` and ``lse`` (``zl_plan_merge``,
+    one launch; head-subset groups land at their strided rows)."""
+    import torch
+    info, d = plan.info, plan.d
+    if info["n_groups"] == 0:
+        return
+    dev = o.device
+    _check_tensor(o_part, "o_part", torch.float32, info["part_rows"], d, dev)
+    _check_tensor(lse_part, "lse_part", torch.float32, info["part_rows"], 1, dev)
+    _check_tensor(o, "o", torch.float32, info["q_rows"], d, dev)
+    _check_tensor(lse, "lse", torch.float32, info["q_rows"], 1, dev)
+    _check(lib().zl_plan_merge(plan.handle, o_part.data_ptr(), lse_part.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               _stream_handle(stream)))
 
 
 def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None, stream=None,

@@ -197,6 +197,20 @@ extern "C" zl_status zl_lse_merge(int32_t n_parts, int64_t n_rows, int32_t d_hea
                        "zl_lse_merge");
 }
 
+extern "C" zl_status zl_plan_merge(const zl_plan* plan, const float* o_part, const float* lse_part, float* o,
+                                   float* lse, void* stream) {
+  zl_status st = check_runnable(plan, "zl_plan_merge");
+  if (st != ZL_OK) return st;
+  if (plan->groups.empty()) return ZL_OK;
+  if (!o_part || !lse_part || !o || !lse) return fail(ZL_ERR_INVALID, "zl_plan_merge: NULL pointer");
+  if (!aligned(o_part, 16) || !aligned(o, 16) || !aligned(lse_part, 4) || !aligned(lse, 4))
+    return fail(ZL_ERR_INVALID, "zl_plan_merge: o_part and o must be 16-byte aligned, lse 4-byte");
+  const int grid = (int)std::min<int64_t>(plan->merge_blocks, (int64_t)plan->n_cu * 16);
+  return launch_status(zl::launch_plan_merge(plan->d, plan->d_groups, (int32_t)plan->gdev.size(), plan->merge_blocks,
+                                             o_part, lse_part, o, lse, grid, stream),
+                       "zl_plan_merge");
+}
+
 extern "C" zl_status zl_attn_bwd(const zl_plan* plan, const void* q, const void* k, const void* v, const float* o,
                                  const float* lse, const void* d_o, float* dq, float* dk, float* dv, void* workspace,
                                  void* stream) {

@@ -515,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
         orow = p.o + lrow * D;
         lse_out = p.lse;
       } else {
-        lrow = sg.part_row0 + (int64_t)(qtok - sg.q_begin) * nh + h;
+        lrow = sg.part_row0 + (int64_t)(qtok - sg.q_begin) * (sg.head_end - sg.head_begin) + (h - sg.head_begin);
         orow = p.o_part + lrow * D;
         lse_out = p.lse_part;
       }

@@ -28,7 +28,7 @@ constexpr int kCounterStride = 16;  // ints between queue counters (64 bytes)
 struct alignas(16) SegDev {
   int64_t q_row0;     // query-side row of (token 0, head 0) of the segment's sequence
   int64_t kv_row0;    // key-side row of (token 0, head 0)
-  int64_t part_row0;  // slab row of (token q_begin, head 0) for a ring part, else -1
+  int64_t part_row0;  // slab row of (token q_begin, head head_begin) for a ring part, else -1
   int32_t nh;         // stored heads of the sequence (row stride between tokens = nh rows)
   int32_t q_begin, q_end, kv_begin, kv_end;
   int32_t head_begin, head_end;
@@ -39,6 +39,23 @@ struct alignas(16) SegDev {
   int32_t pad[3];
 };
 static_assert(sizeof(SegDev) == 80, "SegDev must stay 80 bytes");
+
+// A KV-split group as the merge kernel sees it: its slab rows (token-major over its head
+// subset) and where each lands in O/LSE.
+struct alignas(16) GroupDev {
+  int64_t part_row;  // slab row of part 0, row 0
+  int64_t o_row;     // O/LSE row of (token q_begin, head head_begin)
+  int64_t n_rows;    // tokens x n_sub
+  int64_t block0;    // first merge block of the group (blocks of merge_rows(d) rows)
+  int32_t n_parts;
+  int32_t nh;        // stored heads of the sequence: O/LSE rows between consecutive tokens
+  int32_t n_sub;     // heads in the group
+  int32_t pad;
+};
+static_assert(sizeof(GroupDev) == 48, "GroupDev must stay 48 bytes");
+
+// Rows one merge workgroup (256 lanes, d/4 lanes per row) handles per pass.
+constexpr int merge_rows(int d) { return 256 / (d / 4); }
 
 // One work item: segment index, head, first row (token) of the block, rows in the block.
 struct alignas(16) Tile {
@@ -92,6 +109,8 @@ struct BwdParams {
 // Kernel launchers (defined next to their kernels). They return the launch status.
 int launch_fwd(int d, const FwdParams& p, int grid, void* stream);
 int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages, void* stream);
+int launch_plan_merge(int d, const GroupDev* groups, int32_t n_groups, int64_t n_blocks, const float* o_part,
+                      const float* lse_part, float* o, float* lse, int grid, void* stream);
 int launch_merge(int d, int32_t n_parts, int64_t n_rows, const float* o_part, const float* lse_part,
                  float* o, float* lse, int grid, void* stream);
 // Workgroups of each persistent kernel that fit on one compute unit.
@@ -118,6 +137,8 @@ struct zl_plan {
   std::vector<int32_t> fwd_bounds, bwd_bounds, dq_bounds;            // kQueues + 1 each
   std::vector<int32_t> kv_ranges;
   std::vector<zl_group_info_t> groups;
+  std::vector<zl::GroupDev> gdev;
+  int64_t merge_blocks = 0;  // total blocks of a plan merge launch
   // device copies (one allocation, carved into the three tables)
   void* dev_block = nullptr;
   const zl::SegDev* d_segs = nullptr;
@@ -127,4 +148,5 @@ struct zl_plan {
   const zl::Tile* d_dq = nullptr;
   const int32_t* d_ranges = nullptr;
   const int32_t* d_bounds = nullptr;  // fwd, bwd, dq bounds, kQueues + 1 each
+  const zl::GroupDev* d_groups = nullptr;
 };

@@ -192,10 +192,6 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   const int n_groups = (int)group_members.size();
   for (int gid = 0; gid < n_groups; ++gid) {
     auto& mem = group_members[gid];
-    const zl_segment& f = segs[mem[0]];
-    if (f.head_begin != 0 || f.head_end != seq_heads[f.seq])
-      return fail(ZL_ERR_INVALID, "zl_plan_build: " + seg_str(mem[0], f) +
-                                      ": a ring group must cover every stored head of its sequence");
     std::vector<int> seen(mem.size(), -1);
     for (int i : mem) {
       const int p = segs[i].part;
@@ -245,12 +241,32 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     zl_group_info_t& gi = plan->groups[gid];
     gi.n_parts = (int32_t)group_members[gid].size();
     gi.seq = f.seq;
-    gi.n_rows = (int64_t)(f.q_end - f.q_begin) * seq_heads[f.seq];
-    gi.o_row = qoff[f.seq] + (int64_t)f.q_begin * seq_heads[f.seq];
+    gi.n_rows = (int64_t)(f.q_end - f.q_begin) * (f.head_end - f.head_begin);
+    gi.o_row = qoff[f.seq] + (int64_t)f.q_begin * seq_heads[f.seq] + f.head_begin;
     gi.part_row = slab;
+    gi.head_begin = f.head_begin;
+    gi.head_end = f.head_end;
+    gi.n_heads = seq_heads[f.seq];
+    gi.q_begin = f.q_begin;
+    gi.q_end = f.q_end;
     slab += gi.n_rows * gi.n_parts;
   }
   plan->part_rows = slab;
+  plan->gdev.resize(n_groups);
+  for (int gid = 0; gid < n_groups; ++gid) {
+    const zl_group_info_t& gi = plan->groups[gid];
+    zl::GroupDev& gd = plan->gdev[gid];
+    gd.part_row = gi.part_row;
+    gd.o_row = gi.o_row;
+    gd.n_rows = gi.n_rows;
+    gd.block0 = plan->merge_blocks;
+    gd.n_parts = gi.n_parts;
+    gd.nh = gi.n_heads;
+    gd.n_sub = gi.head_end - gi.head_begin;
+    gd.pad = 0;
+    const int rows = zl::merge_rows(d_head);
+    plan->merge_blocks += (gi.n_rows + rows - 1) / rows;
+  }
 
   // Device segment table.
   plan->segs.resize(n_seg);
@@ -354,7 +370,8 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     const size_t b_dq = align(plan->dq_tiles.size() * sizeof(zl::Tile));
     const size_t b_rng = align(plan->kv_ranges.size() * sizeof(int32_t));
     const size_t b_bnd = align(3 * (zl::kQueues + 1) * sizeof(int32_t));
-    const size_t total = b_segs + b_fwd + b_bwd + b_pre + b_dq + b_rng + b_bnd;
+    const size_t b_grp = align(plan->gdev.size() * sizeof(zl::GroupDev));
+    const size_t total = b_segs + b_fwd + b_bwd + b_pre + b_dq + b_rng + b_bnd + b_grp;
     if (hipMalloc(&plan->dev_block, total) != hipSuccess) {
       plan->dev_block = nullptr;
       (void)hipGetLastError();
@@ -374,6 +391,7 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     plan->d_dq = (const zl::Tile*)carve(b_dq);
     plan->d_ranges = (const int32_t*)carve(b_rng);
     plan->d_bounds = (const int32_t*)carve(b_bnd);
+    plan->d_groups = (const zl::GroupDev*)carve(b_grp);
     hipError_t e = hipSuccess;
     auto up = [&](const void* dst, const void* src, size_t bytes) {
       if (e == hipSuccess && bytes) e = hipMemcpy((void*)dst, src, bytes, hipMemcpyHostToDevice);
@@ -388,6 +406,7 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     for (const auto* b : {&plan->fwd_bounds, &plan->bwd_bounds, &plan->dq_bounds})
       all_bounds.insert(all_bounds.end(), b->begin(), b->end());
     up(plan->d_bounds, all_bounds.data(), all_bounds.size() * sizeof(int32_t));
+    up(plan->d_groups, plan->gdev.data(), plan->gdev.size() * sizeof(zl::GroupDev));
     if (e != hipSuccess) {
       (void)hipFree(plan->dev_block);
       plan->dev_block = nullptr;

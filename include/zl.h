@@ -52,10 +52,12 @@ typedef struct zl_plan zl_plan; /* opaque; immutable after zl_plan_build, safe t
  *   for every stored head h in [head_begin, head_end).
  * part == -1: the result is final and is written to O/LSE at the query rows.
  * part >= 0: the segment is ring part `part` of a KV-split group. A group is the set of
- *   segments with equal (seq, q range, head range); its parts must be numbered 0..n-1, have
- *   disjoint key ranges, and cover every stored head of the sequence. Each part writes a
- *   normalised partial O and its LSE to the partial slab (see zl_plan_group); the exact
- *   merge is zl_lse_merge (ring attention accumulates the output block by block, §II-B).
+ *   segments with equal (seq, q range, head range); its parts must be numbered 0..n-1 and
+ *   have disjoint key ranges. The head range may be a subset of the stored heads: a
+ *   composed placement, Ulysses over heads and ring over keys (§IV-A, Table II). Each part
+ *   writes a normalised partial O and its LSE to the partial slab (see zl_plan_group); the
+ *   exact merge is zl_plan_merge (ring attention accumulates the output block by block,
+ *   §II-B), or zl_attn_fwd_accumulate folds each part in as it runs.
  * No two segments may write the same O rows, and no two may own the same K/V rows (their
  * dK/dV would collide) unless they are parts of one group, whose key ranges are disjoint.
  */
@@ -84,12 +86,24 @@ typedef struct {
   int64_t dq_tiles;       /* work items of the backward dQ queue */
 } zl_plan_info_t;
 
+/*
+ * A KV-split (ring) group: the segments that share a sequence, query range and head range
+ * and carry parts 0..n_parts-1. The group's rows are its (token, head) pairs, token-major:
+ * row r is token q_begin + r / n_sub and head head_begin + r % n_sub, with
+ * n_sub = head_end - head_begin. In O and LSE that pair lives at row
+ * o_row + (r / n_sub) * n_heads + r % n_sub; the rows are contiguous only when the group
+ * covers every stored head (n_sub == n_heads). In the partial slab, part b holds the group's
+ * rows contiguously from part_row + b * n_rows.
+ */
 typedef struct {
   int32_t n_parts;        /* parts in the group */
   int32_t seq;            /* its sequence */
-  int64_t n_rows;         /* rows of the group: (q_end-q_begin) * seq_heads[seq] */
-  int64_t o_row;          /* first row of the group in O and LSE (O elements start at o_row*d) */
+  int64_t n_rows;         /* rows of the group: (q_end-q_begin) * (head_end-head_begin) */
+  int64_t o_row;          /* O/LSE row of (token q_begin, head head_begin) */
   int64_t part_row;       /* first slab row of part 0; part b starts at part_row + b*n_rows */
+  int32_t head_begin, head_end;  /* the group's stored-head range */
+  int32_t n_heads;        /* stored heads of the sequence (O/LSE rows between tokens) */
+  int32_t q_begin, q_end; /* the group's query range */
 } zl_group_info_t;
 
 /* Flags for zl_plan_build. */
@@ -191,11 +205,25 @@ zl_status zl_attn_fwd_accumulate(const zl_plan* plan, const void* q, const void*
  * LSE = -inf.
  *   o_part  fp32 [n_parts][n_rows][d_head]     lse_part  fp32 [n_parts][n_rows]
  *   o       fp32 [n_rows][d_head] (output)     lse       fp32 [n_rows] (output)
- * For a plan's group g, pass o_part + part_row*d, lse_part + part_row, o + o_row*d and
- * lse + o_row from zl_plan_group. d_head is 64 or 128; pointers 16-B aligned.
+ * For a plan's group g that covers every stored head (its O rows are then contiguous), pass
+ * o_part + part_row*d, lse_part + part_row, o + o_row*d and lse + o_row from zl_plan_group;
+ * zl_plan_merge does every group of a plan, head subsets included, in one launch.
+ * d_head is 64 or 128; pointers 16-B aligned.
  */
 zl_status zl_lse_merge(int32_t n_parts, int64_t n_rows, int32_t d_head,
                        const float* o_part, const float* lse_part, float* o, float* lse, void* stream);
+
+/*
+ * The merge of zl_lse_merge for every KV-split group of a plan, in one launch (§II-B ring
+ * accumulation): each group's slab rows are merged over its parts and written to its rows of
+ * o and lse, following the row map of zl_plan_group (head subsets land at their strided O
+ * rows). Rows outside the groups are left untouched.
+ *   o_part, lse_part   the slab zl_attn_fwd wrote (part_rows rows)
+ *   o, lse             fp32 [q_rows][d] and [q_rows]
+ * A plan with no group makes this a no-op. Pointers 16-B aligned (lse 4-B).
+ */
+zl_status zl_plan_merge(const zl_plan* plan, const float* o_part, const float* lse_part, float* o, float* lse,
+                        void* stream);
 
 /*
  * Backward (the exact backward of §V-A): gradients of f = sum over covered rows of

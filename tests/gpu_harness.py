@@ -104,12 +104,9 @@ def compare_full(pack: W.Pack, ins: dict, out: dict, ref: dict, scaled_max_abs: 
         assert_close(name, g[cov], r[cov], max_abs=bound)
         assert np.isnan(g[~cov]).all(), f"{name}: rows no segment covers were written"
     plan = out["plan"]
-    lay = oracle.PackLayout(pack.seq_q, pack.seq_kv, pack.heads)
     for g in plan.groups:
-        keys = {k for (k, _b) in ref["parts"]
-                if k[0] == g["seq"] and lay.q_off[k[0]] + k[1] * pack.heads[k[0]] == g["o_row"]}
-        assert len(keys) == 1, "ring group not found in the oracle's parts"
-        key = keys.pop()
+        key = (g["seq"], g["q_begin"], g["q_end"], g["head_begin"], g["head_end"])
+        assert (key, 0) in ref["parts"], "ring group not found in the oracle's parts"
         s, q0, q1, h0, h1 = key
         for b in range(g["n_parts"]):
             po, pl = ref["parts"][(key, b)]

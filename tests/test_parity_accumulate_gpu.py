@@ -89,3 +89,35 @@ def test_whole_segments_match_plain_forward_bit_for_bit():
     z.attn_fwd_accumulate(plan, q, k, v, o2, l2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_head_subset_group_folded(d):
+    """A ring group over heads [1,3) of 4: each fold lands at the subset's strided rows and
+    leaves the other heads' rows untouched."""
+    z = H.zl()
+    dev = torch.device("cuda:0")
+    seq_q, seq_kv, heads = (140,), (230,), (4,)
+    blocks = ((0, 64), (64, 65), (65, 230))
+    pack = W.Pack(f"acc_sub{d}", seq_q, seq_kv, heads, ((0, 1, 3, 0, 140, 0, 230, -1),), d, 41 + d)
+    ins = W.draw(pack)
+    q, k, v = (ins[n].to(dev) for n in ("q", "k", "v"))
+    lay = oracle.PackLayout(seq_q, seq_kv, heads)
+    rows = _rows(lay, 0, 0, 140, 1, 3)
+    n_q = int(lay.q_off[-1])
+    o = torch.full((n_q, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((n_q,), float("nan"), dtype=torch.float32, device=dev)
+    lse[torch.as_tensor(rows, device=dev)] = float("-inf")
+    print(f"[case] accumulate head subset d={d}", flush=True)
+    for b in (1, 2, 0):
+        plan = z.Plan(seq_q, seq_kv, heads, ((0, 1, 3, 0, 140, blocks[b][0], blocks[b][1], 0),), d)
+        z.attn_fwd_accumulate(plan, q, k, v, o, lse)
+    torch.cuda.synchronize()
+    qf, kf, vf = (H.f64(ins[n]) for n in ("q", "k", "v"))
+    ref = oracle.pack_forward(seq_q, seq_kv, heads, [(0, 1, 3, 0, 140, 0, 230, -1)], d, 1.0 / np.sqrt(d), qf, kf, vf)
+    go, gl = H.f64(o), H.f64(lse)
+    cov = ~np.isnan(ref["lse"])
+    assert cov.sum() == len(rows)
+    H.assert_close("O", go[cov], ref["o"][cov])
+    H.assert_close("LSE", gl[cov], ref["lse"][cov])
+    assert np.isnan(go[~cov]).all() and np.isnan(gl[~cov]).all(), "rows outside the head subset were written"

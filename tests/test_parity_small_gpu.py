@@ -2,7 +2,7 @@
 
 Covers: the tiny 3-sequence pack (d_head 64), ragged lengths around the tile sizes, head
 subsets (Ulysses shards), query ranges (all-gather shards), ring groups with uneven parts
-including a one-key part, peaked and drifting-max softmax inputs, and untouched rows.
+including a one-key part, ring groups over head subsets, peaked and drifting-max softmax inputs, and untouched rows.
 """
 import numpy as np
 import pytest
@@ -66,6 +66,18 @@ def test_two_ring_groups_and_whole():
            (1, 0, 2, 0, 156, 0, 100, 0), (1, 0, 2, 0, 156, 100, 300, 1),
            (2, 0, 2, 0, 90, 0, 90, -1))
     pack = W.Pack("two_rings", (100, 156, 90), (300, 300, 90), (2, 2, 2), seg, 64, 15)
+    _run(pack)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_head_subset_ring_groups(d):
+    """Composed placements (Ulysses heads x ring keys): groups over head subsets, merged in
+    one launch into strided O rows; rows of the subset heads outside the groups stay untouched."""
+    seg = ((0, 0, 2, 0, 200, 0, 100, 0), (0, 0, 2, 0, 200, 100, 260, 1),
+           (0, 2, 5, 0, 130, 0, 1, 0), (0, 2, 5, 0, 130, 1, 77, 1), (0, 2, 5, 0, 130, 77, 260, 2),
+           (0, 5, 6, 0, 200, 0, 260, -1),
+           (1, 1, 3, 5, 90, 0, 45, 1), (1, 1, 3, 5, 90, 45, 90, 0))
+    pack = W.Pack(f"head_subset_rings{d}", (200, 90), (260, 90), (6, 3), seg, d, 18)
     _run(pack)
 
 

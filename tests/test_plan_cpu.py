@@ -140,7 +140,8 @@ def test_ring_group_layout():
     p = host_plan(pack)
     assert p.info["n_groups"] == 1 and p.info["n_parts_max"] == 8
     g = p.groups[0]
-    assert g == {"n_parts": 8, "seq": 0, "n_rows": 9450 * 40, "o_row": 0, "part_row": 0}
+    assert g == {"n_parts": 8, "seq": 0, "n_rows": 9450 * 40, "o_row": 0, "part_row": 0, "head_begin": 0,
+                 "head_end": 40, "n_heads": 40, "q_begin": 0, "q_end": 9450}
     assert p.info["part_rows"] == 8 * 9450 * 40
 
 
@@ -170,8 +171,8 @@ def test_validation_errors():
     expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 4, 0, 8, -1), (0, 0, 2, 4, 8, 2, 5, -1)],
                  match="same K/V rows")
     # ring groups
-    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 1, 0, 8, 0, 4, 0), (0, 0, 1, 0, 8, 4, 8, 1)],
-                 match="every stored head")
+    expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 8, 0, 4, 0), (0, 1, 2, 0, 8, 4, 8, 0)],
+                 match="same output rows")
     expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 8, 0, 4, 0), (0, 0, 2, 0, 8, 4, 8, 0)],
                  match="numbered")
     expect_error(ZL_ERR_INVALID, [8], [8], [2], [(0, 0, 2, 0, 8, 0, 4, 0), (0, 0, 2, 0, 8, 4, 8, 2)],
@@ -236,3 +237,17 @@ def test_accumulate_rejects_two_parts_of_one_group():
     assert lib.zl_attn_fwd_accumulate(one.handle, 16, 16, 16, 16, 16, 16, None) == ZL_ERR_INVALID
     assert b"host-only" in lib.zl_last_error()
     assert lib.zl_attn_fwd_accumulate(None, 16, 16, 16, 16, 16, 16, None) == ZL_ERR_INVALID
+
+
+def test_head_subset_groups():
+    """Composed placements: ring groups over head subsets of one sequence (Ulysses x ring)."""
+    seg = ((0, 0, 2, 0, 10, 0, 5, 0), (0, 0, 2, 0, 10, 5, 9, 1),   # heads [0,2): 2 parts
+           (0, 2, 5, 3, 7, 0, 3, 1), (0, 2, 5, 3, 7, 3, 9, 0),     # heads [2,5), queries [3,7)
+           (1, 0, 5, 0, 6, 0, 6, -1))                              # a final segment beside them
+    p = z.Plan((10, 6), (9, 6), (5, 5), seg, 128, host_only=True)
+    g0, g1 = p.groups
+    assert g0["n_rows"] == 10 * 2 and g0["o_row"] == 0 and g0["part_row"] == 0 and g0["n_heads"] == 5
+    assert (g0["head_begin"], g0["head_end"]) == (0, 2)
+    assert g1["n_rows"] == 4 * 3 and g1["o_row"] == 3 * 5 + 2 and g1["part_row"] == 2 * 20
+    assert (g1["head_begin"], g1["head_end"], g1["q_begin"], g1["q_end"]) == (2, 5, 3, 7)
+    assert p.info["part_rows"] == 2 * 20 + 2 * 12
