@@ -8,7 +8,8 @@ region; nothing is allocated inside it.
 FLOPs follow the metric's convention: 4*Lq*Lkv*d per (segment, head) forward, 2.5x that
 backward. Prints one JSON line; with --json-out also writes it to a file.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixed] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixed] [--no-cpu-baseline] [--ring-fold]
+                    [--no-split]
 """
 from __future__ import annotations
 
@@ -32,6 +33,8 @@ WORKLOAD_TEXT = {
              "Ulysses shard of a 75600-token video; d_head 128, non-causal",
     "ring": "ring KV-split shard: 9450 queries vs 75600 keys in 8 parts + LSE merge, 40 heads, d_head 128",
     "long": "long-video share: 5 heads of a 497760-token sequence + 8 x 4096 tokens at 40 heads, d_head 128",
+    "shard": "Ulysses share of one 32760-token video: 5 of 40 heads at full length, d_head 128",
+    "head1": "one head of a 32760-token video at full length, d_head 128 (forward split over keys)",
 }
 
 
@@ -125,6 +128,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a 2 GiB device copy (counter scale)")
+    ap.add_argument("--no-split", action="store_true", help="build the plan without split-KV of forward items")
+    ap.add_argument("--ring-fold", action="store_true",
+                    help="forward ring groups block by block with the running merge (one launch per ring "
+                         "block, folding into O/LSE) instead of one launch plus the LSE merge")
     args = ap.parse_args()
     if args.calibrate_copy:
         return calibrate_copy()
@@ -144,7 +151,7 @@ def main() -> int:
     torch.cuda.set_device(dev)
     pack = W.config(args.config)
     t0 = time.perf_counter()
-    plan = zl.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale)
+    plan = zl.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale, split=not args.no_split)
     plan_ms = (time.perf_counter() - t0) * 1e3
     info = plan.info
     ins = W.draw(pack)
@@ -160,14 +167,39 @@ def main() -> int:
     ws_b = torch.empty(info["ws_bwd"], dtype=torch.uint8, device=dev)
     has_groups = info["n_groups"] > 0
     stream = torch.cuda.current_stream()
+    fold_plans = []
+    if args.ring_fold:
+        if not has_groups:
+            print(f"bench.py: --ring-fold needs a pack with ring groups ({args.config} has none)", file=sys.stderr)
+            return 2
+        # Ring step b sees only block b of every group (renumbered part 0); whole segments go
+        # with the first step.
+        n_steps = max(g["n_parts"] for g in plan.groups)
+        for b in range(n_steps):
+            segs = tuple(sg[:7] + (0,) for sg in pack.segments if sg[7] == b)
+            if b == 0:
+                segs += tuple(sg for sg in pack.segments if sg[7] < 0)
+            fold_plans.append(zl.Plan(pack.seq_q, pack.seq_kv, pack.heads, segs, pack.d, pack.scale,
+                                      split=not args.no_split))
+        ws_f = torch.empty(max(fp.info["ws_fwd"] for fp in fold_plans), dtype=torch.uint8, device=dev)
+    group_rows = [(g["o_row"], g["n_rows"]) for g in plan.groups]
+
+    def forward():
+        if fold_plans:
+            for r0, n in group_rows:
+                lse[r0:r0 + n].fill_(float("-inf"))
+            for fp in fold_plans:
+                zl.attn_fwd_accumulate(fp, q, k, v, o, lse, workspace=ws_f)
+        else:
+            zl.attn_fwd(plan, q, k, v, o=o, lse=lse, o_part=o_part if has_groups else None,
+                        lse_part=lse_part if has_groups else None, workspace=ws_f)
 
     def step(ev=None):
         rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
         rec(0)
-        zl.attn_fwd(plan, q, k, v, o=o, lse=lse, o_part=o_part if has_groups else None,
-                    lse_part=lse_part if has_groups else None, workspace=ws_f)
+        forward()
         rec(1)
-        if has_groups:
+        if has_groups and not fold_plans:
             zl.merge_groups(plan, o_part, lse_part, o, lse)
         rec(2)
         zl.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b, stages=zl.BWD_PRE)
@@ -222,7 +254,10 @@ def main() -> int:
                        "pct_of_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
                        "fwd_ms": round(fwd_ms, 3), "merge_ms": round(merge_ms, 3), "bwd_ms": round(bwd_ms, 3),
                        "bwd_pre_ms": round(pre_ms, 3), "bwd_dkdv_ms": round(dkdv_ms, 3), "bwd_dq_ms": round(dq_ms, 3),
-                       "plan_build_ms": round(plan_ms, 2), "parallelism": "none (1 GPU)"},
+                       "plan_build_ms": round(plan_ms, 2), "parallelism": "none (1 GPU)",
+                       "ring_forward": (f"running merge, {len(fold_plans)} launches" if fold_plans
+                                        else "partials + LSE merge" if has_groups else "none"),
+                       "split_kv": {"fwd_items_split": info["split_tiles"], "pieces": info["split_pieces"]}},
             "roofline": roof}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pack, ins)

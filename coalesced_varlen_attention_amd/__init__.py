@@ -22,6 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libzl.so")
 
 ZL_PLAN_HOST_ONLY = 1
+ZL_PLAN_NO_SPLIT = 2
 BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 SEGMENT_FIELDS = ("seq", "head_begin", "head_end", "q_begin", "q_end", "kv_begin", "kv_end", "part")
 
@@ -43,7 +44,8 @@ class _PlanInfo(ctypes.Structure):
                 ("kv_rows", ctypes.c_int64), ("part_rows", ctypes.c_int64), ("n_groups", ctypes.c_int32),
                 ("n_parts_max", ctypes.c_int32), ("fwd_tiles", ctypes.c_int64), ("bwd_tiles", ctypes.c_int64),
                 ("fwd_flops", ctypes.c_double), ("bwd_flops", ctypes.c_double), ("d_head", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("dq_tiles", ctypes.c_int64)]
+                ("softmax_scale", ctypes.c_float), ("dq_tiles", ctypes.c_int64), ("split_tiles", ctypes.c_int32),
+                ("split_pieces", ctypes.c_int32)]
 
 
 class _GroupInfo(ctypes.Structure):
@@ -119,7 +121,7 @@ class Plan:
     """
 
     def __init__(self, seq_q: Sequence[int], seq_kv: Sequence[int], heads: Sequence[int], segments, d: int,
-                 scale: Optional[float] = None, host_only: bool = False):
+                 scale: Optional[float] = None, host_only: bool = False, split: bool = True):
         n = len(seq_q)
         if len(seq_kv) != n or len(heads) != n:
             raise ValueError("seq_q, seq_kv and heads must have the same length")
@@ -134,7 +136,7 @@ class Plan:
             for name, val in zip(SEGMENT_FIELDS, s):
                 setattr(segs[i], name, int(val))
         self._h = ctypes.c_void_p()
-        flags = ZL_PLAN_HOST_ONLY if host_only else 0
+        flags = (ZL_PLAN_HOST_ONLY if host_only else 0) | (0 if split else ZL_PLAN_NO_SPLIT)
         _check(lib().zl_plan_build(n, ctypes.cast(cu_q, ctypes.c_void_p), ctypes.cast(cu_kv, ctypes.c_void_p),
                                   ctypes.cast(hs, ctypes.c_void_p), len(segments), ctypes.cast(segs, ctypes.c_void_p),
                                   int(d), float(scale) if scale else 0.0, flags, ctypes.byref(self._h)))
@@ -152,13 +154,15 @@ class Plan:
     def handle(self) -> ctypes.c_void_p:
         return self._h
 
-    def tiles(self, which: int) -> List[Tuple[int, int, int, int]]:
-        """Work queue items (segment, head, first row, rows): 0 forward, 1 backward dK/dV, 2 backward dQ."""
+    def tiles(self, which: int) -> List[Tuple[int, ...]]:
+        """Work queue items (segment, head, first row, rows): 0 forward, 1 backward dK/dV, 2 backward dQ;
+        3 forward with (key begin, key end, split slot, piece | pieces << 16) appended."""
+        w = 8 if which == 3 else 4
         cnt = ctypes.c_int64()
         _check(lib().zl_plan_tiles(self._h, which, None, 0, ctypes.byref(cnt)))
-        buf = (ctypes.c_int32 * (4 * cnt.value))()
+        buf = (ctypes.c_int32 * (w * cnt.value))()
         _check(lib().zl_plan_tiles(self._h, which, ctypes.cast(buf, ctypes.c_void_p), cnt.value, ctypes.byref(cnt)))
-        return [tuple(buf[4 * i:4 * i + 4]) for i in range(cnt.value)]
+        return [tuple(buf[w * i:w * i + w]) for i in range(cnt.value)]
 
     def queues(self, which: int) -> List[int]:
         """Queue boundaries of a work list: items bounds[k]:bounds[k+1] of tiles(which) form queue k."""

@@ -30,6 +30,27 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // kCounterStride ints apart.
 constexpr size_t kCounterBytes = 2 * zl::kQueues * zl::kCounterStride * sizeof(int32_t);
 
+// Forward workspace after the queue counters, for split items: one counter per piece slot,
+// then each piece's normalised O rows and LSEs.
+size_t split_bytes(const zl_plan* plan) {
+  const size_t n = (size_t)plan->split_pieces;
+  if (n == 0) return 0;
+  return align256(n * sizeof(int32_t)) + align256(n * zl::kFwdRows * plan->d * sizeof(float)) +
+         align256(n * zl::kFwdRows * sizeof(float));
+}
+
+void set_split(const zl_plan* plan, void* workspace, zl::FwdParams* p) {
+  const size_t n = (size_t)plan->split_pieces;
+  p->n_split = (int32_t)n;
+  if (n == 0) return;
+  char* base = (char*)workspace + kCounterBytes;
+  p->split_cnt = (int32_t*)base;
+  base += align256(n * sizeof(int32_t));
+  p->split_o = (float*)base;
+  base += align256(n * zl::kFwdRows * plan->d * sizeof(float));
+  p->split_lse = (float*)base;
+}
+
 zl_status check_runnable(const zl_plan* plan, const char* who) {
   if (!plan) return fail(ZL_ERR_INVALID, std::string(who) + ": plan is NULL");
   if (!plan->dev_block) return fail(ZL_ERR_INVALID, std::string(who) + ": plan was built host-only and cannot run");
@@ -62,7 +83,7 @@ extern "C" const char* zl_last_error(void) { return zl::g_last_error.c_str(); }
 extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   if (!plan || !info) return fail(ZL_ERR_INVALID, "zl_plan_info: NULL argument");
   std::memset(info, 0, sizeof(*info));
-  info->ws_fwd = kCounterBytes;
+  info->ws_fwd = kCounterBytes + split_bytes(plan);
   info->ws_bwd = kCounterBytes + 2 * align256((size_t)plan->q_rows * sizeof(float));
   info->q_rows = plan->q_rows;
   info->kv_rows = plan->kv_rows;
@@ -76,6 +97,8 @@ extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   info->dq_tiles = (int64_t)plan->dq_tiles.size();
   info->d_head = plan->d;
   info->softmax_scale = plan->scale;
+  info->split_tiles = plan->split_tiles;
+  info->split_pieces = plan->split_pieces;
   return ZL_OK;
 }
 
@@ -89,17 +112,24 @@ extern "C" zl_status zl_plan_group(const zl_plan* plan, int32_t g, zl_group_info
 
 extern "C" zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* out, int64_t cap, int64_t* count) {
   if (!plan || !count) return fail(ZL_ERR_INVALID, "zl_plan_tiles: NULL argument");
-  if (which < 0 || which > 2) return fail(ZL_ERR_INVALID, "zl_plan_tiles: which must be 0, 1 or 2");
-  const auto& v = which == 0 ? plan->fwd_tiles : which == 1 ? plan->bwd_tiles : plan->dq_tiles;
+  if (which < 0 || which > 3) return fail(ZL_ERR_INVALID, "zl_plan_tiles: which must be 0, 1, 2 or 3");
+  const auto& v = which == 0 || which == 3 ? plan->fwd_tiles : which == 1 ? plan->bwd_tiles : plan->dq_tiles;
+  const int w = which == 3 ? 8 : 4;
   *count = (int64_t)v.size();
   if (cap < 0) return fail(ZL_ERR_INVALID, "zl_plan_tiles: negative capacity");
   if (cap > 0 && !out) return fail(ZL_ERR_INVALID, "zl_plan_tiles: out is NULL");
   const int64_t n = std::min<int64_t>(cap, (int64_t)v.size());
   for (int64_t i = 0; i < n; ++i) {
-    out[4 * i + 0] = v[i].seg;
-    out[4 * i + 1] = v[i].head;
-    out[4 * i + 2] = v[i].row0;
-    out[4 * i + 3] = v[i].nrows;
+    out[w * i + 0] = v[i].seg;
+    out[w * i + 1] = v[i].head;
+    out[w * i + 2] = v[i].row0;
+    out[w * i + 3] = v[i].nrows;
+    if (w == 8) {
+      out[w * i + 4] = v[i].kv_begin;
+      out[w * i + 5] = v[i].kv_end;
+      out[w * i + 6] = v[i].split;
+      out[w * i + 7] = v[i].piece;
+    }
   }
   return ZL_OK;
 }
@@ -138,6 +168,7 @@ extern "C" zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void*
   p.segs = plan->d_segs;
   p.queue = {plan->d_fwd, plan->d_bounds, (int32_t*)workspace};
   p.scale_log2 = plan->scale * 1.4426950408889634f;
+  set_split(plan, workspace, &p);
   const int per_cu = zl::fwd_blocks_per_cu(plan->d);
   if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_fwd: forward kernel cannot be resident");
   const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, (int64_t)plan->fwd_tiles.size());
@@ -170,6 +201,7 @@ extern "C" zl_status zl_attn_fwd_accumulate(const zl_plan* plan, const void* q, 
   p.queue = {plan->d_fwd, plan->d_bounds, (int32_t*)workspace};
   p.scale_log2 = plan->scale * 1.4426950408889634f;
   p.accumulate = 1;
+  set_split(plan, workspace, &p);
   const int per_cu = zl::fwd_blocks_per_cu(plan->d);
   if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_fwd_accumulate: forward kernel cannot be resident");
   const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, (int64_t)plan->fwd_tiles.size());

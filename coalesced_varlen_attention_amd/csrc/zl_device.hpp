@@ -93,10 +93,66 @@ __device__ __forceinline__ int lds_row(int r) { return (r & ~15) | ((r & 3) << 2
 // that publishes the buffer.
 __device__ __forceinline__ void lds_dma16(uint32_t lds_base, const char* base, uint32_t off) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+  // An LDS DMA right after a SALU write of M0 needs one wait state (s_nop 0).
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory");
 }
 
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Device-coherent 16-byte store and loads (sc1: written through to, and read from, the point
+// of coherence of all XCDs, past the per-XCD L2 and per-CU L1). For data one workgroup hands
+// to another within a launch without fences, which would write back and invalidate a whole
+// L2. The stores are complete once vmcnt reaches 0 (store_dev_wait). A store of more than
+// 8 bytes reads its data registers after issue, and the compiler does not see inside inline
+// assembly to keep the next write of those registers away: the s_nop after the store gives
+// the required wait states.
+__device__ __forceinline__ void store_dev16(float* p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 4" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_dev_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Eight device-coherent 16-byte loads at p + 8 k floats (k < 8), one wait for all.
+__device__ __forceinline__ void load_dev16x8(const float* p, f32x4 (&x)[8]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %8, off sc1\n\t"
+      "global_load_dwordx4 %1, %8, off offset:32 sc1\n\t"
+      "global_load_dwordx4 %2, %8, off offset:64 sc1\n\t"
+      "global_load_dwordx4 %3, %8, off offset:96 sc1\n\t"
+      "global_load_dwordx4 %4, %8, off offset:128 sc1\n\t"
+      "global_load_dwordx4 %5, %8, off offset:160 sc1\n\t"
+      "global_load_dwordx4 %6, %8, off offset:192 sc1\n\t"
+      "global_load_dwordx4 %7, %8, off offset:224 sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+      : "v"(p)
+      : "memory");
+}
+// Sixteen device-coherent 16-byte loads at p + 8 k floats (k < 16), one wait for all.
+__device__ __forceinline__ void load_dev16x16(const float* p, f32x4 (&x)[16]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %16, off sc1\n\t"
+      "global_load_dwordx4 %1, %16, off offset:32 sc1\n\t"
+      "global_load_dwordx4 %2, %16, off offset:64 sc1\n\t"
+      "global_load_dwordx4 %3, %16, off offset:96 sc1\n\t"
+      "global_load_dwordx4 %4, %16, off offset:128 sc1\n\t"
+      "global_load_dwordx4 %5, %16, off offset:160 sc1\n\t"
+      "global_load_dwordx4 %6, %16, off offset:192 sc1\n\t"
+      "global_load_dwordx4 %7, %16, off offset:224 sc1\n\t"
+      "global_load_dwordx4 %8, %16, off offset:256 sc1\n\t"
+      "global_load_dwordx4 %9, %16, off offset:288 sc1\n\t"
+      "global_load_dwordx4 %10, %16, off offset:320 sc1\n\t"
+      "global_load_dwordx4 %11, %16, off offset:352 sc1\n\t"
+      "global_load_dwordx4 %12, %16, off offset:384 sc1\n\t"
+      "global_load_dwordx4 %13, %16, off offset:416 sc1\n\t"
+      "global_load_dwordx4 %14, %16, off offset:448 sc1\n\t"
+      "global_load_dwordx4 %15, %16, off offset:480 sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
+        "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]),
+        "=&v"(x[15])
+      : "v"(p)
+      : "memory");
+}
 
 // Next work item for a workgroup (called by one thread): its own XCD's queue first, then the
 // others in order. `drained` counts the queues found empty and only grows, so every

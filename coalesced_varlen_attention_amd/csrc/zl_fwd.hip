@@ -7,6 +7,11 @@
 // writes either the final O and LSE at the query rows or, for a ring part, the normalised
 // partial O and its LSE to the partial slab (§II-B ring accumulation).
 //
+// Split items: an item may cover only a piece of its segment's keys. Its normalised partial
+// goes to the workspace through device-coherent stores; the last piece to finish (a
+// device-scope counter) merges the pieces by their log-sum-exps, read back with
+// device-coherent loads, and stores the item's result as an unsplit item would.
+//
 // Shape of one workgroup: 4 waves x 32 query rows. Each wave keeps its 32 query rows in
 // registers as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so every lane owns
 // one query row of the score tile: the running max and sum are per-lane values that only
@@ -132,7 +137,12 @@ __device__ __forceinline__ void dma_v(const FwdCtx<D>& cx, uint32_t v_lds, int b
   }
 }
 
-__global__ void zero_counters_kernel(int32_t* counters) { counters[threadIdx.x * kCounterStride] = 0; }
+// Clears the queue counters and the split-item counters before a launch.
+__global__ __launch_bounds__(256) void zero_counters_kernel(int32_t* counters, int32_t* split_cnt, int32_t n_split) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < kQueues) counters[i * kCounterStride] = 0;
+  for (int j = i; j < n_split; j += gridDim.x * 256) split_cnt[j] = 0;
+}
 
 // S^T[key][q] of one block: kKb tiles of 32 keys, each a chain of k-steps over d.
 template <int D>
@@ -405,6 +415,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   const uint32_t v_lds0 = lds0, v_lds1 = lds0 + C::kVBytes;
   const uint32_t k_lds0 = lds0 + 2 * C::kVBytes, k_lds1 = k_lds0 + C::kKBytes;
   __shared__ int32_t s_item;
+  __shared__ int32_t s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -448,10 +459,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
     cx.koff_dma = (uint32_t)(wave * C::kGroupRows + cx.dma_krow) * cx.row_bytes + cx.dma_kcol;
     cx.voff_dma = (uint32_t)cx.dma_vrow * cx.row_bytes + cx.dma_vcol;
     cx.k_dma_step = (int64_t)4 * C::kGroupRows * cx.rs * 2;
-    cx.n_kv = sg.kv_end - sg.kv_begin;
+    cx.n_kv = tile.kv_end - tile.kv_begin;  // the segment's keys, or one piece of them
     cx.n_blk = (cx.n_kv + C::kBk - 1) / C::kBk;
-    cx.kbase = (const bf16*)p.k + (sg.kv_row0 + (int64_t)sg.kv_begin * nh + h) * D;
-    cx.vbase = (const bf16*)p.v + (sg.kv_row0 + (int64_t)sg.kv_begin * nh + h) * D;
+    cx.kbase = (const bf16*)p.k + (sg.kv_row0 + (int64_t)tile.kv_begin * nh + h) * D;
+    cx.vbase = (const bf16*)p.v + (sg.kv_row0 + (int64_t)tile.kv_begin * nh + h) * D;
     const int n = cx.n_blk;
 
     // Prologue: K(0), K(1) into LDS; this lane's query row into registers (clamped to the
@@ -503,9 +514,67 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
     //   LSE' = M + ln(e^{LSE - M} + e^{LSE_b - M}),  O' = e^{LSE - LSE'} O + e^{LSE_b - LSE'} O_b.
     // Rows whose running LSE is -inf take the part as it is (their O is not read).
     const float l_tot = half_sum(st.l_run);
-    if (q_valid) {
-      const float inv = 1.0f / l_tot;
-      const float lse_b = 0.69314718055994531f * (st.m_run + __log2f(l_tot));
+    float o_scale = 1.0f / l_tot;
+    float lse_b = 0.69314718055994531f * (st.m_run + __log2f(l_tot));
+    bool store = true;
+    if (tile.split >= 0) {
+      // One key piece of a split item: publish the normalised partial (device-coherent
+      // stores), then count the pieces done; the last piece merges all of them (the same
+      // exact merge) and stores the item's result. No fence: the partials bypass the
+      // per-XCD caches, and each count is issued after this workgroup's stores completed.
+      const int n_pieces = tile.piece >> 16;
+      const int64_t slot = tile.split + (tile.piece & 0xffff);
+      if (q_valid) {
+        float* so = p.split_o + (slot * kFwdRows + qi) * D;
+#pragma unroll
+        for (int cb = 0; cb < C::kCb; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 val = {st.oacc[cb][4 * g] * o_scale, st.oacc[cb][4 * g + 1] * o_scale,
+                               st.oacc[cb][4 * g + 2] * o_scale, st.oacc[cb][4 * g + 3] * o_scale};
+            store_dev16(so + cb * 32 + 8 * g + 4 * hi, val);
+          }
+        if (hi == 0)
+          __hip_atomic_store(p.split_lse + slot * kFwdRows + qi, lse_b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      store_dev_wait();
+      __syncthreads();
+      if (tid == 0)
+        s_last = __hip_atomic_fetch_add(p.split_cnt + tile.split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 n_pieces - 1;
+      __syncthreads();
+      store = s_last;
+      if (store && q_valid) {
+        const float* sl = p.split_lse + (int64_t)tile.split * kFwdRows + qi;
+        float m = -INFINITY;
+        for (int c = 0; c < n_pieces; ++c)
+          m = fmaxf(m, __hip_atomic_load(sl + c * kFwdRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        float tot = 0.f;
+        for (int c = 0; c < n_pieces; ++c)
+          tot += expf(__hip_atomic_load(sl + c * kFwdRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - m);
+        lse_b = m + logf(tot);
+#pragma unroll
+        for (int cb = 0; cb < C::kCb; ++cb) st.oacc[cb] = f32x16{};
+        for (int c = 0; c < n_pieces; ++c) {
+          const float w =
+              expf(__hip_atomic_load(sl + c * kFwdRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - lse_b);
+          const float* so = p.split_o + (((int64_t)tile.split + c) * kFwdRows + qi) * D + 4 * hi;
+          // this lane's D/2 values of the row: D/8 chunks of 16 bytes, 8 floats apart; chunk k
+          // holds (column block k/4, group k%4)
+          f32x4 x[D / 8];
+          if constexpr (D == 128)
+            load_dev16x16(so, x);
+          else
+            load_dev16x8(so, x);
+#pragma unroll
+          for (int k = 0; k < D / 8; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st.oacc[k / 4][4 * (k % 4) + e] += w * x[k][e];
+        }
+        o_scale = 1.0f;
+      }
+    }
+    if (store && q_valid) {
       const bool fold = sg.part >= 0 && p.accumulate;
       float* orow;
       int64_t lrow;
@@ -519,14 +588,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
         orow = p.o_part + lrow * D;
         lse_out = p.lse_part;
       }
-      float w_old = 0.f, w_new = inv, lse_new = lse_b;
+      float w_old = 0.f, w_new = o_scale, lse_new = lse_b;
       if (fold) {
         const float lse_a = lse_out[lrow];
         if (lse_a != -INFINITY) {
           const float mx = fmaxf(lse_a, lse_b);
           lse_new = mx + logf(expf(lse_a - mx) + expf(lse_b - mx));
           w_old = expf(lse_a - lse_new);
-          w_new = expf(lse_b - lse_new) * inv;
+          w_new = expf(lse_b - lse_new) * o_scale;
         }
       }
 #pragma unroll
@@ -562,7 +631,8 @@ int fwd_blocks_per_cu(int d) { return d == 64 ? blocks_per_cu_impl<64>() : block
 
 int launch_fwd(int d, const FwdParams& p, int grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(kQueues), 0, s, p.queue.counters);
+  const int zgrid = p.n_split > 0 ? (int)std::min<int64_t>(64, ((int64_t)p.n_split + 255) / 256) : 1;
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(zgrid), dim3(256), 0, s, p.queue.counters, p.split_cnt, p.n_split);
   if (d == 64)
     hipLaunchKernelGGL(fwd_kernel<64>, dim3(grid), dim3(256), 0, s, p);
   else

@@ -15,6 +15,21 @@ namespace zl {
 // Backward dQ queue item: 128 query rows of one (final segment or ring group, head), looping
 // over every key range of the segment (all parts of a ring group).
 constexpr int kFwdRows = 128;
+constexpr int kFwdKeys = 64;  // keys per forward step
+// Split-KV of forward items (short queues leave compute units idle): a plan whose forward
+// queue holds fewer than kSplitWaves waves of items for the device's resident workgroups cuts
+// every item that costs more than 1/kSplitTargetWaves of a workgroup's fair share into key
+// pieces of about that share (at most kMaxPieces, each at least kMinPieceKeys keys,
+// block-aligned). One wave: a
+// compute unit running one forward workgroup still reaches about 80% of its two-workgroup
+// rate, so longer queues lose little to their tail.
+constexpr int kSplitWaves = 1;
+constexpr int kSplitTargetWaves = 1;  // about one piece per resident workgroup: each piece
+                                      // costs a partial write and its share of a merge
+constexpr int kMaxPieces = 16;
+constexpr int kMinPieceKeys = 1024;
+// Resident forward workgroups assumed by a host-only plan (256 CUs x 2).
+constexpr int kHostOnlySlots = 512;
 constexpr int kBwdKeys = 128;
 constexpr int kBwdRows = 64;
 // Rows (token, head pairs) per item of the backward pre-pass.
@@ -58,9 +73,14 @@ static_assert(sizeof(GroupDev) == 48, "GroupDev must stay 48 bytes");
 constexpr int merge_rows(int d) { return 256 / (d / 4); }
 
 // One work item: segment index, head, first row (token) of the block, rows in the block.
+// Forward items also carry their key range (the segment's, or a piece of it) and, for a
+// piece of a split item, the slot of its piece 0 (split, -1 otherwise) and
+// piece = index | (pieces << 16).
 struct alignas(16) Tile {
   int32_t seg, head, row0, nrows;
+  int32_t kv_begin, kv_end, split, piece;
 };
+static_assert(sizeof(Tile) == 32, "Tile must stay 32 bytes");
 
 // A set of kQueues work queues: items stored queue by queue, bounds[k]..bounds[k+1] for
 // queue k, and one counter per queue (kCounterStride ints apart) in the caller's workspace.
@@ -82,6 +102,10 @@ struct FwdParams {
   Queues queue;
   float scale_log2;  // softmax scale times log2(e)
   int32_t accumulate;  // ring parts fold into o/lse (running merge) instead of the slab
+  int32_t n_split;     // pieces of split items (slots of split_cnt, split_o, split_lse)
+  int32_t* split_cnt;  // per split item (at its piece-0 slot): pieces finished
+  float* split_o;      // [n_split][kFwdRows][D] normalised piece results
+  float* split_lse;    // [n_split][kFwdRows]
 };
 
 struct BwdParams {
@@ -139,6 +163,8 @@ struct zl_plan {
   std::vector<zl_group_info_t> groups;
   std::vector<zl::GroupDev> gdev;
   int64_t merge_blocks = 0;  // total blocks of a plan merge launch
+  int32_t split_tiles = 0;   // forward items cut into key pieces
+  int32_t split_pieces = 0;  // pieces of those items (slots of the split workspace)
   // device copies (one allocation, carved into the three tables)
   void* dev_block = nullptr;
   const zl::SegDev* d_segs = nullptr;

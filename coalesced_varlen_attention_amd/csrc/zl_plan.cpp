@@ -117,6 +117,53 @@ void distribute(const std::vector<Item>& items, const std::vector<int64_t>& unit
   }
 }
 
+// Split-KV of the forward queue. With fewer items than resident workgroups, compute units sit
+// idle while a few long items run; cutting those items into key pieces, each computed as a
+// normalised partial and merged by the last piece to finish (the exact merge of ring
+// accumulation), gives every unit work. Applies only when the queue holds fewer than
+// kSplitWaves waves; items above the cost target are cut into block-aligned pieces of at
+// least kMinPieceKeys keys.
+void split_forward(int64_t slots, std::vector<Item>* fwd, std::vector<int64_t>* unit, int32_t* n_tiles,
+                   int32_t* n_pieces) {
+  *n_tiles = 0;
+  *n_pieces = 0;
+  if (fwd->empty() || (int64_t)fwd->size() >= (int64_t)zl::kSplitWaves * slots) return;
+  double total = 0.0;
+  for (const Item& it : *fwd) total += (double)it.cost;
+  const double target = total / ((double)zl::kSplitTargetWaves * (double)slots);
+  std::vector<Item> out;
+  std::vector<int64_t> out_unit;
+  int64_t next = 0;
+  for (size_t j = 0; j < fwd->size(); ++j) {
+    const Item& it = (*fwd)[j];
+    const int64_t nk = it.t.kv_end - it.t.kv_begin;
+    const int64_t nb = (nk + zl::kFwdKeys - 1) / zl::kFwdKeys;
+    int64_t n = (int64_t)std::llround((double)it.cost / target);  // nearest: a ragged queue tail
+                                                                  // must not add a piece to every item
+    n = std::min<int64_t>(n, std::min<int64_t>(zl::kMaxPieces, nk / zl::kMinPieceKeys));
+    if (n < 2 || next + n > INT32_MAX) {
+      out.push_back(it);
+      out_unit.push_back((*unit)[j]);
+      continue;
+    }
+    for (int64_t pc = 0; pc < n; ++pc) {
+      Item x = it;
+      x.t.kv_begin = it.t.kv_begin + (int32_t)(nb * pc / n * zl::kFwdKeys);
+      x.t.kv_end = pc + 1 == n ? it.t.kv_end : it.t.kv_begin + (int32_t)(nb * (pc + 1) / n * zl::kFwdKeys);
+      x.t.split = (int32_t)next;
+      x.t.piece = (int32_t)(pc | (n << 16));
+      x.cost = (int64_t)x.t.nrows * (x.t.kv_end - x.t.kv_begin);
+      out.push_back(x);
+      out_unit.push_back((*unit)[j]);
+    }
+    next += n;
+    ++*n_tiles;
+  }
+  *n_pieces = (int32_t)next;
+  fwd->swap(out);
+  unit->swap(out_unit);
+}
+
 }  // namespace
 
 extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int64_t* cu_kv,
@@ -126,7 +173,7 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   *out = nullptr;
   if (d_head != 64 && d_head != 128)
     return fail(ZL_ERR_UNSUPPORTED, "zl_plan_build: d_head " + std::to_string(d_head) + " is not 64 or 128");
-  if (flags & ~ZL_PLAN_HOST_ONLY) return fail(ZL_ERR_INVALID, "zl_plan_build: unknown flag bits");
+  if (flags & ~(ZL_PLAN_HOST_ONLY | ZL_PLAN_NO_SPLIT)) return fail(ZL_ERR_INVALID, "zl_plan_build: unknown flag bits");
   if (n_seq < 1) return fail(ZL_ERR_INVALID, "zl_plan_build: n_seq must be >= 1");
   if (!cu_q || !cu_kv || !seq_heads) return fail(ZL_ERR_INVALID, "zl_plan_build: NULL sequence array");
   if (n_seg < 1 || !segs) return fail(ZL_ERR_INVALID, "zl_plan_build: need at least one segment");
@@ -330,16 +377,16 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
       const int64_t unit = (int64_t)i * 65536 + h;
       for (int64_t r = g.q_begin; r < g.q_end; r += zl::kFwdRows) {
         const int32_t n = (int32_t)std::min<int64_t>(zl::kFwdRows, g.q_end - r);
-        fwd.push_back({{i, h, (int32_t)r, n}, (int64_t)n * nk});
+        fwd.push_back({{i, h, (int32_t)r, n, g.kv_begin, g.kv_end, -1, 1 << 16}, (int64_t)n * nk});
         fwd_unit.push_back(unit);
         if (g.part <= 0) {
-          dq.push_back({{i, h, (int32_t)r, n}, (int64_t)n * chain_keys});
+          dq.push_back({{i, h, (int32_t)r, n, g.kv_begin, g.kv_end, -1, 1 << 16}, (int64_t)n * chain_keys});
           dq_unit.push_back(unit);
         }
       }
       for (int64_t r = g.kv_begin; r < g.kv_end; r += zl::kBwdKeys) {
         const int32_t n = (int32_t)std::min<int64_t>(zl::kBwdKeys, g.kv_end - r);
-        bwd.push_back({{i, h, (int32_t)r, n}, (int64_t)n * nq});
+        bwd.push_back({{i, h, (int32_t)r, n, (int32_t)r, (int32_t)r + n, -1, 1 << 16}, (int64_t)n * nq});
         bwd_unit.push_back(unit);
       }
     }
@@ -348,8 +395,24 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
       const int nhr = g.head_end - g.head_begin;
       const int toks = std::max(1, zl::kPreRows / nhr);
       for (int64_t t = g.q_begin; t < g.q_end; t += toks)
-        plan->pre_tiles.push_back({i, g.head_begin, (int32_t)t, (int32_t)std::min<int64_t>(toks, g.q_end - t)});
+        plan->pre_tiles.push_back(
+            {i, g.head_begin, (int32_t)t, (int32_t)std::min<int64_t>(toks, g.q_end - t), 0, 0, -1, 1 << 16});
     }
+  }
+  if (!(flags & ZL_PLAN_HOST_ONLY)) {
+    if (hipGetDevice(&plan->device) != hipSuccess) return fail(ZL_ERR_HIP, "zl_plan_build: hipGetDevice failed");
+    if (hipDeviceGetAttribute(&plan->n_cu, hipDeviceAttributeMultiprocessorCount, plan->device) != hipSuccess ||
+        plan->n_cu < 1)
+      return fail(ZL_ERR_HIP, "zl_plan_build: cannot query the compute unit count");
+  }
+  if (!(flags & ZL_PLAN_NO_SPLIT)) {
+    int64_t slots = zl::kHostOnlySlots;
+    if (!(flags & ZL_PLAN_HOST_ONLY)) {
+      const int per_cu = zl::fwd_blocks_per_cu(d_head);
+      if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_plan_build: forward kernel cannot be resident");
+      slots = (int64_t)plan->n_cu * per_cu;
+    }
+    split_forward(slots, &fwd, &fwd_unit, &plan->split_tiles, &plan->split_pieces);
   }
   if (fwd.size() > (size_t)INT32_MAX || bwd.size() > (size_t)INT32_MAX || plan->pre_tiles.size() > (size_t)INT32_MAX)
     return fail(ZL_ERR_INVALID, "zl_plan_build: too many work items");
@@ -358,10 +421,6 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   distribute(dq, dq_unit, &plan->dq_tiles, &plan->dq_bounds);
 
   if (!(flags & ZL_PLAN_HOST_ONLY)) {
-    if (hipGetDevice(&plan->device) != hipSuccess) return fail(ZL_ERR_HIP, "zl_plan_build: hipGetDevice failed");
-    if (hipDeviceGetAttribute(&plan->n_cu, hipDeviceAttributeMultiprocessorCount, plan->device) != hipSuccess ||
-        plan->n_cu < 1)
-      return fail(ZL_ERR_HIP, "zl_plan_build: cannot query the compute unit count");
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t b_segs = align(plan->segs.size() * sizeof(zl::SegDev));
     const size_t b_fwd = align(plan->fwd_tiles.size() * sizeof(zl::Tile));

@@ -84,6 +84,8 @@ typedef struct {
   int32_t d_head;
   float softmax_scale;
   int64_t dq_tiles;       /* work items of the backward dQ queue */
+  int32_t split_tiles;    /* forward items cut into key pieces (split-KV) */
+  int32_t split_pieces;   /* pieces of those items */
 } zl_plan_info_t;
 
 /*
@@ -109,6 +111,7 @@ typedef struct {
 /* Flags for zl_plan_build. */
 #define ZL_PLAN_HOST_ONLY 1u /* build and validate on the host only; no device tables, so the
                                 plan can be inspected but not run (used by CPU-only tests) */
+#define ZL_PLAN_NO_SPLIT 2u  /* never cut forward items into key pieces (see zl_plan_build) */
 
 /*
  * Validate the segment list and lower it into device work queues.
@@ -119,7 +122,7 @@ typedef struct {
  *   n_seg, segs           host array of segments (see zl_segment), n_seg >= 1
  *   d_head                64 or 128 (else ZL_ERR_UNSUPPORTED)
  *   softmax_scale         tau in softmax(tau * Q K^T); <= 0 selects 1/sqrt(d_head)
- *   flags                 0 or ZL_PLAN_HOST_ONLY
+ *   flags                 0, ZL_PLAN_HOST_ONLY, ZL_PLAN_NO_SPLIT, or both
  *   out                   receives the plan; the caller frees it with zl_plan_destroy
  * The host arrays are copied; the plan owns its device tables (allocated on the current
  * device) and nothing else. The forward queue holds one item per (segment, head, block of
@@ -129,6 +132,14 @@ typedef struct {
  * consecutive items of one (segment, head) go to the least-loaded queue, largest first, and
  * each queue is sorted by decreasing cost (rows x length of the other side), ties kept in
  * (segment, head, block) order. A workgroup drains its own XCD's queue, then the others.
+ * Split-KV: when the forward queue holds fewer items than there are resident forward
+ * workgroups (the device's CU count times the kernel's occupancy; 512 for a host-only plan),
+ * so that compute units would sit idle, every item costing more than a workgroup's fair share
+ * (the queue's total cost over the resident workgroups) is cut into block-aligned key pieces
+ * of about that share (at most 16, each at least 1024 keys). Each piece is a normalised partial over its keys; the
+ * last piece of an item to finish merges them exactly (the ring merge, §II-B) and stores the
+ * item's result. ZL_PLAN_NO_SPLIT turns this off. The pieces' partials live in the forward
+ * workspace, whose size grows accordingly (info.ws_fwd).
  */
 zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                         const int32_t* seq_heads, int32_t n_seg, const zl_segment* segs,
@@ -144,6 +155,9 @@ zl_status zl_plan_group(const zl_plan* plan, int32_t g, zl_group_info_t* info);
  * Copy a work queue to the host for inspection: which = 0 forward, 1 backward dK/dV,
  * 2 backward dQ (items of a ring group name its part-0 segment).
  * Each item is 4 int32: segment index, head, first row of the block, rows in the block.
+ * which = 3 is the forward queue again with 8 int32 per item: the same 4, then the item's
+ * key range [kv_begin, kv_end), the workspace slot of its piece 0 (-1 unless the item is a
+ * piece of a split item) and its piece index | (pieces << 16).
  * Writes min(cap, count) items to out (may be NULL when cap == 0); *count gets the total.
  */
 zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* out, int64_t cap, int64_t* count);

@@ -1,4 +1,4 @@
-"""HIP path vs the fp64 oracle at the full sizes of the four large packs, in the launch
+"""HIP path vs the fp64 oracle at the full sizes of the six large packs (the last one split-KV), in the launch
 configuration the benchmark times (one plan, one forward launch, ring merges, one backward
 launch over the whole pack).
 
@@ -126,7 +126,7 @@ def _check_sampled(pack, ins, out, seed):
             H.assert_close(n, np.concatenate(got[n]), np.concatenate(ref[n]))
 
 
-@pytest.mark.parametrize("name", ["image", "mixed", "ring", "long"])
+@pytest.mark.parametrize("name", ["image", "mixed", "ring", "long", "shard", "head1"])
 def test_full_size(name):
     pack = W.config(name)
     print(f"[case] {name}: {len(pack.segments)} segments, q rows {pack.q_rows()}, kv rows {pack.kv_rows()}", flush=True)

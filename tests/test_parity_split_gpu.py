@@ -1,0 +1,92 @@
+"""Split-KV forward (items cut into key pieces, merged by the last piece) vs the fp64 oracle.
+
+Packs with few long items make the plan cut every forward item into key pieces; the result
+must match the oracle element by element as an unsplit forward does, for final segments,
+ring parts (partials in the slab, then the plan merge) and the running merge, with ragged
+piece tails, at d_head 64 and 128. The backward runs on the split forward's O and LSE.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_harness as H
+
+pytestmark = [pytest.mark.gpu, H.requires_gpu]
+
+
+def _run(pack):
+    ins = W.draw(pack)
+    print(f"[case] {pack.name} d={pack.d} seqs={pack.seq_q}/{pack.seq_kv} segs={len(pack.segments)}", flush=True)
+    out = H.run_pack(pack, ins)
+    assert out["plan"].info["split_tiles"] > 0, "the pack was meant to be split"
+    ref = H.oracle_pack(pack, ins)
+    H.compare_full(pack, ins, out, ref)
+    return out, ref, ins
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_split_whole_sequences(d):
+    seg = ((0, 0, 1, 0, 4100, 0, 4100, -1), (1, 0, 2, 0, 700, 0, 2500, -1), (2, 0, 2, 0, 90, 0, 90, -1))
+    _run(W.Pack(f"split_whole{d}", (4100, 700, 90), (4100, 2500, 90), (1, 2, 2), seg, d, 51 + d))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_split_ring_parts(d):
+    """Ring parts long enough to be split: each part's pieces merge into its slab rows, then
+    the plan merge combines the parts."""
+    seg = ((0, 0, 2, 0, 333, 0, 2100, 1), (0, 0, 2, 0, 333, 2100, 6000, 0), (1, 1, 2, 0, 150, 0, 3000, -1))
+    _run(W.Pack(f"split_ring{d}", (333, 150), (6000, 3000), (2, 2), seg, d, 61 + d))
+
+
+def test_split_matches_unsplit_plan():
+    """The same pack with and without split-KV: both within the oracle tolerance of the
+    oracle and of each other. They are not closer to each other than to the oracle: P is
+    rounded to bf16 relative to each piece's own running max, so the two round differently."""
+    z = H.zl()
+    dev = torch.device("cuda:0")
+    seg = ((0, 0, 2, 0, 500, 0, 5000, -1),)
+    pack = W.Pack("split_vs_unsplit", (500,), (5000,), (2,), seg, 128, 71)
+    ins = W.draw(pack)
+    q, k, v = (ins[n].to(dev) for n in ("q", "k", "v"))
+    print("[case] split vs unsplit plan", flush=True)
+    outs = []
+    for split in (True, False):
+        plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, split=split)
+        assert (plan.info["split_tiles"] > 0) == split
+        o, lse, _, _ = z.attn_fwd(plan, q, k, v)
+        outs.append((H.f64(o), H.f64(lse)))
+    torch.cuda.synchronize()
+    ref = H.oracle_pack(pack, ins)
+    for (o, lse) in outs:
+        H.assert_close("O", o, ref["o"])
+        H.assert_close("LSE", lse, ref["lse"])
+    H.assert_close("O split vs unsplit", outs[0][0], outs[1][0])
+    H.assert_close("LSE split vs unsplit", outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_split_running_merge(d):
+    """Running merge of ring blocks whose items are split: the last piece of each item folds
+    the merged block result into the running O/LSE."""
+    z = H.zl()
+    dev = torch.device("cuda:0")
+    seq_q, seq_kv, heads = (260,), (7000,), (1,)
+    blocks = ((0, 2600), (2600, 2700), (2700, 7000))
+    pack = W.Pack(f"split_acc{d}", seq_q, seq_kv, heads, ((0, 0, 1, 0, 260, 0, 7000, -1),), d, 81 + d)
+    ins = W.draw(pack)
+    q, k, v = (ins[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.full((260, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((260,), float("-inf"), dtype=torch.float32, device=dev)
+    print(f"[case] split running merge d={d}", flush=True)
+    n_split = 0
+    for b in (2, 0, 1):
+        plan = z.Plan(seq_q, seq_kv, heads, ((0, 0, 1, 0, 260, blocks[b][0], blocks[b][1], 0),), d)
+        n_split += plan.info["split_tiles"]
+        z.attn_fwd_accumulate(plan, q, k, v, o, lse)
+    torch.cuda.synchronize()
+    assert n_split > 0
+    ref = H.oracle_pack(pack, ins)
+    H.assert_close("O", H.f64(o), ref["o"])
+    H.assert_close("LSE", H.f64(lse), ref["lse"])

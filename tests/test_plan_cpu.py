@@ -251,3 +251,59 @@ def test_head_subset_groups():
     assert g1["n_rows"] == 4 * 3 and g1["o_row"] == 3 * 5 + 2 and g1["part_row"] == 2 * 20
     assert (g1["head_begin"], g1["head_end"], g1["q_begin"], g1["q_end"]) == (2, 5, 3, 7)
     assert p.info["part_rows"] == 2 * 20 + 2 * 12
+
+
+def _pieces_by_item(p):
+    items = {}
+    for (seg, head, row0, nrows, k0, k1, split, piece) in p.tiles(3):
+        items.setdefault((seg, head, row0, nrows), []).append((k0, k1, split, piece & 0xFFFF, piece >> 16))
+    return items
+
+
+def test_split_kv_cuts_long_items_of_a_short_queue():
+    """One head of 8192 tokens: 64 forward items, far below 4 per resident workgroup (512
+    assumed for a host-only plan), so every item is cut into 8 key pieces of 1024 keys."""
+    p = z.Plan((8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, host_only=True)
+    assert p.info["split_tiles"] == 64 and p.info["split_pieces"] == 64 * 8
+    assert p.info["fwd_tiles"] == 64 * 8
+    slots = set()
+    for key, pieces in _pieces_by_item(p).items():
+        pieces.sort()
+        assert len(pieces) == 8
+        assert pieces[0][0] == 0 and pieces[-1][1] == 8192
+        for a, b in zip(pieces[:-1], pieces[1:]):
+            assert a[1] == b[0]                                  # contiguous, disjoint
+        for (k0, k1, split, idx, n) in pieces:
+            assert n == 8 and k0 % 64 == 0 and k1 - k0 >= 1024
+        assert sorted(x[3] for x in pieces) == list(range(8))
+        assert len({x[2] for x in pieces}) == 1                  # one slot per item
+        slots.add(pieces[0][2])
+    assert sorted(slots) == list(range(0, 512, 8))
+    # the workspace holds a counter, 128 O rows and 128 LSEs per piece
+    nosplit = z.Plan((8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, host_only=True, split=False)
+    assert nosplit.info["split_tiles"] == 0 and nosplit.info["fwd_tiles"] == 64
+    extra = p.info["ws_fwd"] - nosplit.info["ws_fwd"]
+    assert extra >= 512 * (4 + 128 * 128 * 4 + 128 * 4)
+    assert p.tiles(1) == nosplit.tiles(1) and p.tiles(2) == nosplit.tiles(2)  # backward untouched
+
+
+def test_split_kv_ragged_and_short_items():
+    """Pieces are block-aligned with the ragged tail in the last one; items with fewer than
+    2048 keys stay whole; unsplit items carry slot -1 and one piece."""
+    seg = ((0, 0, 2, 0, 300, 0, 4100, -1), (1, 0, 2, 0, 200, 0, 2000, -1))
+    p = z.Plan((300, 200), (4100, 2000), (2, 2), seg, 64, host_only=True)
+    for key, pieces in _pieces_by_item(p).items():
+        if key[0] == 1:
+            assert pieces == [(0, 2000, -1, 0, 1)]
+            continue
+        pieces.sort()
+        n = len(pieces)
+        assert 2 <= n <= 4 and pieces[0][0] == 0 and pieces[-1][1] == 4100
+        assert all(k0 % 64 == 0 for (k0, *_r) in pieces)
+
+
+def test_split_kv_leaves_large_packs_alone():
+    for name in ("image", "mixed", "ring", "long", "shard"):
+        assert host_plan(W.config(name)).info["split_tiles"] == 0, name
+    p = host_plan(W.config("head1"))  # 256 items < 512 resident workgroups: 2 pieces each
+    assert p.info["split_tiles"] == 256 and p.info["split_pieces"] == 256 * 2

@@ -108,7 +108,20 @@ def long() -> Pack:
     return whole_pack("long", lens, heads, 128, 5)
 
 
-CONFIGS = {"tiny": tiny, "image": image, "mixed": mixed, "ring": ring, "long": long}
+def shard() -> Pack:
+    """One GPU's Ulysses share of a single 32760-token video: 5 of its 40 heads (8-way head
+    split), full length, d_head 128, seed 6. 1280 forward items, 2.5 per resident workgroup."""
+    return whole_pack("shard", [32760], [5], 128, 6)
+
+
+def head1() -> Pack:
+    """One stored head of a 32760-token video, full length, d_head 128, seed 7: 256 forward
+    items, fewer than the resident workgroups, so the forward is split over keys."""
+    return whole_pack("head1", [32760], [1], 128, 7)
+
+
+CONFIGS = {"tiny": tiny, "image": image, "mixed": mixed, "ring": ring, "long": long, "shard": shard,
+           "head1": head1}
 
 
 def config(name: str) -> Pack:
