@@ -10,6 +10,7 @@ backward. Prints one JSON line; with --json-out also writes it to a file.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixed] [--no-cpu-baseline] [--ring-fold]
                     [--no-split]
+    python bench.py --price-table [--price-reps R] [--json-out FILE]
 """
 from __future__ import annotations
 
@@ -119,6 +120,96 @@ def calibrate_copy(gib: float = 2.0, reps: int = 3) -> int:
     return 0
 
 
+# Placement options of one sequence on `degree` ranks, as one rank's local attention share
+# (Zellige §IV-A, Table II): whole (1,1,1); Ulysses (1,h,1) keeps H/h heads at full length;
+# ring (1,1,k) keeps L/k queries against the L keys in k blocks, accumulated block by block;
+# all-gather (q,1,1) keeps L/q queries against all L keys; composed (1,h,k) both.
+PRICE_BUCKETS = (1024, 4096, 9450, 32760, 75600)
+PRICE_CONFIGS = (("whole", 1, 1, 1), ("ulysses", 2, 1, 1), ("ulysses", 4, 1, 1), ("ulysses", 8, 1, 1),
+                 ("ring", 1, 2, 1), ("ring", 1, 4, 1), ("ring", 1, 8, 1), ("allgather", 1, 1, 2),
+                 ("allgather", 1, 1, 4), ("allgather", 1, 1, 8), ("ulysses_ring", 2, 2, 1),
+                 ("ulysses_ring", 4, 2, 1), ("ulysses_ring", 2, 4, 1))
+PRICE_HEADS = 40
+
+
+def price_table(reps: int, out_path) -> int:
+    """Per-rank attention prices P_{b,theta} of this engine (Zellige §IV-B): forward and
+    backward time of one rank's local share of a bucket-length sequence under each placement
+    option, on this GPU, communication excluded. The ring forward runs as the ring executor
+    computes it, one running-merge launch per arriving key block; its backward is one launch
+    over all blocks. Also reports the launch floor: the same calls on a 64-token sequence."""
+    import torch
+    import workloads as W
+    import coalesced_varlen_attention_amd as zl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d, H = 128, PRICE_HEADS
+
+    def measure(L, h, k, qd):
+        heads = H // h
+        lq = L // (k * qd)                      # this rank's queries
+        blocks = [(b * L // k, (b + 1) * L // k) for b in range(k)]
+        segs = tuple((0, 0, heads, 0, lq, b0, b1, b if k > 1 else -1) for b, (b0, b1) in enumerate(blocks))
+        pack = W.Pack("price", (lq,), (L,), (heads,), segs, d, 11)
+        full = zl.Plan(pack.seq_q, pack.seq_kv, pack.heads, segs, d)
+        steps = [zl.Plan(pack.seq_q, pack.seq_kv, pack.heads, (sg[:7] + (0,),), d) for sg in segs] if k > 1 else [full]
+        info = full.info
+        g = torch.Generator(device=dev)
+        g.manual_seed(L * 64 + h * 8 + k + qd)
+        rnd = lambda rows: torch.randn(rows, d, generator=g, device=dev).to(torch.bfloat16)
+        q, kk, v, do = rnd(info["q_rows"]), rnd(info["kv_rows"]), rnd(info["kv_rows"]), rnd(info["q_rows"])
+        o = torch.empty(info["q_rows"], d, device=dev)
+        lse = torch.empty(info["q_rows"], device=dev)
+        dq = torch.empty(info["q_rows"], d, device=dev)
+        dk = torch.empty(info["kv_rows"], d, device=dev)
+        dv = torch.empty(info["kv_rows"], d, device=dev)
+        ws_f = torch.empty(max(p.info["ws_fwd"] for p in steps), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(info["ws_bwd"], dtype=torch.uint8, device=dev)
+
+        def fwd():
+            if k > 1:
+                lse.fill_(float("-inf"))
+                for p in steps:
+                    zl.attn_fwd_accumulate(p, q, kk, v, o, lse, workspace=ws_f)
+            else:
+                zl.attn_fwd(full, q, kk, v, o=o, lse=lse, workspace=ws_f)
+
+        def bwd():
+            zl.attn_bwd(full, q, kk, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+
+        fwd(); bwd()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        f_ms = b_ms = 0.0
+        for _ in range(reps):
+            ev[0].record(); fwd(); ev[1].record(); bwd(); ev[2].record()
+            torch.cuda.synchronize()
+            f_ms += ev[0].elapsed_time(ev[1]) / reps
+            b_ms += ev[1].elapsed_time(ev[2]) / reps
+        return f_ms, b_ms, 3.5 * info["fwd_flops"]
+
+    floor_f, floor_b, _ = measure(64, 1, 1, 1)
+    rows = []
+    for L in PRICE_BUCKETS:
+        for (name, h, k, qd) in PRICE_CONFIGS:
+            f_ms, b_ms, flops = measure(L, h, k, qd)
+            row = {"bucket_tokens": L, "config": name, "theta_qhk": [qd, h, k], "degree": qd * h * k,
+                   "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "price_ms": round(f_ms + b_ms, 4),
+                   "net_price_ms": round(f_ms + b_ms - floor_f - floor_b, 4),
+                   "tflops": round(flops / ((f_ms + b_ms) * 1e-3) / 1e12, 1)}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+    head = {"launch_floor_ms": round(floor_f + floor_b, 4), "heads": H, "d_head": d, "reps": reps}
+    print(json.dumps(head), flush=True)
+    if out_path:
+        with open(out_path, "w") as fh:
+            fh.write(json.dumps(head) + "\n")
+            for r in rows:
+                fh.write(json.dumps(r) + "\n")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,9 +223,14 @@ def main() -> int:
     ap.add_argument("--ring-fold", action="store_true",
                     help="forward ring groups block by block with the running merge (one launch per ring "
                          "block, folding into O/LSE) instead of one launch plus the LSE merge")
+    ap.add_argument("--price-table", action="store_true",
+                    help="print per-rank attention prices for every bucket x placement option (one JSON line each)")
+    ap.add_argument("--price-reps", type=int, default=3)
     args = ap.parse_args()
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.price_table:
+        return price_table(args.price_reps, args.json_out)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding is a design, not a measured path", file=sys.stderr)
