@@ -150,7 +150,9 @@ __device__ __forceinline__ void kv_dma(const KvDma& dm, uint32_t stage, int qb, 
   }
 }
 
-// LSE log2(e) (+inf past the end: P = 0) and D of the step's rows, one value per thread.
+// Row values of the step, one per thread: LSE log2(e) (+inf past the end) for threads below
+// 64, D (0 past the end) for the next 64. They become the accumulator initialisers when stored
+// to LDS (kv_rowinit_value), after the loads have long completed.
 __device__ __forceinline__ float kv_rowval(const float* lse2, const float* dvec, int64_t hmbase, int qb, int n_q,
                                            int tid) {
   const int r = tid & (kBwdRows - 1);
@@ -159,30 +161,11 @@ __device__ __forceinline__ float kv_rowval(const float* lse2, const float* dvec,
   return q < n_q ? dvec[hmbase + q] : 0.f;
 }
 
-// P = exp2(S tau log2e - LSE log2e) and dS = P (dP - D) for one 32-row half of a step, rounded
-// to bf16 in the two B-operand halves (rows 8(i/4) + 4hi + i%4; lse and dd point at row 4hi).
-__device__ __forceinline__ void bwd_p_ds(const f32x16& sacc, const f32x16& dpacc, ZL_LDS const float* lse,
-                                         ZL_LDS const float* dd, bool k_valid, float scale_log2, bf16x8 (&pb)[2],
-                                         bf16x8 (&dsb)[2]) {
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs) {
-    f32x8 a, b;
-#pragma unroll
-    for (int g2 = 0; g2 < 2; ++g2) {
-      const int g = 2 * hs + g2;
-      const f32x4 L = *(ZL_LDS const f32x4*)&lse[8 * g];
-      const f32x4 Dd = *(ZL_LDS const f32x4*)&dd[8 * g];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = 4 * g + u;
-        const float pe = k_valid ? fast_exp2(fmaf(sacc[i], scale_log2, -L[u])) : 0.f;
-        a[4 * g2 + u] = pe;
-        b[4 * g2 + u] = pe * (dpacc[i] - Dd[u]);
-      }
-    }
-    pb[hs] = to_bf16x8(a);
-    dsb[hs] = to_bf16x8(b);
-  }
+// Accumulator initialiser from a row value: -LSE log2e / (tau log2e) = -LSE / tau for S, so that
+// S tau log2e - LSE log2e = (Q K^T - LSE / tau) tau log2e (-inf past the end: P = 0); -D for
+// dP, so that dS = P dP' with dP' = dO V^T - D. `neg_inv_scale` is -1 / (tau log2e).
+__device__ __forceinline__ float kv_rowinit_value(float v, int tid, float neg_inv_scale) {
+  return tid < kBwdRows ? v * neg_inv_scale : -v;
 }
 
 // Operand reads of the key-major kernel (offsets in bytes within a stage's tile).
@@ -202,14 +185,28 @@ __device__ __forceinline__ bf16x8 kv_tr_op(ZL_LDS const char* tile, const int (&
              lds_read_tr(tile + (r0 + 8) / C::kGroupRows * C::kPitch + tbase[cb]));
 }
 
-// S and dP of one 32-row half (16 MFMAs, S and dP alternating), operands two MFMAs ahead;
-// with kValu, the P / dS of the other half (element m per MFMA, rounded per 8) in the slots.
+// The step's row initialisers of half mb in accumulator order: element i of a lane is row
+// 8(i/4) + 4hi + i%4.
+__device__ __forceinline__ f32x16 kv_rowinit(ZL_LDS const float* vals, int mb, int hi) {
+  f32x16 r;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 x = *(ZL_LDS const f32x4*)&vals[32 * mb + 8 * g + 4 * hi];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[4 * g + u] = x[u];
+  }
+  return r;
+}
+
+// S' = Q K^T - LSE / tau and dP' = dO V^T - D of one 32-row half (16 MFMAs, alternating; sacc
+// and dpacc hold the row initialisers on entry), operands two MFMAs ahead; with kValu, the
+// P = exp2(S' tau log2e) and dS = P dP' of the other half (element m per MFMA, rounded per 8)
+// in the slots.
 template <int D, bool kValu>
 __device__ __forceinline__ void kv_scores(ZL_LDS const char* qt, ZL_LDS const char* dot, const int (&rbase)[4], int mb,
                                           const bf16x8 (&kreg)[KvCfg<D>::kSteps],
                                           const bf16x8 (&vreg)[KvCfg<D>::kSteps], f32x16& sacc, f32x16& dpacc,
-                                          const f32x16& s_o, const f32x16& dp_o, const float (&lse_o)[16],
-                                          const float (&dd_o)[16], float scale_log2, bf16x8 (&pb)[2],
+                                          const f32x16& s_o, const f32x16& dp_o, float scale_log2, bf16x8 (&pb)[2],
                                           bf16x8 (&dsb)[2]) {
   using C = KvCfg<D>;
   constexpr int kM = 2 * C::kSteps;
@@ -221,16 +218,16 @@ __device__ __forceinline__ void kv_scores(ZL_LDS const char* qt, ZL_LDS const ch
   for (int m = 0; m < kM; ++m) {
     if (m + 2 < kM) op[m + 2] = kv_row_op<D>((m + 2) & 1 ? dot : qt, rbase, mb, (m + 2) >> 1);
     if (m & 1)
-      dpacc = mfma32(op[m], vreg[m >> 1], m == 1 ? f32x16{} : dpacc);
+      dpacc = mfma32(op[m], vreg[m >> 1], dpacc);
     else
-      sacc = mfma32(op[m], kreg[m >> 1], m == 0 ? f32x16{} : sacc);
+      sacc = mfma32(op[m], kreg[m >> 1], sacc);
     if (kValu) {
 #pragma unroll
       for (int u = 0; u < 16 / kM; ++u) {
         const int e = m * (16 / kM) + u;
-        const float pv = fast_exp2(fmaf(s_o[e], scale_log2, -lse_o[e]));
+        const float pv = fast_exp2(s_o[e] * scale_log2);
         pe[e % 8] = pv;
-        ds[e % 8] = pv * (dp_o[e] - dd_o[e]);
+        ds[e % 8] = pv * dp_o[e];
         if (e % 8 == 7) {
           pb[e / 8] = to_bf16x8(pe);
           dsb[e / 8] = to_bf16x8(ds);
@@ -247,8 +244,7 @@ __device__ __forceinline__ void kv_grads(ZL_LDS const char* qt, ZL_LDS const cha
                                          const int (&tbase)[KvCfg<D>::kCb], int mb, const bf16x8 (&pb)[2],
                                          const bf16x8 (&dsb)[2], f32x16 (&dv_acc)[KvCfg<D>::kCb],
                                          f32x16 (&dk_acc)[KvCfg<D>::kCb], const f32x16& s_o, const f32x16& dp_o,
-                                         const float (&lse_o)[16], const float (&dd_o)[16], float scale_log2,
-                                         bf16x8 (&pb_o)[2], bf16x8 (&dsb_o)[2]) {
+                                         float scale_log2, bf16x8 (&pb_o)[2], bf16x8 (&dsb_o)[2]) {
   using C = KvCfg<D>;
   constexpr int kM = 4 * C::kCb;  // (hs, cb) x {dV, dK}
   bf16x8 op[kM];
@@ -268,29 +264,14 @@ __device__ __forceinline__ void kv_grads(ZL_LDS const char* qt, ZL_LDS const cha
 #pragma unroll
       for (int u = 0; u < 16 / kM; ++u) {
         const int e = m * (16 / kM) + u;
-        const float pv = fast_exp2(fmaf(s_o[e], scale_log2, -lse_o[e]));
+        const float pv = fast_exp2(s_o[e] * scale_log2);
         pe[e % 8] = pv;
-        ds[e % 8] = pv * (dp_o[e] - dd_o[e]);
+        ds[e % 8] = pv * dp_o[e];
         if (e % 8 == 7) {
           pb_o[e / 8] = to_bf16x8(pe);
           dsb_o[e / 8] = to_bf16x8(ds);
         }
       }
-    }
-  }
-}
-
-// LSE log2(e) and D of the rows 8(e/4) + 4hi + e%4 of half mb.
-__device__ __forceinline__ void kv_rowvals(ZL_LDS const float* lse_s, ZL_LDS const float* dd_s, int mb, int hi,
-                                           float (&lse)[16], float (&dd)[16]) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 L = *(ZL_LDS const f32x4*)&lse_s[32 * mb + 8 * g + 4 * hi];
-    const f32x4 Dd = *(ZL_LDS const f32x4*)&dd_s[32 * mb + 8 * g + 4 * hi];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      lse[4 * g + u] = L[u];
-      dd[4 * g + u] = Dd[u];
     }
   }
 }
@@ -332,6 +313,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   }
   const int dma_row = lane / C::kRowChunks;
   const int dma_col = 16 * ((lane % C::kRowChunks) ^ qt_x<D>(dma_row));
+  const float neg_inv_scale = -1.0f / p.scale_log2;
 
   const int home = blockIdx.x % kQueues;
   int drained = 0;
@@ -380,7 +362,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
       dk_acc[cb] = f32x16{};
       dv_acc[cb] = f32x16{};
     }
-    if (tid < 2 * C::kBq) *(ZL_LDS float*)(lds0 + 2 * C::kTileBytes + 4 * tid) = rv0;
+    if (tid < 2 * C::kBq) *(ZL_LDS float*)(lds0 + 2 * C::kTileBytes + 4 * tid) = kv_rowinit_value(rv0, tid, neg_inv_scale);
     dma_wait();
     __syncthreads();
 
@@ -413,18 +395,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
       //   D: dV, dK of half 1
       f32x16 s0, dp0, s1, dp1;
       bf16x8 pb0[2], dsb0[2], pb1[2], dsb1[2];
-      float lse0[16], dd0[16], lse1[16], dd1[16];
-      kv_rowvals(lse_s, dd_s, 0, hi, lse0, dd0);
-      kv_scores<D, false>(qt, dot, rbase, 0, kreg, vreg, s0, dp0, s1, dp1, lse0, dd0, p.scale_log2, pb1, dsb1);
-      kv_rowvals(lse_s, dd_s, 1, hi, lse1, dd1);
+      // Row initialisers: half 0 first (its first MFMAs need them), half 1 under phase A.
+      s0 = kv_rowinit(lse_s, 0, hi);
+      dp0 = kv_rowinit(dd_s, 0, hi);
+      s1 = kv_rowinit(lse_s, 1, hi);
+      dp1 = kv_rowinit(dd_s, 1, hi);
+      kv_scores<D, false>(qt, dot, rbase, 0, kreg, vreg, s0, dp0, s1, dp1, p.scale_log2, pb1, dsb1);
       __builtin_amdgcn_sched_barrier(0);
-      kv_scores<D, true>(qt, dot, rbase, 1, kreg, vreg, s1, dp1, s0, dp0, lse0, dd0, p.scale_log2, pb0, dsb0);
+      kv_scores<D, true>(qt, dot, rbase, 1, kreg, vreg, s1, dp1, s0, dp0, p.scale_log2, pb0, dsb0);
       __builtin_amdgcn_sched_barrier(0);
-      kv_grads<D, true>(qt, dot, tbase, 0, pb0, dsb0, dv_acc, dk_acc, s1, dp1, lse1, dd1, p.scale_log2, pb1, dsb1);
+      kv_grads<D, true>(qt, dot, tbase, 0, pb0, dsb0, dv_acc, dk_acc, s1, dp1, p.scale_log2, pb1, dsb1);
       __builtin_amdgcn_sched_barrier(0);
-      kv_grads<D, false>(qt, dot, tbase, 1, pb1, dsb1, dv_acc, dk_acc, s1, dp1, lse1, dd1, p.scale_log2, pb0, dsb0);
+      kv_grads<D, false>(qt, dot, tbase, 1, pb1, dsb1, dv_acc, dk_acc, s1, dp1, p.scale_log2, pb0, dsb0);
       __builtin_amdgcn_sched_barrier(0);
-      if (qb + 1 < nqb && tid < 2 * C::kBq) *(ZL_LDS float*)(nxt + 2 * C::kTileBytes + 4 * tid) = rvn;
+      if (qb + 1 < nqb && tid < 2 * C::kBq)
+        *(ZL_LDS float*)(nxt + 2 * C::kTileBytes + 4 * tid) = kv_rowinit_value(rvn, tid, neg_inv_scale);
       dma_wait();
       __syncthreads();
     }
