@@ -23,6 +23,7 @@ _LIB_PATH = os.path.join(_HERE, "libzl.so")
 
 ZL_PLAN_HOST_ONLY = 1
 ZL_PLAN_NO_SPLIT = 2
+ZL_PLAN_QKV_PACKED = 4
 BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 SEGMENT_FIELDS = ("seq", "head_begin", "head_end", "q_begin", "q_end", "kv_begin", "kv_end", "part")
 
@@ -45,7 +46,7 @@ class _PlanInfo(ctypes.Structure):
                 ("n_parts_max", ctypes.c_int32), ("fwd_tiles", ctypes.c_int64), ("bwd_tiles", ctypes.c_int64),
                 ("fwd_flops", ctypes.c_double), ("bwd_flops", ctypes.c_double), ("d_head", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("dq_tiles", ctypes.c_int64), ("split_tiles", ctypes.c_int32),
-                ("split_pieces", ctypes.c_int32)]
+                ("split_pieces", ctypes.c_int32), ("qkv_rows", ctypes.c_int64)]
 
 
 class _GroupInfo(ctypes.Structure):
@@ -121,7 +122,8 @@ class Plan:
     """
 
     def __init__(self, seq_q: Sequence[int], seq_kv: Sequence[int], heads: Sequence[int], segments, d: int,
-                 scale: Optional[float] = None, host_only: bool = False, split: bool = True):
+                 scale: Optional[float] = None, host_only: bool = False, split: bool = True,
+                 qkv_packed: bool = False):
         n = len(seq_q)
         if len(seq_kv) != n or len(heads) != n:
             raise ValueError("seq_q, seq_kv and heads must have the same length")
@@ -136,7 +138,8 @@ class Plan:
             for name, val in zip(SEGMENT_FIELDS, s):
                 setattr(segs[i], name, int(val))
         self._h = ctypes.c_void_p()
-        flags = (ZL_PLAN_HOST_ONLY if host_only else 0) | (0 if split else ZL_PLAN_NO_SPLIT)
+        flags = ((ZL_PLAN_HOST_ONLY if host_only else 0) | (0 if split else ZL_PLAN_NO_SPLIT) |
+                 (ZL_PLAN_QKV_PACKED if qkv_packed else 0))
         _check(lib().zl_plan_build(n, ctypes.cast(cu_q, ctypes.c_void_p), ctypes.cast(cu_kv, ctypes.c_void_p),
                                   ctypes.cast(hs, ctypes.c_void_p), len(segments), ctypes.cast(segs, ctypes.c_void_p),
                                   int(d), float(scale) if scale else 0.0, flags, ctypes.byref(self._h)))
@@ -183,6 +186,13 @@ class Plan:
             pass
 
 
+def _input_rows(info):
+    """Rows of q and of k / v: the packed buffer's for a QKV-packed plan."""
+    if info["qkv_rows"]:
+        return info["qkv_rows"], info["qkv_rows"]
+    return info["q_rows"], info["kv_rows"]
+
+
 def _check_tensor(t, name, dtype, rows, d, device):
     import torch
     if t.dtype != dtype:
@@ -204,9 +214,10 @@ def attn_fwd(plan: Plan, q, k, v, o=None, lse=None, o_part=None, lse_part=None, 
     """
     import torch
     info, d, dev = plan.info, plan.d, q.device
-    _check_tensor(q, "q", torch.bfloat16, info["q_rows"], d, dev)
-    _check_tensor(k, "k", torch.bfloat16, info["kv_rows"], d, dev)
-    _check_tensor(v, "v", torch.bfloat16, info["kv_rows"], d, dev)
+    rq, rkv = _input_rows(info)
+    _check_tensor(q, "q", torch.bfloat16, rq, d, dev)
+    _check_tensor(k, "k", torch.bfloat16, rkv, d, dev)
+    _check_tensor(v, "v", torch.bfloat16, rkv, d, dev)
     if o is None:
         o = torch.empty(info["q_rows"], d, dtype=torch.float32, device=dev)
     if lse is None:
@@ -236,9 +247,10 @@ def attn_fwd_accumulate(plan: Plan, q, k, v, o, lse, workspace=None, stream=None
     may hold at most one part per group. Returns ``(o, lse)``."""
     import torch
     info, d, dev = plan.info, plan.d, q.device
-    _check_tensor(q, "q", torch.bfloat16, info["q_rows"], d, dev)
-    _check_tensor(k, "k", torch.bfloat16, info["kv_rows"], d, dev)
-    _check_tensor(v, "v", torch.bfloat16, info["kv_rows"], d, dev)
+    rq, rkv = _input_rows(info)
+    _check_tensor(q, "q", torch.bfloat16, rq, d, dev)
+    _check_tensor(k, "k", torch.bfloat16, rkv, d, dev)
+    _check_tensor(v, "v", torch.bfloat16, rkv, d, dev)
     _check_tensor(o, "o", torch.float32, info["q_rows"], d, dev)
     _check_tensor(lse, "lse", torch.float32, info["q_rows"], 1, dev)
     if workspace is None:
@@ -287,21 +299,28 @@ def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspa
     each of them on the same workspace."""
     import torch
     info, d, dev = plan.info, plan.d, q.device
-    _check_tensor(q, "q", torch.bfloat16, info["q_rows"], d, dev)
-    _check_tensor(k, "k", torch.bfloat16, info["kv_rows"], d, dev)
-    _check_tensor(v, "v", torch.bfloat16, info["kv_rows"], d, dev)
+    rq, rkv = _input_rows(info)
+    _check_tensor(q, "q", torch.bfloat16, rq, d, dev)
+    _check_tensor(k, "k", torch.bfloat16, rkv, d, dev)
+    _check_tensor(v, "v", torch.bfloat16, rkv, d, dev)
     _check_tensor(do, "do", torch.bfloat16, info["q_rows"], d, dev)
     _check_tensor(o, "o", torch.float32, info["q_rows"], d, dev)
     _check_tensor(lse, "lse", torch.float32, info["q_rows"], 1, dev)
-    if dq is None:
-        dq = torch.empty(info["q_rows"], d, dtype=torch.float32, device=dev)
-    if dk is None:
-        dk = torch.empty(info["kv_rows"], d, dtype=torch.float32, device=dev)
-    if dv is None:
-        dv = torch.empty(info["kv_rows"], d, dtype=torch.float32, device=dev)
-    _check_tensor(dq, "dq", torch.float32, info["q_rows"], d, dev)
-    _check_tensor(dk, "dk", torch.float32, info["kv_rows"], d, dev)
-    _check_tensor(dv, "dv", torch.float32, info["kv_rows"], d, dev)
+    if info["qkv_rows"]:  # one packed gradient buffer, passed as dq, dk and dv
+        if dq is None:
+            dq = torch.empty(info["qkv_rows"], d, dtype=torch.float32, device=dev)
+        dk = dk if dk is not None else dq
+        dv = dv if dv is not None else dq
+    else:
+        if dq is None:
+            dq = torch.empty(info["q_rows"], d, dtype=torch.float32, device=dev)
+        if dk is None:
+            dk = torch.empty(info["kv_rows"], d, dtype=torch.float32, device=dev)
+        if dv is None:
+            dv = torch.empty(info["kv_rows"], d, dtype=torch.float32, device=dev)
+    _check_tensor(dq, "dq", torch.float32, rq, d, dev)
+    _check_tensor(dk, "dk", torch.float32, rkv, d, dev)
+    _check_tensor(dv, "dv", torch.float32, rkv, d, dev)
     if workspace is None:
         workspace = torch.empty(info["ws_bwd"], dtype=torch.uint8, device=dev)
     if workspace.numel() < info["ws_bwd"]:

@@ -62,6 +62,11 @@ zl_status check_runnable(const zl_plan* plan, const char* who) {
   return ZL_OK;
 }
 
+// In the QKV-packed layout the three tensors (and the three gradients) are one buffer.
+bool packed_ok(const zl_plan* plan, const void* a, const void* b, const void* c) {
+  return !(plan->flags & ZL_PLAN_QKV_PACKED) || (a == b && b == c);
+}
+
 bool has_final(const zl_plan* plan) {
   for (const auto& s : plan->segs)
     if (s.part < 0) return true;
@@ -87,6 +92,7 @@ extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   info->ws_bwd = kCounterBytes + 2 * align256((size_t)plan->q_rows * sizeof(float));
   info->q_rows = plan->q_rows;
   info->kv_rows = plan->kv_rows;
+  info->qkv_rows = (plan->flags & ZL_PLAN_QKV_PACKED) ? 3 * plan->q_rows : 0;
   info->part_rows = plan->part_rows;
   info->n_groups = (int32_t)plan->groups.size();
   info->n_parts_max = plan->n_parts_max;
@@ -150,6 +156,7 @@ extern "C" zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void*
   zl_status st = check_runnable(plan, "zl_attn_fwd");
   if (st != ZL_OK) return st;
   if (!q || !k || !v) return fail(ZL_ERR_INVALID, "zl_attn_fwd: q, k or v is NULL");
+  if (!packed_ok(plan, q, k, v)) return fail(ZL_ERR_INVALID, "zl_attn_fwd: a QKV-packed plan needs q == k == v");
   if (!workspace) return fail(ZL_ERR_INVALID, "zl_attn_fwd: workspace is NULL");
   if (has_final(plan) && (!o || !lse)) return fail(ZL_ERR_INVALID, "zl_attn_fwd: o or lse is NULL");
   if (!plan->groups.empty() && (!o_part || !lse_part))
@@ -169,6 +176,7 @@ extern "C" zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void*
   p.queue = {plan->d_fwd, plan->d_bounds, (int32_t*)workspace};
   p.scale_log2 = plan->scale * 1.4426950408889634f;
   set_split(plan, workspace, &p);
+  p.packed = (plan->flags & ZL_PLAN_QKV_PACKED) ? 1 : 0;
   const int per_cu = zl::fwd_blocks_per_cu(plan->d);
   if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_fwd: forward kernel cannot be resident");
   const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, (int64_t)plan->fwd_tiles.size());
@@ -186,6 +194,8 @@ extern "C" zl_status zl_attn_fwd_accumulate(const zl_plan* plan, const void* q, 
   zl_status st = check_runnable(plan, "zl_attn_fwd_accumulate");
   if (st != ZL_OK) return st;
   if (!q || !k || !v) return fail(ZL_ERR_INVALID, "zl_attn_fwd_accumulate: q, k or v is NULL");
+  if (!packed_ok(plan, q, k, v))
+    return fail(ZL_ERR_INVALID, "zl_attn_fwd_accumulate: a QKV-packed plan needs q == k == v");
   if (!workspace) return fail(ZL_ERR_INVALID, "zl_attn_fwd_accumulate: workspace is NULL");
   if (!o || !lse) return fail(ZL_ERR_INVALID, "zl_attn_fwd_accumulate: o or lse is NULL");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(workspace, 16) ||
@@ -202,6 +212,7 @@ extern "C" zl_status zl_attn_fwd_accumulate(const zl_plan* plan, const void* q, 
   p.scale_log2 = plan->scale * 1.4426950408889634f;
   p.accumulate = 1;
   set_split(plan, workspace, &p);
+  p.packed = (plan->flags & ZL_PLAN_QKV_PACKED) ? 1 : 0;
   const int per_cu = zl::fwd_blocks_per_cu(plan->d);
   if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_fwd_accumulate: forward kernel cannot be resident");
   const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, (int64_t)plan->fwd_tiles.size());
@@ -257,6 +268,8 @@ extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, cons
   if (st != ZL_OK) return st;
   if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv || !workspace)
     return fail(ZL_ERR_INVALID, "zl_attn_bwd: NULL pointer");
+  if (!packed_ok(plan, q, k, v) || !packed_ok(plan, dq, dk, dv))
+    return fail(ZL_ERR_INVALID, "zl_attn_bwd: a QKV-packed plan needs q == k == v and dq == dk == dv");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(d_o, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16) || !aligned(lse, 4))
     return fail(ZL_ERR_INVALID, "zl_attn_bwd: tensors and workspace must be 16-byte aligned, lse 4-byte");
@@ -281,6 +294,7 @@ extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, cons
   p.kv_ranges = plan->d_ranges;
   p.scale = plan->scale;
   p.scale_log2 = plan->scale * 1.4426950408889634f;
+  p.packed = (plan->flags & ZL_PLAN_QKV_PACKED) ? 1 : 0;
   const int per_cu = zl::bwd_blocks_per_cu(plan->d);
   const int per_cu_dq = zl::dq_blocks_per_cu(plan->d);
   if (per_cu < 1 || per_cu_dq < 1) return fail(ZL_ERR_HIP, "zl_attn_bwd: backward kernels cannot be resident");

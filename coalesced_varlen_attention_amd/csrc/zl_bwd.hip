@@ -116,8 +116,10 @@ __device__ __forceinline__ int qt_row(int r) {
 struct KvDma {
   const char* qbase;    // row of local query 0 of the segment (Q)
   const char* dobase;   // ... (dO)
-  int64_t rs_bytes;     // bytes between consecutive query tokens
-  uint32_t lane_off;    // this lane's byte offset within a full step (row in group, chunk)
+  int64_t rs_bytes;     // bytes between consecutive query tokens of Q
+  int64_t rs_do;        // ... of dO (differs from Q's in the QKV-packed layout)
+  uint32_t lane_off;    // this lane's byte offset within a full step (row in group, chunk), Q
+  uint32_t lane_off_do; // ... dO
   int lane_row;         // this lane's row within its load group
   int lane_col;         // this lane's byte column
   int n_q;
@@ -133,19 +135,19 @@ __device__ __forceinline__ void kv_dma(const KvDma& dm, uint32_t stage, int qb, 
 #pragma unroll
     for (int i = 0; i < C::kDma; ++i) {
       const int grp = i * 4 + wave;
-      const int64_t off = (int64_t)(q0 + grp * C::kGroupRows) * dm.rs_bytes;
-      lds_dma16(stage + grp * C::kPitch, dm.qbase + off, dm.lane_off);
-      lds_dma16(stage + C::kTileBytes + grp * C::kPitch, dm.dobase + off, dm.lane_off);
+      const int64_t r = q0 + grp * C::kGroupRows;
+      lds_dma16(stage + grp * C::kPitch, dm.qbase + r * dm.rs_bytes, dm.lane_off);
+      lds_dma16(stage + C::kTileBytes + grp * C::kPitch, dm.dobase + r * dm.rs_do, dm.lane_off_do);
     }
   } else {
-    const int64_t off0 = (int64_t)q0 * dm.rs_bytes;
 #pragma unroll
     for (int i = 0; i < C::kDma; ++i) {
       const int grp = i * 4 + wave;
       const int row = min(grp * C::kGroupRows + dm.lane_row, dm.n_q - 1 - q0);
-      const uint32_t off = (uint32_t)row * (uint32_t)dm.rs_bytes + dm.lane_col;
-      lds_dma16(stage + grp * C::kPitch, dm.qbase + off0, off);
-      lds_dma16(stage + C::kTileBytes + grp * C::kPitch, dm.dobase + off0, off);
+      lds_dma16(stage + grp * C::kPitch, dm.qbase + (int64_t)q0 * dm.rs_bytes,
+                (uint32_t)row * (uint32_t)dm.rs_bytes + dm.lane_col);
+      lds_dma16(stage + C::kTileBytes + grp * C::kPitch, dm.dobase + (int64_t)q0 * dm.rs_do,
+                (uint32_t)row * (uint32_t)dm.rs_do + dm.lane_col);
     }
   }
 }
@@ -276,7 +278,7 @@ __device__ __forceinline__ void kv_grads(ZL_LDS const char* qt, ZL_LDS const cha
   }
 }
 
-template <int D>
+template <int D, bool kPacked>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
@@ -330,12 +332,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
 
     KvDma dm;
     dm.n_q = sg.q_end - sg.q_begin;
-    dm.rs_bytes = (int64_t)nh * D * 2;
-    dm.qbase = (const char*)p.q + (sg.q_row0 + (int64_t)sg.q_begin * nh + h) * D * 2;
+    const QkvRows qr = qkv_rows<kPacked>(sg);  // planar, or the QKV-packed layout
+    const int tstr = qr.t_stride;
+    const int64_t kp0 = qr.k0;
+    const int voff = qr.v_off;
+    dm.rs_bytes = (int64_t)tstr * D * 2;
+    dm.rs_do = (int64_t)nh * D * 2;
+    dm.qbase = (const char*)p.q + (qr.q0 + (int64_t)sg.q_begin * tstr + h) * D * 2;
     dm.dobase = (const char*)p.d_o + (sg.q_row0 + (int64_t)sg.q_begin * nh + h) * D * 2;
     dm.lane_row = dma_row;
     dm.lane_col = dma_col;
     dm.lane_off = (uint32_t)dma_row * (uint32_t)dm.rs_bytes + dma_col;
+    dm.lane_off_do = (uint32_t)dma_row * (uint32_t)dm.rs_do + dma_col;
     const int nqb = (dm.n_q + C::kBq - 1) / C::kBq;
     const int64_t hmbase = sg.q_row0 + (int64_t)h * sg.lq + sg.q_begin;  // head-major row of local token 0
 
@@ -349,11 +357,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
     const int ktok = tile.row0 + min(key_local, nk - 1);
     bf16x8 kreg[C::kSteps], vreg[C::kSteps];
     {
-      const int64_t off = (sg.kv_row0 + (int64_t)ktok * nh + h) * D + 8 * hi;
+      const int64_t off = (kp0 + (int64_t)ktok * tstr + h) * D + 8 * hi;
+      const int64_t vo = off + (int64_t)voff * D;
 #pragma unroll
       for (int s = 0; s < C::kSteps; ++s) {
         kreg[s] = *(const bf16x8*)(gk + off + 16 * s);
-        vreg[s] = *(const bf16x8*)(gv + off + 16 * s);
+        vreg[s] = *(const bf16x8*)(gv + vo + 16 * s);
       }
     }
     f32x16 dk_acc[C::kCb], dv_acc[C::kCb];
@@ -416,9 +425,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
 
     // dK = tau dK^T, dV = dV^T, written once: lane = key, 4 consecutive columns per store.
     if (k_valid) {
-      const int64_t row = sg.kv_row0 + (int64_t)ktok * nh + h;
+      const int64_t row = kp0 + (int64_t)ktok * tstr + h;
       float* dkr = p.dk + row * D;
-      float* dvr = p.dv + row * D;
+      float* dvr = p.dv + (row + voff) * D;
 #pragma unroll
       for (int cb = 0; cb < C::kCb; ++cb)
 #pragma unroll
@@ -562,7 +571,7 @@ __device__ __forceinline__ void dq_mask(f32x16& s, int vr) {
     if (8 * (i / 4) + (i % 4) >= vr) s[i] = -INFINITY;
 }
 
-template <int D>
+template <int D, bool kPacked>
 __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
   using C = DqCfg<D>;
   using L = KvCfg<D>;
@@ -609,10 +618,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
     const SegDev sg = p.segs[tile.seg];
     const int nh = sg.nh;
     const int h = tile.head;
-    const int64_t rs_bytes = (int64_t)nh * D * 2;
+    const QkvRows qr = qkv_rows<kPacked>(sg);  // planar, or the QKV-packed layout
+    const int tstr = qr.t_stride;
+    const int64_t kp0 = qr.k0;
+    const int voff = qr.v_off;
+    const int64_t rs_bytes = (int64_t)tstr * D * 2;
     const uint32_t lane_off = (uint32_t)dma_row * (uint32_t)rs_bytes + dma_col;
-    const char* kseq = (const char*)p.k + (sg.kv_row0 + h) * D * 2;
-    const char* vseq = (const char*)p.v + (sg.kv_row0 + h) * D * 2;
+    const char* kseq = (const char*)p.k + (kp0 + h) * D * 2;
+    const char* vseq = (const char*)p.v + (kp0 + voff + h) * D * 2;
 
     int n_blk = 0;
     for (int r = 0; r < sg.chain_len; ++r) {
@@ -631,11 +644,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
     const int qi = wave * 32 + l32;
     const bool q_valid = qi < tile.nrows;
     const int qtok = tile.row0 + (q_valid ? qi : tile.nrows - 1);
-    const int64_t qrow = sg.q_row0 + (int64_t)qtok * nh + h;
+    const int64_t qrow = sg.q_row0 + (int64_t)qtok * nh + h;                // dO (planar)
+    const int64_t qprow = qr.q0 + (int64_t)qtok * tstr + h;  // Q, dQ
     bf16x8 qreg[C::kSteps], doreg[C::kSteps];
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s) {
-      qreg[s] = *(const bf16x8*)(gq + qrow * D + 8 * hi + 16 * s);
+      qreg[s] = *(const bf16x8*)(gq + qprow * D + 8 * hi + 16 * s);
       doreg[s] = *(const bf16x8*)(gdo + qrow * D + 8 * hi + 16 * s);
     }
     const int64_t hm = sg.q_row0 + (int64_t)h * sg.lq + qtok;
@@ -683,7 +697,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
     }
 
     if (q_valid) {
-      float* out = p.dq + qrow * D;
+      float* out = p.dq + qprow * D;
 #pragma unroll
       for (int cb = 0; cb < C::kCb; ++cb)
 #pragma unroll
@@ -708,28 +722,34 @@ int occupancy(K kernel) {
 int bwd_blocks_per_cu(int d) {
   static int c64 = -1, c128 = -1;
   int& c = d == 64 ? c64 : c128;
-  if (c < 0) c = d == 64 ? occupancy(dkdv_kernel<64>) : occupancy(dkdv_kernel<128>);
+  if (c < 0) c = d == 64 ? occupancy(dkdv_kernel<64, false>) : occupancy(dkdv_kernel<128, false>);
   return c;
 }
 
 int dq_blocks_per_cu(int d) {
   static int c64 = -1, c128 = -1;
   int& c = d == 64 ? c64 : c128;
-  if (c < 0) c = d == 64 ? occupancy(dq_kernel<64>) : occupancy(dq_kernel<128>);
+  if (c < 0) c = d == 64 ? occupancy(dq_kernel<64, false>) : occupancy(dq_kernel<128, false>);
   return c;
+}
+
+template <int D, bool kPacked>
+void launch_bwd_impl(const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages, hipStream_t s) {
+  if (stages & ZL_BWD_PRE) hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(grid_pre), dim3(256), 0, s, p);
+  if (stages & ZL_BWD_DKDV) hipLaunchKernelGGL((dkdv_kernel<D, kPacked>), dim3(grid), dim3(256), 0, s, p);
+  if (stages & ZL_BWD_DQ) hipLaunchKernelGGL((dq_kernel<D, kPacked>), dim3(grid_dq), dim3(256), 0, s, p);
 }
 
 int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (d == 64) {
-    if (stages & ZL_BWD_PRE) hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(grid_pre), dim3(256), 0, s, p);
-    if (stages & ZL_BWD_DKDV) hipLaunchKernelGGL(dkdv_kernel<64>, dim3(grid), dim3(256), 0, s, p);
-    if (stages & ZL_BWD_DQ) hipLaunchKernelGGL(dq_kernel<64>, dim3(grid_dq), dim3(256), 0, s, p);
-  } else {
-    if (stages & ZL_BWD_PRE) hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid_pre), dim3(256), 0, s, p);
-    if (stages & ZL_BWD_DKDV) hipLaunchKernelGGL(dkdv_kernel<128>, dim3(grid), dim3(256), 0, s, p);
-    if (stages & ZL_BWD_DQ) hipLaunchKernelGGL(dq_kernel<128>, dim3(grid_dq), dim3(256), 0, s, p);
-  }
+  if (d == 64 && p.packed)
+    launch_bwd_impl<64, true>(p, grid_pre, grid, grid_dq, stages, s);
+  else if (d == 64)
+    launch_bwd_impl<64, false>(p, grid_pre, grid, grid_dq, stages, s);
+  else if (p.packed)
+    launch_bwd_impl<128, true>(p, grid_pre, grid, grid_dq, stages, s);
+  else
+    launch_bwd_impl<128, false>(p, grid_pre, grid, grid_dq, stages, s);
   return hipPeekAtLastError() == hipSuccess ? 0 : 1;
 }
 

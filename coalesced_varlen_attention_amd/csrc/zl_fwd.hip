@@ -406,7 +406,7 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D>& cx, FwdState<D>& st, i
   __syncthreads();
 }
 
-template <int D>
+template <int D, bool kPacked>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::kVBytes + 2 * C::kKBytes];
@@ -453,7 +453,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
     const SegDev sg = p.segs[tile.seg];
     const int nh = sg.nh;
     const int h = tile.head;
-    cx.rs = (int64_t)nh * D;
+    const QkvRows qr = qkv_rows<kPacked>(sg);  // planar, or the QKV-packed layout
+    cx.rs = (int64_t)qr.t_stride * D;          // K / V elements between consecutive tokens
     cx.row_bytes = (uint32_t)(cx.rs * 2);
     cx.blk_bytes = (int64_t)C::kBk * cx.rs * 2;
     cx.koff_dma = (uint32_t)(wave * C::kGroupRows + cx.dma_krow) * cx.row_bytes + cx.dma_kcol;
@@ -461,8 +462,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
     cx.k_dma_step = (int64_t)4 * C::kGroupRows * cx.rs * 2;
     cx.n_kv = tile.kv_end - tile.kv_begin;  // the segment's keys, or one piece of them
     cx.n_blk = (cx.n_kv + C::kBk - 1) / C::kBk;
-    cx.kbase = (const bf16*)p.k + (sg.kv_row0 + (int64_t)tile.kv_begin * nh + h) * D;
-    cx.vbase = (const bf16*)p.v + (sg.kv_row0 + (int64_t)tile.kv_begin * nh + h) * D;
+    cx.kbase = (const bf16*)p.k + (qr.k0 + (int64_t)tile.kv_begin * qr.t_stride + h) * D;
+    cx.vbase = (const bf16*)p.v + (qr.k0 + qr.v_off + (int64_t)tile.kv_begin * qr.t_stride + h) * D;
     const int n = cx.n_blk;
 
     // Prologue: K(0), K(1) into LDS; this lane's query row into registers (clamped to the
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
     const int qtok = tile.row0 + (q_valid ? qi : tile.nrows - 1);
     FwdState<D> st;
     {
-      const bf16* qp = gq + (sg.q_row0 + (int64_t)qtok * nh + h) * D + 8 * hi;
+      const bf16* qp = gq + (qr.q0 + (int64_t)qtok * qr.t_stride + h) * D + 8 * hi;
 #pragma unroll
       for (int s = 0; s < C::kSteps; ++s) st.q[s] = *(const bf16x8*)(qp + 16 * s);
     }
@@ -619,7 +620,7 @@ int blocks_per_cu_impl() {
   static int cached = -1;
   if (cached < 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<D>, 256, 0) != hipSuccess) n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<D, false>, 256, 0) != hipSuccess) n = 0;
     cached = n;
   }
   return cached;
@@ -633,10 +634,14 @@ int launch_fwd(int d, const FwdParams& p, int grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int zgrid = p.n_split > 0 ? (int)std::min<int64_t>(64, ((int64_t)p.n_split + 255) / 256) : 1;
   hipLaunchKernelGGL(zero_counters_kernel, dim3(zgrid), dim3(256), 0, s, p.queue.counters, p.split_cnt, p.n_split);
-  if (d == 64)
-    hipLaunchKernelGGL(fwd_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+  if (d == 64 && p.packed)
+    hipLaunchKernelGGL((fwd_kernel<64, true>), dim3(grid), dim3(256), 0, s, p);
+  else if (d == 64)
+    hipLaunchKernelGGL((fwd_kernel<64, false>), dim3(grid), dim3(256), 0, s, p);
+  else if (p.packed)
+    hipLaunchKernelGGL((fwd_kernel<128, true>), dim3(grid), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(fwd_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<128, false>), dim3(grid), dim3(256), 0, s, p);
   return hipPeekAtLastError() == hipSuccess ? 0 : 1;
 }
 

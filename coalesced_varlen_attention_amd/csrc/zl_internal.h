@@ -40,6 +40,10 @@ constexpr int kQueues = 8;
 constexpr int kCounterStride = 16;  // ints between queue counters (64 bytes)
 
 // A segment as the kernels see it. Rows are (token, head) pairs of d contiguous values.
+// O, LSE and dO always use the planar query-side layout (q_row0, nh rows per token). Q, K, V
+// and their gradients are planar too (Q at q_row0, K and V at kv_row0), or, in the QKV-packed
+// layout [tokens][Q, K, V][heads][d] (equal query and key lengths), one buffer in which the
+// sequence starts at row 3 q_row0 with 3 nh rows per token and K, V nh and 2 nh rows after Q.
 struct alignas(16) SegDev {
   int64_t q_row0;     // query-side row of (token 0, head 0) of the segment's sequence
   int64_t kv_row0;    // key-side row of (token 0, head 0)
@@ -54,6 +58,19 @@ struct alignas(16) SegDev {
   int32_t pad[3];
 };
 static_assert(sizeof(SegDev) == 80, "SegDev must stay 80 bytes");
+
+// Q / K / V (and gradient) rows of a segment: token stride, row of (token 0, head 0) of Q and
+// of K, and rows from K to V.
+struct QkvRows {
+  int32_t t_stride;
+  int64_t q0, k0;
+  int32_t v_off;
+};
+template <bool kPacked>
+__host__ __device__ __forceinline__ QkvRows qkv_rows(const SegDev& sg) {
+  if (kPacked) return {3 * sg.nh, 3 * sg.q_row0, 3 * sg.q_row0 + sg.nh, sg.nh};
+  return {sg.nh, sg.q_row0, sg.kv_row0, 0};
+}
 
 // A KV-split group as the merge kernel sees it: its slab rows (token-major over its head
 // subset) and where each lands in O/LSE.
@@ -106,6 +123,7 @@ struct FwdParams {
   int32_t* split_cnt;  // per split item (at its piece-0 slot): pieces finished
   float* split_o;      // [n_split][kFwdRows][D] normalised piece results
   float* split_lse;    // [n_split][kFwdRows]
+  int32_t packed;      // Q, K, V in the QKV-packed layout (selects the kernel instance)
 };
 
 struct BwdParams {
@@ -128,6 +146,7 @@ struct BwdParams {
   const int32_t* kv_ranges;  // (kv_begin, kv_end) pairs of the key-range chains
   float scale;       // softmax scale
   float scale_log2;  // softmax scale times log2(e)
+  int32_t packed;    // Q, K, V and their gradients in the QKV-packed layout (kernel instance)
 };
 
 // Kernel launchers (defined next to their kernels). They return the launch status.

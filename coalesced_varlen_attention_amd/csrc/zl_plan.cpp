@@ -173,7 +173,7 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   *out = nullptr;
   if (d_head != 64 && d_head != 128)
     return fail(ZL_ERR_UNSUPPORTED, "zl_plan_build: d_head " + std::to_string(d_head) + " is not 64 or 128");
-  if (flags & ~(ZL_PLAN_HOST_ONLY | ZL_PLAN_NO_SPLIT)) return fail(ZL_ERR_INVALID, "zl_plan_build: unknown flag bits");
+  if (flags & ~(ZL_PLAN_HOST_ONLY | ZL_PLAN_NO_SPLIT | ZL_PLAN_QKV_PACKED)) return fail(ZL_ERR_INVALID, "zl_plan_build: unknown flag bits");
   if (n_seq < 1) return fail(ZL_ERR_INVALID, "zl_plan_build: n_seq must be >= 1");
   if (!cu_q || !cu_kv || !seq_heads) return fail(ZL_ERR_INVALID, "zl_plan_build: NULL sequence array");
   if (n_seg < 1 || !segs) return fail(ZL_ERR_INVALID, "zl_plan_build: need at least one segment");
@@ -205,6 +205,13 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   }
   plan->q_rows = qoff[n_seq];
   plan->kv_rows = kvoff[n_seq];
+  const bool packed = flags & ZL_PLAN_QKV_PACKED;
+  if (packed)
+    for (int s = 0; s < n_seq; ++s)
+      if (lq[s] != lkv[s])
+        return fail(ZL_ERR_INVALID, "zl_plan_build: ZL_PLAN_QKV_PACKED needs equal query and key lengths; sequence " +
+                                        std::to_string(s) + " has " + std::to_string(lq[s]) + " and " +
+                                        std::to_string(lkv[s]));
 
   // Segment checks and ring groups (keyed by sequence, query range and head range).
   std::map<std::tuple<int, int, int, int, int>, int> group_of;
@@ -324,6 +331,7 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     d.q_row0 = qoff[g.seq];
     d.kv_row0 = kvoff[g.seq];
     d.nh = seq_heads[g.seq];
+
     d.lq = (int32_t)lq[g.seq];
     d.q_begin = g.q_begin;
     d.q_end = g.q_end;

@@ -86,6 +86,8 @@ typedef struct {
   int64_t dq_tiles;       /* work items of the backward dQ queue */
   int32_t split_tiles;    /* forward items cut into key pieces (split-KV) */
   int32_t split_pieces;   /* pieces of those items */
+  int64_t qkv_rows;       /* rows of the packed QKV (and dQKV) buffer: 3 * q_rows, or 0 unless
+                             ZL_PLAN_QKV_PACKED */
 } zl_plan_info_t;
 
 /*
@@ -112,6 +114,11 @@ typedef struct {
 #define ZL_PLAN_HOST_ONLY 1u /* build and validate on the host only; no device tables, so the
                                 plan can be inspected but not run (used by CPU-only tests) */
 #define ZL_PLAN_NO_SPLIT 2u  /* never cut forward items into key pieces (see zl_plan_build) */
+#define ZL_PLAN_QKV_PACKED 4u /* Q, K, V share one buffer, per sequence [tokens][Q, K, V][heads][d]
+                                 (the layout of a QKV-packed all-to-all, §IV-D / Table II), and so
+                                 do dQ, dK, dV; needs equal query and key lengths. Sequence s starts
+                                 at packed row 3 * (its first planar row); O, LSE, dO stay planar.
+                                 Pass the packed buffer as q, k and v (and as dq, dk, dv). */
 
 /*
  * Validate the segment list and lower it into device work queues.
@@ -122,7 +129,7 @@ typedef struct {
  *   n_seg, segs           host array of segments (see zl_segment), n_seg >= 1
  *   d_head                64 or 128 (else ZL_ERR_UNSUPPORTED)
  *   softmax_scale         tau in softmax(tau * Q K^T); <= 0 selects 1/sqrt(d_head)
- *   flags                 0, ZL_PLAN_HOST_ONLY, ZL_PLAN_NO_SPLIT, or both
+ *   flags                 0 or an OR of ZL_PLAN_HOST_ONLY, ZL_PLAN_NO_SPLIT, ZL_PLAN_QKV_PACKED
  *   out                   receives the plan; the caller frees it with zl_plan_destroy
  * The host arrays are copied; the plan owns its device tables (allocated on the current
  * device) and nothing else. The forward queue holds one item per (segment, head, block of

@@ -13,9 +13,9 @@ def host_plan(pack):
     return z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale, host_only=True)
 
 
-def expect_error(status, seq_q, seq_kv, heads, segs, d=128, scale=None, match=None):
+def expect_error(status, seq_q, seq_kv, heads, segs, d=128, scale=None, match=None, **kw):
     with pytest.raises(z.ZlError) as e:
-        z.Plan(seq_q, seq_kv, heads, segs, d, scale, host_only=True)
+        z.Plan(seq_q, seq_kv, heads, segs, d, scale, host_only=True, **kw)
     assert e.value.status == status
     if match:
         assert match in str(e.value), str(e.value)
@@ -307,3 +307,12 @@ def test_split_kv_leaves_large_packs_alone():
         assert host_plan(W.config(name)).info["split_tiles"] == 0, name
     p = host_plan(W.config("head1"))  # 256 items < 512 resident workgroups: 2 pieces each
     assert p.info["split_tiles"] == 256 and p.info["split_pieces"] == 256 * 2
+
+
+def test_qkv_packed_plan():
+    seg = ((0, 0, 2, 0, 10, 0, 10, -1), (1, 0, 3, 0, 6, 0, 6, -1))
+    p = z.Plan((10, 6), (10, 6), (2, 3), seg, 64, host_only=True, qkv_packed=True)
+    assert p.info["qkv_rows"] == 3 * (10 * 2 + 6 * 3) and p.info["q_rows"] == 38
+    assert z.Plan((10, 6), (10, 6), (2, 3), seg, 64, host_only=True).info["qkv_rows"] == 0
+    expect_error(ZL_ERR_INVALID, [10], [12], [2], [(0, 0, 2, 0, 10, 0, 12, -1)], match="equal query and key",
+                 qkv_packed=True)
