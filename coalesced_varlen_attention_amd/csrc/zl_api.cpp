@@ -29,6 +29,11 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Queue counters at the head of each workspace: forward kQueues, backward 2 x kQueues, each
 // kCounterStride ints apart.
 constexpr size_t kCounterBytes = 2 * zl::kQueues * zl::kCounterStride * sizeof(int32_t);
+// Backward workspace after the counters: -D and -LSE / tau per query row, then the sentinel
+// rows (64 x -inf, 64 x 0). The key-major kernel addresses the arrays with 32-bit byte
+// offsets, so the query rows are limited to 2^29.
+constexpr size_t kSentinelBytes = 2 * zl::kBwdRows * sizeof(float);
+constexpr int64_t kMaxBwdQueryRows = INT64_C(1) << 29;
 
 // Forward workspace after the queue counters, for split items: one counter per piece slot,
 // then each piece's normalised O rows and LSEs.
@@ -89,7 +94,7 @@ extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   if (!plan || !info) return fail(ZL_ERR_INVALID, "zl_plan_info: NULL argument");
   std::memset(info, 0, sizeof(*info));
   info->ws_fwd = kCounterBytes + split_bytes(plan);
-  info->ws_bwd = kCounterBytes + 2 * align256((size_t)plan->q_rows * sizeof(float));
+  info->ws_bwd = kCounterBytes + 2 * align256((size_t)plan->q_rows * sizeof(float)) + kSentinelBytes;
   info->q_rows = plan->q_rows;
   info->kv_rows = plan->kv_rows;
   info->qkv_rows = (plan->flags & ZL_PLAN_QKV_PACKED) ? 3 * plan->q_rows : 0;
@@ -268,6 +273,8 @@ extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, cons
   if (st != ZL_OK) return st;
   if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv || !workspace)
     return fail(ZL_ERR_INVALID, "zl_attn_bwd: NULL pointer");
+  if (plan->q_rows > kMaxBwdQueryRows)
+    return fail(ZL_ERR_UNSUPPORTED, "zl_attn_bwd: more than 2^29 query rows");
   if (!packed_ok(plan, q, k, v) || !packed_ok(plan, dq, dk, dv))
     return fail(ZL_ERR_INVALID, "zl_attn_bwd: a QKV-packed plan needs q == k == v and dq == dk == dv");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(d_o, 16) ||
@@ -286,8 +293,9 @@ extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, cons
   p.kvq = {plan->d_bwd, plan->d_bounds + (zl::kQueues + 1), (int32_t*)workspace};
   p.dqq = {plan->d_dq, plan->d_bounds + 2 * (zl::kQueues + 1),
            (int32_t*)workspace + zl::kQueues * zl::kCounterStride};
-  p.dvec = (float*)((char*)workspace + kCounterBytes);
-  p.lse2 = (float*)((char*)workspace + kCounterBytes + align256((size_t)plan->q_rows * sizeof(float)));
+  p.dneg = (float*)((char*)workspace + kCounterBytes);
+  p.lsec = (float*)((char*)workspace + kCounterBytes + align256((size_t)plan->q_rows * sizeof(float)));
+  p.sentinel = (float*)((char*)workspace + kCounterBytes + 2 * align256((size_t)plan->q_rows * sizeof(float)));
   p.segs = plan->d_segs;
   p.pre_tiles = plan->d_pre;
   p.n_pre = (int32_t)plan->pre_tiles.size();

@@ -7,16 +7,19 @@
 // For a ring part the LSE and O are the merged ones, so P is the global softmax restricted
 // to the part's keys; dQ sums over every part of the group.
 //
-// Pre-pass: D and LSE log2(e) for every covered query row, stored head-major (row
-//   q_row0 + h * Lq + t of the sequence) so that the key-major kernel reads the 64 rows of a
-//   step as one contiguous 256-byte run; both queue counters zeroed.
+// Pre-pass: -D and -LSE / tau for every covered query row, stored head-major (row
+//   q_row0 + h * Lq + t of the sequence) so that the key-major kernel loads the 64 rows of a
+//   step as one contiguous 256-byte run; both queue counters zeroed; the sentinel rows
+//   (-inf, 0) that stand in for rows past a segment's end written.
 // dK/dV kernel: one item = 128 key rows of one (segment, head); 4 waves x 32 keys. Each wave
 //   keeps its K and V rows in registers as B operands of S = Q K^T and dP = dO V^T (lane = one
 //   key column), so P and dS come out of the MFMA already in the B-operand layout of
 //   dV^T = dO^T P and dK^T = Q^T dS; dO^T and Q^T are read from the same LDS tiles with
-//   transposed LDS reads. The 64-row Q and dO tiles of a step reach LDS by direct global-to-LDS
-//   loads, double-buffered and issued one step ahead, so a step costs one barrier. dK and dV
-//   accumulate in registers and are written once.
+//   transposed LDS reads. The 64-row Q and dO tiles of a step, and its rows' -LSE / tau and
+//   -D (the initial values of the S and dP accumulators), reach LDS by direct global-to-LDS
+//   loads into a ring of three stages, issued two steps ahead, so a step costs one barrier and
+//   waits only for loads issued a step earlier. dK and dV accumulate in registers and are
+//   written once.
 // dQ kernel: one item = 128 query rows of one (segment or ring group, head); 4 waves x 32
 //   query rows, the forward's shape: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers
 //   (lane = one query row, whose LSE and D are then per-lane scalars), and
@@ -41,6 +44,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
     p.kvq.counters[threadIdx.x * kCounterStride] = 0;
     p.dqq.counters[threadIdx.x * kCounterStride] = 0;
   }
+  if (blockIdx.x == 0 && threadIdx.x < 2 * kBwdRows) p.sentinel[threadIdx.x] = threadIdx.x < kBwdRows ? -INFINITY : 0.f;
+  const float neg_inv_tau = -1.0f / p.scale;
   constexpr int kPer = D / 16;  // elements per lane
   const int sub = threadIdx.x & 15;
   const int rsel = threadIdx.x >> 4;
@@ -66,8 +71,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
       for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
       if (sub == 0) {
         const int64_t hm = sg.q_row0 + (int64_t)h * sg.lq + tok;
-        p.dvec[hm] = acc;
-        p.lse2[hm] = p.lse[row] * 1.4426950408889634f;
+        p.dneg[hm] = -acc;
+        p.lsec[hm] = p.lse[row] * neg_inv_tau;
       }
     }
   }
@@ -93,7 +98,10 @@ struct KvCfg {
   static constexpr int kPitch = 1024 + 16;
   static constexpr int kTileBytes = kBq / kGroupRows * kPitch;
   static constexpr int kDma = kBq / kGroupRows / 4;       // loads per thread per tile
-  static constexpr int kStageBytes = 2 * kTileBytes + 2 * kBq * 4;  // Q, dO, LSE, D
+  static constexpr int kStageBytes = 2 * kTileBytes + 2 * kBq * 4;  // Q, dO, -LSE/tau, -D
+  static constexpr int kStages = 3;
+  static constexpr int kDmaPerStep = 2 * kDma;            // tile loads per wave per step (+1 rows
+                                                          // load on waves 0 and 1)
   static constexpr int kSub = kSteps / 4;                 // k-steps per operand base
 };
 
@@ -152,22 +160,18 @@ __device__ __forceinline__ void kv_dma(const KvDma& dm, uint32_t stage, int qb, 
   }
 }
 
-// Row values of the step, one per thread: LSE log2(e) (+inf past the end) for threads below
-// 64, D (0 past the end) for the next 64. They become the accumulator initialisers when stored
-// to LDS (kv_rowinit_value), after the loads have long completed.
-__device__ __forceinline__ float kv_rowval(const float* lse2, const float* dvec, int64_t hmbase, int qb, int n_q,
-                                           int tid) {
-  const int r = tid & (kBwdRows - 1);
-  const int q = qb * kBwdRows + r;
-  if (tid < kBwdRows) return q < n_q ? lse2[hmbase + q] : INFINITY;
-  return q < n_q ? dvec[hmbase + q] : 0.f;
-}
-
-// Accumulator initialiser from a row value: -LSE log2e / (tau log2e) = -LSE / tau for S, so that
-// S tau log2e - LSE log2e = (Q K^T - LSE / tau) tau log2e (-inf past the end: P = 0); -D for
-// dP, so that dS = P dP' with dP' = dO V^T - D. `neg_inv_scale` is -1 / (tau log2e).
-__device__ __forceinline__ float kv_rowinit_value(float v, int tid, float neg_inv_scale) {
-  return tid < kBwdRows ? v * neg_inv_scale : -v;
+// Row values of step qb into a stage (after its Q and dO tiles): wave 0 loads the 64 rows'
+// -LSE / tau, wave 1 their -D, one direct global-to-LDS load each. Rows past the segment's end
+// read the sentinel (-inf: P = 0; 0), so every value is the initial value of the S or dP
+// accumulator of its row. Offsets are bytes from the array (the sentinel lies after both).
+__device__ __forceinline__ void kv_dma_rows(uint32_t rows_lds, const BwdParams& p, int64_t hmbase, int qb, int n_q,
+                                            int wave, int lane) {
+  if (wave >= 2) return;
+  const char* base = wave == 0 ? (const char*)p.lsec : (const char*)p.dneg;
+  const int q = qb * kBwdRows + lane;
+  const uint32_t off = q < n_q ? (uint32_t)((hmbase + q) * 4)
+                               : (uint32_t)((const char*)(p.sentinel + wave * kBwdRows) - base);
+  lds_dma4(rows_lds + wave * kBwdRows * 4, base, off);
 }
 
 // Operand reads of the key-major kernel (offsets in bytes within a stage's tile).
@@ -281,7 +285,7 @@ __device__ __forceinline__ void kv_grads(ZL_LDS const char* qt, ZL_LDS const cha
 template <int D, bool kPacked>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   using C = KvCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[C::kStages * C::kStageBytes];
   __shared__ int32_t s_item;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(ZL_LDS char*)smem;
 
@@ -315,7 +319,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   }
   const int dma_row = lane / C::kRowChunks;
   const int dma_col = 16 * ((lane % C::kRowChunks) ^ qt_x<D>(dma_row));
-  const float neg_inv_scale = -1.0f / p.scale_log2;
 
   const int home = blockIdx.x % kQueues;
   int drained = 0;
@@ -347,11 +350,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
     const int nqb = (dm.n_q + C::kBq - 1) / C::kBq;
     const int64_t hmbase = sg.q_row0 + (int64_t)h * sg.lq + sg.q_begin;  // head-major row of local token 0
 
-    // Step 0's rows into stage 0 while this wave's keys load.
-    kv_dma<D>(dm, lds0, 0, wave_u);
-    const float rv0 = tid < 2 * C::kBq ? kv_rowval(p.lse2, p.dvec, hmbase, 0, dm.n_q, tid) : 0.f;
-
     // This wave's 32 keys in registers (B operands, lane = key column); clamped past the end.
+    // Issued before the first two steps' loads, so that waiting for step 0 covers them.
     const int key_local = wave * 32 + l32;
     const bool k_valid = key_local < nk;
     const int ktok = tile.row0 + min(key_local, nk - 1);
@@ -371,19 +371,26 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
       dk_acc[cb] = f32x16{};
       dv_acc[cb] = f32x16{};
     }
-    if (tid < 2 * C::kBq) *(ZL_LDS float*)(lds0 + 2 * C::kTileBytes + 4 * tid) = kv_rowinit_value(rv0, tid, neg_inv_scale);
+    // Steps 0 and 1 into stages 0 and 1, then wait for everything: the key registers must be
+    // complete before the step loop in the compiler's own accounting too (the fake uses below),
+    // or it would wait inside every step; waiting for step 1 as well costs once per item.
+    kv_dma<D>(dm, lds0, 0, wave_u);
+    kv_dma_rows(lds0 + 2 * C::kTileBytes, p, hmbase, 0, dm.n_q, wave_u, lane);
+    if (nqb > 1) {
+      kv_dma<D>(dm, lds0 + C::kStageBytes, 1, wave_u);
+      kv_dma_rows(lds0 + C::kStageBytes + 2 * C::kTileBytes, p, hmbase, 1, dm.n_q, wave_u, lane);
+    }
     dma_wait();
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) asm volatile("" ::"v"(kreg[s]), "v"(vreg[s]));
     __syncthreads();
 
+    uint32_t cur = lds0, ahead = lds0 + 2 * C::kStageBytes;  // stages of steps qb and qb + 2
     for (int qb = 0; qb < nqb; ++qb) {
-      const uint32_t cur = lds0 + (qb & 1) * C::kStageBytes;
-      const uint32_t nxt = lds0 + ((qb + 1) & 1) * C::kStageBytes;
-      // The next step's rows go to the other stage (read in the previous step, which every
-      // wave has finished); its LSE and D are stored at the end of this step.
-      float rvn = 0.f;
-      if (qb + 1 < nqb) {
-        kv_dma<D>(dm, nxt, qb + 1, wave_u);
-        if (tid < 2 * C::kBq) rvn = kv_rowval(p.lse2, p.dvec, hmbase, qb + 1, dm.n_q, tid);
+      // Step qb + 2 goes to the stage step qb - 1 read (every wave passed the barrier after it).
+      if (qb + 2 < nqb) {
+        kv_dma<D>(dm, ahead, qb + 2, wave_u);
+        kv_dma_rows(ahead + 2 * C::kTileBytes, p, hmbase, qb + 2, dm.n_q, wave_u, lane);
       }
       ZL_LDS const char* qt = (ZL_LDS const char*)cur;
       ZL_LDS const char* dot = (ZL_LDS const char*)(cur + C::kTileBytes);
@@ -417,10 +424,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
       kv_grads<D, false>(qt, dot, tbase, 1, pb1, dsb1, dv_acc, dk_acc, s1, dp1, p.scale_log2, pb0, dsb0);
       __builtin_amdgcn_sched_barrier(0);
-      if (qb + 1 < nqb && tid < 2 * C::kBq)
-        *(ZL_LDS float*)(nxt + 2 * C::kTileBytes + 4 * tid) = kv_rowinit_value(rvn, tid, neg_inv_scale);
-      dma_wait();
-      __syncthreads();
+      // Step qb + 1's loads (issued a step ago) have landed once only step qb + 2's are
+      // outstanding.
+      if (qb + 1 < nqb) {
+        if (qb + 2 < nqb) {
+          if (wave_u < 2)
+            dma_wait_all_but<C::kDmaPerStep + 1>();
+          else
+            dma_wait_all_but<C::kDmaPerStep>();
+        } else {
+          dma_wait();
+        }
+        __syncthreads();
+      }
+      cur = cur + C::kStageBytes == lds0 + C::kStages * C::kStageBytes ? lds0 : cur + C::kStageBytes;
+      ahead = ahead + C::kStageBytes == lds0 + C::kStages * C::kStageBytes ? lds0 : ahead + C::kStageBytes;
     }
 
     // dK = tau dK^T, dV = dV^T, written once: lane = key, 4 consecutive columns per store.
@@ -653,8 +671,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
       doreg[s] = *(const bf16x8*)(gdo + qrow * D + 8 * hi + 16 * s);
     }
     const int64_t hm = sg.q_row0 + (int64_t)h * sg.lq + qtok;
-    const float lse2 = p.lse2[hm];
-    const float dd = p.dvec[hm];
+    const float lse2 = -p.lsec[hm] * p.scale_log2;  // LSE log2(e)
+    const float dd = -p.dneg[hm];                     // D
 
     f32x16 acc[C::kCb];
 #pragma unroll

@@ -98,7 +98,20 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_base, const char* base, u
                : "memory");
 }
 
+// The same with 4 bytes per lane: lane l's bytes land at lds_base + 4 l.
+__device__ __forceinline__ void lds_dma4(uint32_t lds_base, const char* base, uint32_t off) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory");
+}
+
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector memory operations of this wave are outstanding (they complete in
+// issue order): the loads issued before the last N have landed.
+template <int N>
+__device__ __forceinline__ void dma_wait_all_but() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Device-coherent 16-byte store and loads (sc1: written through to, and read from, the point
 // of coherence of all XCDs, past the per-XCD L2 and per-CU L1). For data one workgroup hands

@@ -136,8 +136,9 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
-  float* dvec;  // per query row: sum_c dO * O, head-major rows (workspace)
-  float* lse2;  // per query row: LSE * log2(e), head-major rows (workspace)
+  float* dneg;  // per query row: -D = -sum_c dO * O, head-major rows (workspace)
+  float* lsec;  // per query row: -LSE / tau, head-major rows (workspace)
+  float* sentinel;  // 64 x -inf then 64 x 0 (workspace): row values past a segment's end
   const SegDev* segs;
   Queues kvq;             // dK/dV queues
   Queues dqq;             // dQ queues

@@ -253,9 +253,10 @@ zl_status zl_plan_merge(const zl_plan* plan, const float* o_part, const float* l
  *   dq             fp32 [q_rows][d]: overwritten for every covered row; a KV-split group
  *                  gets the sum over its parts
  *   dk, dv         fp32 [kv_rows][d]: overwritten for every covered row
- *   workspace      device memory of info.ws_bwd bytes (queue counters and row dot products),
- *                  not shared with a concurrent call
- * Rows that no segment covers are left untouched. Pointers must be 16-B aligned.
+ *   workspace      device memory of info.ws_bwd bytes (queue counters, per-row -D and
+ *                  -LSE / tau, sentinel rows), not shared with a concurrent call
+ * Rows that no segment covers are left untouched. Pointers must be 16-B aligned. Plans with
+ * more than 2^29 query rows are rejected (ZL_ERR_UNSUPPORTED).
  */
 zl_status zl_attn_bwd(const zl_plan* plan, const void* q, const void* k, const void* v,
                       const float* o, const float* lse, const void* d_o,
