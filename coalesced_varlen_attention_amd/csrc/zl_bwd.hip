@@ -174,6 +174,14 @@ __device__ __forceinline__ void kv_dma_rows(uint32_t rows_lds, const BwdParams& 
   lds_dma4(rows_lds + wave * kBwdRows * 4, base, off);
 }
 
+// acc += a b with the accumulator in AGPRs (inline assembly pins the register class: the dK and
+// dV accumulators are only ever read by MFMAs, so they need no arch VGPRs). The compiler does not
+// see this MFMA's latency: readers of acc outside MFMAs must wait (kv_acc_settle).
+__device__ __forceinline__ void mfma32_acc(bf16x8 a, bf16x8 b, f32x16& acc) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void kv_acc_settle() { asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory"); }
+
 // Operand reads of the key-major kernel (offsets in bytes within a stage's tile).
 template <int D>
 __device__ __forceinline__ bf16x8 kv_row_op(ZL_LDS const char* tile, const int (&rbase)[4], int mb, int st) {
@@ -281,9 +289,9 @@ __device__ __forceinline__ void kv_grads(ZL_LDS const char* qt, ZL_LDS const cha
       next[m + 2 - kM] = kv_tr_op<D>((m + 2 - kM) & 1 ? qt : dot, tbase, 1, 0, 0);
     const int hs = (m >> 1) / C::kCb, cb = (m >> 1) % C::kCb;
     if (m & 1)
-      dk_acc[cb] = mfma32(op[m], dsb[hs], dk_acc[cb]);
+      mfma32_acc(op[m], dsb[hs], dk_acc[cb]);
     else
-      dv_acc[cb] = mfma32(op[m], pb[hs], dv_acc[cb]);
+      mfma32_acc(op[m], pb[hs], dv_acc[cb]);
     if (kValu) {
 #pragma unroll
       for (int u = 0; u < 16 / kM; ++u) {
@@ -463,6 +471,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
     }
 
     // dK = tau dK^T, dV = dV^T, written once: lane = key, 4 consecutive columns per store.
+    kv_acc_settle();
     if (k_valid) {
       const int64_t row = kp0 + (int64_t)ktok * tstr + h;
       float* dkr = p.dk + row * D;
