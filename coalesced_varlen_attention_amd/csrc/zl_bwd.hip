@@ -176,9 +176,11 @@ __device__ __forceinline__ void kv_dma_rows(uint32_t rows_lds, const BwdParams& 
 
 // acc += a b with the accumulator in AGPRs (inline assembly pins the register class: the dK and
 // dV accumulators are only ever read by MFMAs, so they need no arch VGPRs). The compiler does not
-// see this MFMA's latency: readers of acc outside MFMAs must wait (kv_acc_settle).
+// see into the assembly, so it keeps neither of the MFMA's hazards: a vector write of a or b needs
+// two wait states before the MFMA reads it (the s_nop 1), and readers of acc outside MFMAs must
+// wait for it (kv_acc_settle).
 __device__ __forceinline__ void mfma32_acc(bf16x8 a, bf16x8 b, f32x16& acc) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void kv_acc_settle() { asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory"); }
 

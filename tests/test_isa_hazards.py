@@ -43,24 +43,32 @@ def _vgprs(operand):
     return {int(m.group(1))} if m else set()
 
 
+def _wait_states(instr):
+    m = re.fullmatch(r"s_nop (\d+)", instr)
+    return int(m.group(1)) + 1 if m else 1
+
+
 def test_inline_mfma_operands_are_not_written_just_before(asm_lines):
+    """Walk back from every inline-assembly MFMA until two wait states have passed (an
+    instruction counts one, s_nop N counts N + 1); no vector instruction in that window may
+    write the MFMA's A or B operand registers."""
     n_checked = 0
     for i, line in enumerate(asm_lines):
         t = _instr(line)
-        if not t or not t.startswith("v_mfma") or ";;#ASMSTART" not in asm_lines[i - 1]:
+        if not t or not t.startswith("v_mfma") or not any(";;#ASMSTART" in asm_lines[k] for k in (i - 1, i - 2)):
             continue
         ops = [o.strip() for o in t.split(None, 1)[1].split(",")]
         src = _vgprs(ops[1]) | _vgprs(ops[2])
-        prev, k = [], i - 2
-        while len(prev) < 2 and k >= 0:
+        waited, k = 0, i - 1
+        while waited < 2 and k >= 0:
             p = _instr(asm_lines[k])
-            if p and not p.startswith(";;#ASM"):
-                prev.append(p)
             k -= 1
-        for p in prev:
+            if not p or p.startswith(";;#ASM"):
+                continue
             if p.startswith("v_") and not p.startswith("v_mfma"):
                 dst = p.split(None, 1)[1].split(",")[0].strip()
-                assert not (_vgprs(dst) & src), f"VALU write right before an inline MFMA: {p!r} -> {t!r}"
+                assert not (_vgprs(dst) & src), f"VALU write too close before an inline MFMA: {p!r} -> {t!r}"
+            waited += _wait_states(p)
         n_checked += 1
     assert n_checked >= 32, "expected the dK/dV inline MFMAs in the assembly"
 
