@@ -138,3 +138,16 @@ def test_full_size(name):
         assert not torch.isnan(out[n]).any(), f"{n}: a covered row was not written"
     _check_invariants(pack, out, ins["do"].to(out["o"].device))
     _check_sampled(pack, ins, out, seed=pack.seed)
+
+
+def test_full_size_d64():
+    """d_head 64 at scale: 4 x 8192 tokens at 8 heads and one 32,760-token sequence at 2 heads,
+    in the benchmark's launch configuration, checked on sampled rows like the packs above."""
+    pack = W.whole_pack("wide64", [8192] * 4 + [32760], [8] * 4 + [2], 64, 9)
+    print(f"[case] wide64: {len(pack.segments)} segments, q rows {pack.q_rows()}", flush=True)
+    ins = W.draw(pack)
+    out = H.run_pack(pack, ins)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert not torch.isnan(out[n]).any(), f"{n}: a covered row was not written"
+    _check_invariants(pack, out, ins["do"].to(out["o"].device))
+    _check_sampled(pack, ins, out, seed=pack.seed)
