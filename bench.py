@@ -9,7 +9,10 @@ FLOPs follow the metric's convention: 4*Lq*Lkv*d per (segment, head) forward, 2.
 backward. Prints one JSON line; with --json-out also writes it to a file.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixed] [--no-cpu-baseline] [--ring-fold]
-                    [--no-split]
+                    [--no-split] [--graph]
+
+With --graph the step is captured once in a HIP graph and the K timed steps are replays of
+it (per-kernel times still come from event-bracketed eager steps run before them).
     python bench.py --price-table [--price-reps R] [--json-out FILE]
 """
 from __future__ import annotations
@@ -226,6 +229,8 @@ def main() -> int:
     ap.add_argument("--price-table", action="store_true",
                     help="print per-rank attention prices for every bucket x placement option (one JSON line each)")
     ap.add_argument("--price-reps", type=int, default=3)
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured in a HIP graph (launch-bound packs)")
     args = ap.parse_args()
     if args.calibrate_copy:
         return calibrate_copy()
@@ -315,6 +320,22 @@ def main() -> int:
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    if args.graph:
+        # Capture on a side stream (the library launches on the current stream, which the
+        # capture makes the side stream), then time replays on the default stream.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
     avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in events) / args.steps
     fwd_ms, merge_ms, pre_ms, dkdv_ms, dq_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4), avg(4, 5)
     bwd_ms = pre_ms + dkdv_ms + dq_ms
@@ -351,6 +372,7 @@ def main() -> int:
                        "fwd_ms": round(fwd_ms, 3), "merge_ms": round(merge_ms, 3), "bwd_ms": round(bwd_ms, 3),
                        "bwd_pre_ms": round(pre_ms, 3), "bwd_dkdv_ms": round(dkdv_ms, 3), "bwd_dq_ms": round(dq_ms, 3),
                        "plan_build_ms": round(plan_ms, 2), "parallelism": "none (1 GPU)",
+                       "launch": "HIP graph replay" if args.graph else "eager",
                        "ring_forward": (f"running merge, {len(fold_plans)} launches" if fold_plans
                                         else "partials + LSE merge" if has_groups else "none"),
                        "split_kv": {"fwd_items_split": info["split_tiles"], "pieces": info["split_pieces"]}},
