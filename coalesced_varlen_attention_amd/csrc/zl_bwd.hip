@@ -353,7 +353,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   for (;;) {
     if (tid == 0) s_item = take_item(p.kvq, home, drained);
     __syncthreads();
-    const int item = s_item;
+    const int item = __builtin_amdgcn_readfirstlane(s_item);  // the same for every lane
     if (item < 0) break;
     const Tile tile = p.kvq.items[item];
     const SegDev sg = p.segs[tile.seg];
@@ -497,7 +497,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
 
 template <int D>
 struct DqCfg {
-  static constexpr int kThreads = 256;
+  static constexpr int kWaves = kDqWaves;                 // 32 query rows each
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int kBk = kBwdRows;                    // keys per block (64)
   static constexpr int kSteps = D / 16;
   static constexpr int kCb = D / 32;
@@ -505,6 +506,9 @@ struct DqCfg {
   // bank conflicts): K is read by rows (S^T = K Q^T) and transposed (dQ^T = K^T dS^T), V by rows.
   static constexpr int kTileBytes = KvCfg<D>::kTileBytes;
   static constexpr int kStageBytes = 2 * kTileBytes;
+  static constexpr int kGroups = kBk / KvCfg<D>::kGroupRows;  // 1 KB row groups per tile
+  static constexpr int kDma = kGroups / kWaves;               // K (and V) loads per thread per block
+  static_assert(kDma >= 1 && kDma * kWaves == kGroups, "the waves share each block's loads evenly");
 };
 
 // Global -> LDS loads of one key block: rows [0, 64) after `kblk` / `vblk` (the block's first
@@ -513,18 +517,19 @@ template <int D>
 __device__ __forceinline__ void dq_dma(uint32_t stage, const char* kblk, const char* vblk, int64_t rs_bytes, int rows,
                                        uint32_t lane_off, int lane_row, int lane_col, int wave) {
   using L = KvCfg<D>;
+  using C = DqCfg<D>;
   if (rows >= L::kBq) {
 #pragma unroll
-    for (int i = 0; i < L::kDma; ++i) {
-      const int grp = i * 4 + wave;
+    for (int i = 0; i < C::kDma; ++i) {
+      const int grp = i * C::kWaves + wave;
       const int64_t off = (int64_t)grp * L::kGroupRows * rs_bytes;
       lds_dma16(stage + grp * L::kPitch, kblk + off, lane_off);
       lds_dma16(stage + L::kTileBytes + grp * L::kPitch, vblk + off, lane_off);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < L::kDma; ++i) {
-      const int grp = i * 4 + wave;
+    for (int i = 0; i < C::kDma; ++i) {
+      const int grp = i * C::kWaves + wave;
       const int row = min(grp * L::kGroupRows + lane_row, rows - 1);
       const uint32_t off = (uint32_t)row * (uint32_t)rs_bytes + lane_col;
       lds_dma16(stage + grp * L::kPitch, kblk, off);
@@ -622,7 +627,7 @@ __device__ __forceinline__ void dq_mask(f32x16& s, int vr) {
 }
 
 template <int D, bool kPacked>
-__global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const BwdParams p) {
   using C = DqCfg<D>;
   using L = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
@@ -662,7 +667,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
   for (;;) {
     if (tid == 0) s_item = take_item(p.dqq, home, drained);
     __syncthreads();
-    const int item = s_item;
+    const int item = __builtin_amdgcn_readfirstlane(s_item);  // the same for every lane
     if (item < 0) break;
     const Tile tile = p.dqq.items[item];
     const SegDev sg = p.segs[tile.seg];
@@ -674,8 +679,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
     const int voff = qr.v_off;
     const int64_t rs_bytes = (int64_t)tstr * D * 2;
     const uint32_t lane_off = (uint32_t)dma_row * (uint32_t)rs_bytes + dma_col;
-    const char* kseq = (const char*)p.k + (kp0 + h) * D * 2;
-    const char* vseq = (const char*)p.v + (kp0 + voff + h) * D * 2;
+    const char* kseq = uniform_ptr((const char*)p.k + (kp0 + h) * D * 2);
+    const char* vseq = uniform_ptr((const char*)p.v + (kp0 + voff + h) * D * 2);
 
     int n_blk = 0;
     for (int r = 0; r < sg.chain_len; ++r) {
@@ -761,9 +766,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const BwdParams p) {
 }
 
 template <typename K>
-int occupancy(K kernel) {
+int occupancy(K kernel, int threads) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess) n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) n = 0;
   return n;
 }
 
@@ -772,14 +777,15 @@ int occupancy(K kernel) {
 int bwd_blocks_per_cu(int d) {
   static int c64 = -1, c128 = -1;
   int& c = d == 64 ? c64 : c128;
-  if (c < 0) c = d == 64 ? occupancy(dkdv_kernel<64, false>) : occupancy(dkdv_kernel<128, false>);
+  if (c < 0) c = d == 64 ? occupancy(dkdv_kernel<64, false>, 256) : occupancy(dkdv_kernel<128, false>, 256);
   return c;
 }
 
 int dq_blocks_per_cu(int d) {
   static int c64 = -1, c128 = -1;
   int& c = d == 64 ? c64 : c128;
-  if (c < 0) c = d == 64 ? occupancy(dq_kernel<64, false>) : occupancy(dq_kernel<128, false>);
+  if (c < 0)
+    c = d == 64 ? occupancy(dq_kernel<64, false>, DqCfg<64>::kThreads) : occupancy(dq_kernel<128, false>, DqCfg<128>::kThreads);
   return c;
 }
 
@@ -787,7 +793,7 @@ template <int D, bool kPacked>
 void launch_bwd_impl(const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages, hipStream_t s) {
   if (stages & ZL_BWD_PRE) hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(grid_pre), dim3(256), 0, s, p);
   if (stages & ZL_BWD_DKDV) hipLaunchKernelGGL((dkdv_kernel<D, kPacked>), dim3(grid), dim3(256), 0, s, p);
-  if (stages & ZL_BWD_DQ) hipLaunchKernelGGL((dq_kernel<D, kPacked>), dim3(grid_dq), dim3(256), 0, s, p);
+  if (stages & ZL_BWD_DQ) hipLaunchKernelGGL((dq_kernel<D, kPacked>), dim3(grid_dq), dim3(DqCfg<D>::kThreads), 0, s, p);
 }
 
 int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages, void* stream) {

@@ -86,6 +86,16 @@ struct LdsTile {
 };
 __device__ __forceinline__ int lds_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// A pointer that every lane of the wave holds, moved to scalar registers (the compiler cannot
+// always prove that a value loaded from memory is the same in every lane).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
 // Direct global -> LDS load of 16 bytes per lane: lane l reads base + off (off per lane) and
 // its bytes land at lds_base + 16 l (base and lds_base are the same for the whole wave).
 // Issued as inline assembly so that the compiler does not order later LDS reads of other

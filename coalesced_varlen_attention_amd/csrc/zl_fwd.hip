@@ -447,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   for (;;) {
     if (tid == 0) s_item = take_item(p.queue, home, drained);
     __syncthreads();
-    const int item = s_item;
+    const int item = __builtin_amdgcn_readfirstlane(s_item);  // the same for every lane
     if (item < 0) break;
     const Tile tile = p.queue.items[item];
     const SegDev sg = p.segs[tile.seg];

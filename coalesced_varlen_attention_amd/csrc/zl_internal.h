@@ -12,9 +12,11 @@ namespace zl {
 
 // Forward queue item: 128 query rows of one (segment, head). Backward dK/dV queue item: 128
 // key rows of one (segment, head), looping over the segment's query rows in blocks of 64.
-// Backward dQ queue item: 128 query rows of one (final segment or ring group, head), looping
-// over every key range of the segment (all parts of a ring group).
+// Backward dQ queue item: kDqRows query rows of one (final segment or ring group, head),
+// looping over every key range of the segment (all parts of a ring group).
 constexpr int kFwdRows = 128;
+constexpr int kDqWaves = 4;                // waves per dQ workgroup, 32 query rows each
+constexpr int kDqRows = 32 * kDqWaves;
 constexpr int kFwdKeys = 64;  // keys per forward step
 // Split-KV of forward items (short queues leave compute units idle): a plan whose forward
 // queue holds fewer than kSplitWaves waves of items for the device's resident workgroups cuts

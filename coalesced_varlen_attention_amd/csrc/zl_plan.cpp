@@ -387,11 +387,13 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
         const int32_t n = (int32_t)std::min<int64_t>(zl::kFwdRows, g.q_end - r);
         fwd.push_back({{i, h, (int32_t)r, n, g.kv_begin, g.kv_end, -1, 1 << 16}, (int64_t)n * nk});
         fwd_unit.push_back(unit);
-        if (g.part <= 0) {
+      }
+      if (g.part <= 0)
+        for (int64_t r = g.q_begin; r < g.q_end; r += zl::kDqRows) {
+          const int32_t n = (int32_t)std::min<int64_t>(zl::kDqRows, g.q_end - r);
           dq.push_back({{i, h, (int32_t)r, n, g.kv_begin, g.kv_end, -1, 1 << 16}, (int64_t)n * chain_keys});
           dq_unit.push_back(unit);
         }
-      }
       for (int64_t r = g.kv_begin; r < g.kv_end; r += zl::kBwdKeys) {
         const int32_t n = (int32_t)std::min<int64_t>(zl::kBwdKeys, g.kv_end - r);
         bwd.push_back({{i, h, (int32_t)r, n, (int32_t)r, (int32_t)r + n, -1, 1 << 16}, (int64_t)n * nq});

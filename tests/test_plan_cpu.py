@@ -106,12 +106,15 @@ def test_queue_keeps_heads_together():
 
 @pytest.mark.parametrize("name", ["tiny", "mixed", "ring"])
 def test_dq_queue(name):
-    """One dQ item per (final segment or ring group, head, 128 query rows), in decreasing cost
-    (rows x keys of the whole group) order; a ring group's items name its part-0 segment."""
+    """One dQ item per (final segment or ring group, head, block of query rows), in decreasing
+    cost (rows x keys of the whole group) order; a ring group's items name its part-0 segment.
+    Every pack here has a segment longer than a block, so the largest item is one block."""
     pack = W.config(name)
     p = host_plan(pack)
     tiles = p.tiles(2)
     assert p.info["dq_tiles"] == len(tiles)
+    block = max(t[3] for t in tiles)
+    assert block in (128, 256)
     owners = [i for i, s in enumerate(pack.segments) if s[7] <= 0]
     keys_of = {}
     for i in owners:
@@ -124,10 +127,10 @@ def test_dq_queue(name):
     for (seg, h, r0, n) in tiles:
         assert seg in keys_of
         s = pack.segments[seg]
-        assert s[1] <= h < s[2] and s[3] <= r0 and r0 + n <= s[4] and (r0 - s[3]) % 128 == 0
+        assert s[1] <= h < s[2] and s[3] <= r0 and r0 + n <= s[4] and (r0 - s[3]) % block == 0
         seen.add((seg, h, r0))
     assert len(seen) == len(tiles) == sum((pack.segments[i][2] - pack.segments[i][1]) *
-                                          -(-(pack.segments[i][4] - pack.segments[i][3]) // 128) for i in owners)
+                                          -(-(pack.segments[i][4] - pack.segments[i][3]) // block) for i in owners)
     costs = [t[3] * keys_of[t[0]] for t in tiles]
     bounds = p.queues(2)
     assert bounds[-1] == len(tiles)
