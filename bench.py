@@ -9,10 +9,11 @@ FLOPs follow the metric's convention: 4*Lq*Lkv*d per (segment, head) forward, 2.
 backward. Prints one JSON line; with --json-out also writes it to a file.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixed] [--no-cpu-baseline] [--ring-fold]
-                    [--no-split] [--graph]
+                    [--no-split] [--graph] [--power]
 
 With --graph the step is captured once in a HIP graph and the K timed steps are replays of
-it (per-kernel times still come from event-bracketed eager steps run before them).
+it (per-kernel times still come from event-bracketed eager steps run before them). With --power
+the host samples socket power and graphics clocks (amd-smi) while the queued timed steps run.
     python bench.py --price-table [--price-reps R] [--json-out FILE]
 """
 from __future__ import annotations
@@ -213,11 +214,37 @@ def price_table(reps: int, out_path) -> int:
     return 0
 
 
+def sample_power(done_event, period_s: float = 0.5) -> dict:
+    """Socket power and graphics clocks from `amd-smi metric -p -c --json`, sampled until
+    `done_event` has completed (the GPU runs the queued steps meanwhile)."""
+    import subprocess
+    watts, mhz, n = [], [], 0
+    while not done_event.query() and n < 200:
+        n += 1
+        try:
+            out = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                                 timeout=10).stdout
+            gpu = json.loads(out[out.index("{"):])["gpu_data"][0]
+            watts.append(float(gpu["power"]["socket_power"]["value"]))
+            clk = [float(v["clk"]["value"]) for k, v in gpu["clock"].items()
+                   if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+            if clk:
+                mhz.append(sum(clk) / len(clk))
+        except Exception:
+            pass
+        time.sleep(period_s)
+    if not watts:
+        return {"samples": 0}
+    return {"samples": len(watts), "socket_w_mean": round(sum(watts) / len(watts), 1), "socket_w_max": max(watts),
+            "gfx_mhz_mean": round(sum(mhz) / len(mhz), 1) if mhz else None,
+            "source": "amd-smi metric -p -c, sampled during the timed steps"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="mixed", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
@@ -231,6 +258,8 @@ def main() -> int:
     ap.add_argument("--price-reps", type=int, default=3)
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured in a HIP graph (launch-bound packs)")
+    ap.add_argument("--power", action="store_true",
+                    help="sample socket power and graphics clocks (amd-smi) while the timed steps run")
     args = ap.parse_args()
     if args.calibrate_copy:
         return calibrate_copy()
@@ -318,6 +347,8 @@ def main() -> int:
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
+    # The steps are queued; the host samples power and clocks until the last one has finished.
+    smi = sample_power(events[-1][5]) if args.power else None
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     if args.graph:
@@ -337,6 +368,7 @@ def main() -> int:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
     avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in events) / args.steps
+    per_step = sorted(e[0].elapsed_time(e[5]) for e in events)
     fwd_ms, merge_ms, pre_ms, dkdv_ms, dq_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4), avg(4, 5)
     bwd_ms = pre_ms + dkdv_ms + dq_ms
     ms_per_step = wall * 1e3 / args.steps
@@ -373,10 +405,14 @@ def main() -> int:
                        "bwd_pre_ms": round(pre_ms, 3), "bwd_dkdv_ms": round(dkdv_ms, 3), "bwd_dq_ms": round(dq_ms, 3),
                        "plan_build_ms": round(plan_ms, 2), "parallelism": "none (1 GPU)",
                        "launch": "HIP graph replay" if args.graph else "eager",
+                       "step_ms_events": {"median": round(per_step[len(per_step) // 2], 3),
+                                          "min": round(per_step[0], 3), "max": round(per_step[-1], 3)},
                        "ring_forward": (f"running merge, {len(fold_plans)} launches" if fold_plans
                                         else "partials + LSE merge" if has_groups else "none"),
                        "split_kv": {"fwd_items_split": info["split_tiles"], "pieces": info["split_pieces"]}},
             "roofline": roof}
+    if smi is not None:
+        line["config"]["power"] = smi
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pack, ins)
     text = json.dumps(line)
