@@ -554,19 +554,21 @@ __device__ __forceinline__ void chain_block(const int32_t* ranges, int off, int 
   }
 }
 
-// dS^T = exp2(S^T tau log2e - LSE log2e) (dP^T - D) of element e of a tile (lane = query row).
-__device__ __forceinline__ float dq_ds(float s, float dp, float scale_log2, float lse2, float dd) {
-  return fast_exp2(fmaf(s, scale_log2, -lse2)) * (dp - dd);
+// dS^T = exp2(S^T tau log2e - LSE log2e) (dP^T - D) of element e of a tile (lane = query row);
+// `dpd` is dP^T - D (the dP^T accumulator starts at -D).
+__device__ __forceinline__ float dq_ds(float s, float dpd, float scale_log2, float lse2) {
+  return fast_exp2(fmaf(s, scale_log2, -lse2)) * dpd;
 }
 
-// S^T and dP^T of one 32-key half of a block (16 MFMAs, alternating), operands two MFMAs ahead;
-// with kValu, the dS^T of the other half (one element per MFMA, rounded per 8) in the slots.
+// S^T and dP^T - D of one 32-key half of a block (16 MFMAs, alternating; the dP^T chain starts
+// from `negd`, this lane's -D in every element), operands two MFMAs ahead; with kValu, the dS^T
+// of the other half (one element per MFMA, rounded per 8) in the slots.
 template <int D, bool kValu>
 __device__ __forceinline__ void dq_scores(ZL_LDS const char* kt, ZL_LDS const char* vt, const int (&rbase)[4], int kb,
                                           const bf16x8 (&qreg)[DqCfg<D>::kSteps],
                                           const bf16x8 (&doreg)[DqCfg<D>::kSteps], f32x16& sacc, f32x16& dpacc,
-                                          const f32x16& s_o, const f32x16& dp_o, float scale_log2, float lse2, float dd,
-                                          bf16x8 (&dsb)[2]) {
+                                          const f32x16& s_o, const f32x16& dp_o, const f32x16& negd,
+                                          float scale_log2, float lse2, bf16x8 (&dsb)[2]) {
   using C = DqCfg<D>;
   constexpr int kM = 2 * C::kSteps;
   bf16x8 op[kM];
@@ -577,14 +579,14 @@ __device__ __forceinline__ void dq_scores(ZL_LDS const char* kt, ZL_LDS const ch
   for (int m = 0; m < kM; ++m) {
     if (m + 2 < kM) op[m + 2] = kv_row_op<D>((m + 2) & 1 ? vt : kt, rbase, kb, (m + 2) >> 1);
     if (m & 1)
-      dpacc = mfma32(op[m], doreg[m >> 1], m == 1 ? f32x16{} : dpacc);
+      dpacc = mfma32(op[m], doreg[m >> 1], m == 1 ? negd : dpacc);
     else
       sacc = mfma32(op[m], qreg[m >> 1], m == 0 ? f32x16{} : sacc);
     if (kValu) {
 #pragma unroll
       for (int u = 0; u < 16 / kM; ++u) {
         const int e = m * (16 / kM) + u;
-        x[e % 8] = dq_ds(s_o[e], dp_o[e], scale_log2, lse2, dd);
+        x[e % 8] = dq_ds(s_o[e], dp_o[e], scale_log2, lse2);
         if (e % 8 == 7) dsb[e / 8] = to_bf16x8(x);
       }
     }
@@ -596,8 +598,7 @@ __device__ __forceinline__ void dq_scores(ZL_LDS const char* kt, ZL_LDS const ch
 template <int D, bool kValu>
 __device__ __forceinline__ void dq_grads(ZL_LDS const char* kt, const int (&tbase)[DqCfg<D>::kCb], int kb,
                                          const bf16x8 (&dsb)[2], f32x16 (&acc)[DqCfg<D>::kCb], const f32x16& s_o,
-                                         const f32x16& dp_o, float scale_log2, float lse2, float dd,
-                                         bf16x8 (&dsb_o)[2]) {
+                                         const f32x16& dp_o, float scale_log2, float lse2, bf16x8 (&dsb_o)[2]) {
   using C = DqCfg<D>;
   constexpr int kM = 2 * C::kCb;
   bf16x8 op[kM];
@@ -612,7 +613,7 @@ __device__ __forceinline__ void dq_grads(ZL_LDS const char* kt, const int (&tbas
 #pragma unroll
       for (int u = 0; u < 16 / kM; ++u) {
         const int e = m * (16 / kM) + u;
-        x[e % 8] = dq_ds(s_o[e], dp_o[e], scale_log2, lse2, dd);
+        x[e % 8] = dq_ds(s_o[e], dp_o[e], scale_log2, lse2);
         if (e % 8 == 7) dsb_o[e / 8] = to_bf16x8(x);
       }
     }
@@ -709,7 +710,9 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
     }
     const int64_t hm = sg.q_row0 + (int64_t)h * sg.lq + qtok;
     const float lse2 = -p.lsec[hm] * p.scale_log2;  // LSE log2(e)
-    const float dd = -p.dneg[hm];                     // D
+    f32x16 negd;                                      // -D in every element
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negd[i] = p.dneg[hm];
 
     f32x16 acc[C::kCb];
 #pragma unroll
@@ -737,15 +740,15 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
       // C: dQ of half 0 with dS of half 1 | D: dQ of half 1.
       f32x16 s0, dp0, s1, dp1;
       bf16x8 dsb0[2], dsb1[2];
-      dq_scores<D, false>(kt, vt, rbase, 0, qreg, doreg, s0, dp0, s1, dp1, p.scale_log2, lse2, dd, dsb1);
+      dq_scores<D, false>(kt, vt, rbase, 0, qreg, doreg, s0, dp0, s1, dp1, negd, p.scale_log2, lse2, dsb1);
       if (valid < C::kBk) dq_mask(s0, valid - 4 * hi);
       __builtin_amdgcn_sched_barrier(0);
-      dq_scores<D, true>(kt, vt, rbase, 1, qreg, doreg, s1, dp1, s0, dp0, p.scale_log2, lse2, dd, dsb0);
+      dq_scores<D, true>(kt, vt, rbase, 1, qreg, doreg, s1, dp1, s0, dp0, negd, p.scale_log2, lse2, dsb0);
       if (valid < C::kBk) dq_mask(s1, valid - 32 - 4 * hi);
       __builtin_amdgcn_sched_barrier(0);
-      dq_grads<D, true>(kt, tbase, 0, dsb0, acc, s1, dp1, p.scale_log2, lse2, dd, dsb1);
+      dq_grads<D, true>(kt, tbase, 0, dsb0, acc, s1, dp1, p.scale_log2, lse2, dsb1);
       __builtin_amdgcn_sched_barrier(0);
-      dq_grads<D, false>(kt, tbase, 1, dsb1, acc, s1, dp1, p.scale_log2, lse2, dd, dsb0);
+      dq_grads<D, false>(kt, tbase, 1, dsb1, acc, s1, dp1, p.scale_log2, lse2, dsb0);
       __builtin_amdgcn_sched_barrier(0);
       dma_wait();
       __syncthreads();
