@@ -538,21 +538,25 @@ __device__ __forceinline__ void dq_dma(uint32_t stage, const char* kblk, const c
   }
 }
 
-// Block j of a key-range chain: the range it lies in and its first key within the range.
-__device__ __forceinline__ void chain_block(const int32_t* ranges, int off, int len, int j, int bk, int* kv0,
-                                            int* n_kv, int* key0) {
-  for (int r = 0; r < len; ++r) {
-    const int b = ranges[2 * (off + r)], e = ranges[2 * (off + r) + 1];
-    const int nb = (e - b + bk - 1) / bk;
-    if (j < nb || r == len - 1) {
-      *kv0 = b;
-      *n_kv = e - b;
-      *key0 = j * bk;
-      return;
-    }
-    j -= nb;
+// Walk over the 64-key blocks of a key-range chain (one range, or the parts of a ring group in
+// order): the current range [kv0, kv0 + n_kv) and the block's first key within it. Range bounds
+// are read only when the walk enters a range, so the block loop issues no other memory reads.
+struct ChainWalk {
+  const int32_t* ranges;  // [begin, end) pairs of the chain
+  int r, kv0, n_kv, key0;
+
+  __device__ __forceinline__ void enter(int rr) {
+    r = rr;
+    kv0 = __builtin_amdgcn_readfirstlane(ranges[2 * rr]);
+    n_kv = __builtin_amdgcn_readfirstlane(ranges[2 * rr + 1]) - kv0;
+    key0 = 0;
   }
-}
+  // The next block; the caller guarantees that one exists (ranges are never empty).
+  __device__ __forceinline__ void next(int bk) {
+    key0 += bk;
+    if (key0 >= n_kv) enter(r + 1);
+  }
+};
 
 // dS^T = exp2(S^T tau log2e - LSE log2e) (dP^T - D) of element e of a tile (lane = query row);
 // `dpd` is dP^T - D (the dP^T accumulator starts at -D).
@@ -688,11 +692,12 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
       const int len = p.kv_ranges[2 * (sg.chain_off + r) + 1] - p.kv_ranges[2 * (sg.chain_off + r)];
       n_blk += (len + C::kBk - 1) / C::kBk;
     }
-    int kv0, n_kv, key0;
-    chain_block(p.kv_ranges, sg.chain_off, sg.chain_len, 0, C::kBk, &kv0, &n_kv, &key0);
+    ChainWalk cw;
+    cw.ranges = p.kv_ranges + 2 * sg.chain_off;
+    cw.enter(0);
     {
-      const int64_t off = (int64_t)(kv0 + key0) * rs_bytes;
-      dq_dma<D>(lds0, kseq + off, vseq + off, rs_bytes, n_kv - key0, lane_off, dma_row, dma_col, wave_u);
+      const int64_t off = (int64_t)cw.kv0 * rs_bytes;
+      dq_dma<D>(lds0, kseq + off, vseq + off, rs_bytes, cw.n_kv, lane_off, dma_row, dma_col, wave_u);
     }
 
     // This lane's query row (clamped; results of clamped rows are dropped), with its Q and dO
@@ -722,12 +727,12 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
 
     for (int j = 0; j < n_blk; ++j) {
       const uint32_t cur = lds0 + (j & 1) * C::kStageBytes;
-      const int valid = n_kv - key0;  // keys of this block inside its range
+      const int valid = cw.n_kv - cw.key0;  // keys of this block inside its range
       if (j + 1 < n_blk) {
-        chain_block(p.kv_ranges, sg.chain_off, sg.chain_len, j + 1, C::kBk, &kv0, &n_kv, &key0);
-        const int64_t off = (int64_t)(kv0 + key0) * rs_bytes;
-        dq_dma<D>(lds0 + ((j + 1) & 1) * C::kStageBytes, kseq + off, vseq + off, rs_bytes, n_kv - key0, lane_off,
-                  dma_row, dma_col, wave_u);
+        cw.next(C::kBk);
+        const int64_t off = (int64_t)(cw.kv0 + cw.key0) * rs_bytes;
+        dq_dma<D>(lds0 + ((j + 1) & 1) * C::kStageBytes, kseq + off, vseq + off, rs_bytes, cw.n_kv - cw.key0,
+                  lane_off, dma_row, dma_col, wave_u);
       }
       ZL_LDS const char* kt = (ZL_LDS const char*)cur;
       ZL_LDS const char* vt = (ZL_LDS const char*)(cur + C::kTileBytes);
