@@ -409,7 +409,8 @@ def main() -> int:
                                           "min": round(per_step[0], 3), "max": round(per_step[-1], 3)},
                        "ring_forward": (f"running merge, {len(fold_plans)} launches" if fold_plans
                                         else "partials + LSE merge" if has_groups else "none"),
-                       "split_kv": {"fwd_items_split": info["split_tiles"], "pieces": info["split_pieces"]}},
+                       "split_kv": {"fwd_items_split": info["split_tiles"], "pieces": info["split_pieces"],
+                                    "dq_items_split": info["dq_split_tiles"], "dq_pieces": info["dq_split_pieces"]}},
             "roofline": roof}
     if smi is not None:
         line["config"]["power"] = smi

@@ -46,7 +46,8 @@ class _PlanInfo(ctypes.Structure):
                 ("n_parts_max", ctypes.c_int32), ("fwd_tiles", ctypes.c_int64), ("bwd_tiles", ctypes.c_int64),
                 ("fwd_flops", ctypes.c_double), ("bwd_flops", ctypes.c_double), ("d_head", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("dq_tiles", ctypes.c_int64), ("split_tiles", ctypes.c_int32),
-                ("split_pieces", ctypes.c_int32), ("qkv_rows", ctypes.c_int64)]
+                ("split_pieces", ctypes.c_int32), ("qkv_rows", ctypes.c_int64),
+                ("dq_split_tiles", ctypes.c_int32), ("dq_split_pieces", ctypes.c_int32)]
 
 
 class _GroupInfo(ctypes.Structure):
@@ -159,8 +160,9 @@ class Plan:
 
     def tiles(self, which: int) -> List[Tuple[int, ...]]:
         """Work queue items (segment, head, first row, rows): 0 forward, 1 backward dK/dV, 2 backward dQ;
-        3 forward with (key begin, key end, split slot, piece | pieces << 16) appended."""
-        w = 8 if which == 3 else 4
+        3 forward with (key begin, key end, split slot, piece | pieces << 16) appended; 4 dQ with
+        (first block, end block of the key-block chain, split slot, piece | pieces << 16) appended."""
+        w = 8 if which >= 3 else 4
         cnt = ctypes.c_int64()
         _check(lib().zl_plan_tiles(self._h, which, None, 0, ctypes.byref(cnt)))
         buf = (ctypes.c_int32 * (w * cnt.value))()

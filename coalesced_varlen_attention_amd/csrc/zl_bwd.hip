@@ -45,6 +45,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
     p.dqq.counters[threadIdx.x * kCounterStride] = 0;
   }
   if (blockIdx.x == 0 && threadIdx.x < 2 * kBwdRows) p.sentinel[threadIdx.x] = threadIdx.x < kBwdRows ? -INFINITY : 0.f;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < p.n_dq_split; j += gridDim.x * blockDim.x)
+    p.dq_split_cnt[j] = 0;  // pieces finished per split dQ item
   const float neg_inv_tau = -1.0f / p.scale;
   constexpr int kPer = D / 16;  // elements per lane
   const int sub = threadIdx.x & 15;
@@ -637,6 +639,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
   using L = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
   __shared__ int32_t s_item;
+  __shared__ int32_t s_last;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(ZL_LDS char*)smem;
 
   const int tid = threadIdx.x;
@@ -687,17 +690,23 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
     const char* kseq = uniform_ptr((const char*)p.k + (kp0 + h) * D * 2);
     const char* vseq = uniform_ptr((const char*)p.v + (kp0 + voff + h) * D * 2);
 
-    int n_blk = 0;
-    for (int r = 0; r < sg.chain_len; ++r) {
-      const int len = p.kv_ranges[2 * (sg.chain_off + r) + 1] - p.kv_ranges[2 * (sg.chain_off + r)];
-      n_blk += (len + C::kBk - 1) / C::kBk;
-    }
+    // The item's key blocks [kv_begin, kv_end) of the chain: all of them, or one piece's run.
+    const int n_blk = tile.kv_end - tile.kv_begin;
     ChainWalk cw;
     cw.ranges = p.kv_ranges + 2 * sg.chain_off;
     cw.enter(0);
+    for (int b = tile.kv_begin;;) {
+      const int nb = (cw.n_kv + C::kBk - 1) / C::kBk;
+      if (b < nb) {
+        cw.key0 = b * C::kBk;
+        break;
+      }
+      b -= nb;
+      cw.enter(cw.r + 1);
+    }
     {
-      const int64_t off = (int64_t)cw.kv0 * rs_bytes;
-      dq_dma<D>(lds0, kseq + off, vseq + off, rs_bytes, cw.n_kv, lane_off, dma_row, dma_col, wave_u);
+      const int64_t off = (int64_t)(cw.kv0 + cw.key0) * rs_bytes;
+      dq_dma<D>(lds0, kseq + off, vseq + off, rs_bytes, cw.n_kv - cw.key0, lane_off, dma_row, dma_col, wave_u);
     }
 
     // This lane's query row (clamped; results of clamped rows are dropped), with its Q and dO
@@ -759,15 +768,61 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
       __syncthreads();
     }
 
-    if (q_valid) {
+    // dQ = tau dQ^T, written once: lane = query row, 4 consecutive columns per store. A piece of
+    // a split item publishes its scaled partial (device-coherent stores, as the forward's
+    // pieces do) and counts itself done; the last piece adds every piece's partial in piece
+    // order, its own included, and stores the item's rows.
+    float osc = p.scale;
+    bool store = true;
+    if (tile.split >= 0) {
+      const int n_pieces = tile.piece >> 16;
+      const int64_t slot = tile.split + (tile.piece & 0xffff);
+      if (q_valid) {
+        float* so = p.dq_split + (slot * kDqRows + qi) * D;
+#pragma unroll
+        for (int cb = 0; cb < C::kCb; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            store_dev16(so + cb * 32 + 8 * g + 4 * hi,
+                        f32x4{acc[cb][4 * g] * osc, acc[cb][4 * g + 1] * osc, acc[cb][4 * g + 2] * osc,
+                              acc[cb][4 * g + 3] * osc});
+      }
+      store_dev_wait();
+      __syncthreads();
+      if (tid == 0)
+        s_last = __hip_atomic_fetch_add(p.dq_split_cnt + tile.split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 n_pieces - 1;
+      __syncthreads();
+      store = s_last;
+      if (store && q_valid) {
+#pragma unroll
+        for (int cb = 0; cb < C::kCb; ++cb) acc[cb] = f32x16{};
+        for (int c = 0; c < n_pieces; ++c) {
+          const float* so = p.dq_split + (((int64_t)tile.split + c) * kDqRows + qi) * D + 4 * hi;
+          // this lane's D/2 values of the row: D/8 chunks of 16 bytes, 8 floats apart; chunk k
+          // holds (column block k/4, group k%4)
+          f32x4 x[D / 8];
+          if constexpr (D == 128)
+            load_dev16x16(so, x);
+          else
+            load_dev16x8(so, x);
+#pragma unroll
+          for (int k = 0; k < D / 8; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[k / 4][4 * (k % 4) + e] += x[k][e];
+        }
+        osc = 1.0f;
+      }
+    }
+    if (store && q_valid) {
       float* out = p.dq + qprow * D;
 #pragma unroll
       for (int cb = 0; cb < C::kCb; ++cb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int c = cb * 32 + 8 * g + 4 * hi;
-          *(f32x4*)(out + c) = f32x4{acc[cb][4 * g] * p.scale, acc[cb][4 * g + 1] * p.scale,
-                                     acc[cb][4 * g + 2] * p.scale, acc[cb][4 * g + 3] * p.scale};
+          *(f32x4*)(out + c) = f32x4{acc[cb][4 * g] * osc, acc[cb][4 * g + 1] * osc, acc[cb][4 * g + 2] * osc,
+                                     acc[cb][4 * g + 3] * osc};
         }
     }
   }

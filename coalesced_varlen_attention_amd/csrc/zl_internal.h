@@ -150,6 +150,9 @@ struct BwdParams {
   float scale;       // softmax scale
   float scale_log2;  // softmax scale times log2(e)
   int32_t packed;    // Q, K, V and their gradients in the QKV-packed layout (kernel instance)
+  int32_t n_dq_split;     // pieces of split dQ items (slots of dq_split_cnt, dq_split)
+  int32_t* dq_split_cnt;  // per split dQ item (at its piece-0 slot): pieces finished
+  float* dq_split;        // [n_dq_split][kDqRows][D] scaled partial dQ of each piece
 };
 
 // Kernel launchers (defined next to their kernels). They return the launch status.
@@ -187,6 +190,8 @@ struct zl_plan {
   int64_t merge_blocks = 0;  // total blocks of a plan merge launch
   int32_t split_tiles = 0;   // forward items cut into key pieces
   int32_t split_pieces = 0;  // pieces of those items (slots of the split workspace)
+  int32_t dq_split_tiles = 0;   // dQ items cut into pieces of their key-block chain
+  int32_t dq_split_pieces = 0;  // pieces of those items (slots of the backward split workspace)
   // device copies (one allocation, carved into the three tables)
   void* dev_block = nullptr;
   const zl::SegDev* d_segs = nullptr;

@@ -164,6 +164,50 @@ void split_forward(int64_t slots, std::vector<Item>* fwd, std::vector<int64_t>* 
   unit->swap(out_unit);
 }
 
+// Split-KV of the dQ queue, for the same reason: with fewer dQ items than resident dQ
+// workgroups, every item above the fair share is cut into pieces of its key-block chain (at
+// most kMaxPieces, each at least kMinPieceKeys keys). A piece's key range is a block range
+// [kv_begin, kv_end) of the chain; its partial dQ is a plain sum term (every piece uses the
+// final LSE), and the item's last piece to finish adds the pieces in order.
+void split_dq(int64_t slots, std::vector<Item>* dq, std::vector<int64_t>* unit, int32_t* n_tiles,
+              int32_t* n_pieces) {
+  *n_tiles = 0;
+  *n_pieces = 0;
+  if (dq->empty() || (int64_t)dq->size() >= (int64_t)zl::kSplitWaves * slots) return;
+  double total = 0.0;
+  for (const Item& it : *dq) total += (double)it.cost;
+  const double target = total / ((double)zl::kSplitTargetWaves * (double)slots);
+  std::vector<Item> out;
+  std::vector<int64_t> out_unit;
+  int64_t next = 0;
+  for (size_t j = 0; j < dq->size(); ++j) {
+    const Item& it = (*dq)[j];
+    const int64_t nb = it.t.kv_end - it.t.kv_begin;
+    int64_t n = (int64_t)std::llround((double)it.cost / target);
+    n = std::min<int64_t>(n, std::min<int64_t>(zl::kMaxPieces, nb * zl::kBwdRows / zl::kMinPieceKeys));
+    if (n < 2 || next + n > INT32_MAX) {
+      out.push_back(it);
+      out_unit.push_back((*unit)[j]);
+      continue;
+    }
+    for (int64_t pc = 0; pc < n; ++pc) {
+      Item x = it;
+      x.t.kv_begin = it.t.kv_begin + (int32_t)(nb * pc / n);
+      x.t.kv_end = it.t.kv_begin + (int32_t)(nb * (pc + 1) / n);
+      x.t.split = (int32_t)next;
+      x.t.piece = (int32_t)(pc | (n << 16));
+      x.cost = (int64_t)((double)it.cost * (double)(x.t.kv_end - x.t.kv_begin) / (double)nb);
+      out.push_back(x);
+      out_unit.push_back((*unit)[j]);
+    }
+    next += n;
+    ++*n_tiles;
+  }
+  *n_pieces = (int32_t)next;
+  dq->swap(out);
+  unit->swap(out_unit);
+}
+
 }  // namespace
 
 extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int64_t* cu_kv,
@@ -378,9 +422,13 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   for (int i = 0; i < n_seg; ++i) {
     const zl_segment& g = segs[i];
     const int64_t nq = g.q_end - g.q_begin, nk = g.kv_end - g.kv_begin;
-    int64_t chain_keys = 0;
-    for (int c = 0; c < plan->segs[i].chain_len; ++c)
-      chain_keys += plan->kv_ranges[2 * (plan->segs[i].chain_off + c) + 1] - plan->kv_ranges[2 * (plan->segs[i].chain_off + c)];
+    int64_t chain_keys = 0, chain_blocks = 0;
+    for (int c = 0; c < plan->segs[i].chain_len; ++c) {
+      const int64_t len =
+          plan->kv_ranges[2 * (plan->segs[i].chain_off + c) + 1] - plan->kv_ranges[2 * (plan->segs[i].chain_off + c)];
+      chain_keys += len;
+      chain_blocks += (len + zl::kBwdRows - 1) / zl::kBwdRows;
+    }
     for (int h = g.head_begin; h < g.head_end; ++h) {
       const int64_t unit = (int64_t)i * 65536 + h;
       for (int64_t r = g.q_begin; r < g.q_end; r += zl::kFwdRows) {
@@ -391,7 +439,8 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
       if (g.part <= 0)
         for (int64_t r = g.q_begin; r < g.q_end; r += zl::kDqRows) {
           const int32_t n = (int32_t)std::min<int64_t>(zl::kDqRows, g.q_end - r);
-          dq.push_back({{i, h, (int32_t)r, n, g.kv_begin, g.kv_end, -1, 1 << 16}, (int64_t)n * chain_keys});
+          // A dQ item's key range is its block range [0, chain_blocks) of the segment's chain.
+          dq.push_back({{i, h, (int32_t)r, n, 0, (int32_t)chain_blocks, -1, 1 << 16}, (int64_t)n * chain_keys});
           dq_unit.push_back(unit);
         }
       for (int64_t r = g.kv_begin; r < g.kv_end; r += zl::kBwdKeys) {
@@ -423,8 +472,16 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
       slots = (int64_t)plan->n_cu * per_cu;
     }
     split_forward(slots, &fwd, &fwd_unit, &plan->split_tiles, &plan->split_pieces);
+    int64_t dq_slots = zl::kHostOnlySlots;
+    if (!(flags & ZL_PLAN_HOST_ONLY)) {
+      const int per_cu = zl::dq_blocks_per_cu(d_head);
+      if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_plan_build: dQ kernel cannot be resident");
+      dq_slots = (int64_t)plan->n_cu * per_cu;
+    }
+    split_dq(dq_slots, &dq, &dq_unit, &plan->dq_split_tiles, &plan->dq_split_pieces);
   }
-  if (fwd.size() > (size_t)INT32_MAX || bwd.size() > (size_t)INT32_MAX || plan->pre_tiles.size() > (size_t)INT32_MAX)
+  if (fwd.size() > (size_t)INT32_MAX || bwd.size() > (size_t)INT32_MAX || dq.size() > (size_t)INT32_MAX ||
+      plan->pre_tiles.size() > (size_t)INT32_MAX)
     return fail(ZL_ERR_INVALID, "zl_plan_build: too many work items");
   distribute(fwd, fwd_unit, &plan->fwd_tiles, &plan->fwd_bounds);
   distribute(bwd, bwd_unit, &plan->bwd_tiles, &plan->bwd_bounds);

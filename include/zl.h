@@ -88,6 +88,8 @@ typedef struct {
   int32_t split_pieces;   /* pieces of those items */
   int64_t qkv_rows;       /* rows of the packed QKV (and dQKV) buffer: 3 * q_rows, or 0 unless
                              ZL_PLAN_QKV_PACKED */
+  int32_t dq_split_tiles;  /* dQ items cut into pieces of their key blocks (split-KV backward) */
+  int32_t dq_split_pieces; /* pieces of those items */
 } zl_plan_info_t;
 
 /*
@@ -113,7 +115,7 @@ typedef struct {
 /* Flags for zl_plan_build. */
 #define ZL_PLAN_HOST_ONLY 1u /* build and validate on the host only; no device tables, so the
                                 plan can be inspected but not run (used by CPU-only tests) */
-#define ZL_PLAN_NO_SPLIT 2u  /* never cut forward items into key pieces (see zl_plan_build) */
+#define ZL_PLAN_NO_SPLIT 2u  /* never cut forward or dQ items into key pieces (see zl_plan_build) */
 #define ZL_PLAN_QKV_PACKED 4u /* Q, K, V share one buffer, per sequence [tokens][Q, K, V][heads][d]
                                  (the layout of a QKV-packed all-to-all, §IV-D / Table II), and so
                                  do dQ, dK, dV; needs equal query and key lengths. Sequence s starts
@@ -145,8 +147,13 @@ typedef struct {
  * (the queue's total cost over the resident workgroups) is cut into block-aligned key pieces
  * of about that share (at most 16, each at least 1024 keys). Each piece is a normalised partial over its keys; the
  * last piece of an item to finish merges them exactly (the ring merge, §II-B) and stores the
- * item's result. ZL_PLAN_NO_SPLIT turns this off. The pieces' partials live in the forward
- * workspace, whose size grows accordingly (info.ws_fwd).
+ * item's result. The dQ queue is split the same way when it holds fewer items than there are
+ * resident dQ workgroups: a dQ item's keys are the 64-key blocks of its segment's key ranges
+ * (all parts of a ring group, in part order), and a piece takes a contiguous run of them. A
+ * piece's partial dQ is a plain sum term (every piece uses the final LSE); the last piece of
+ * an item to finish adds the pieces in piece order, so the result does not depend on which
+ * piece finishes last. ZL_PLAN_NO_SPLIT turns both off. The pieces' partials live in the
+ * forward and backward workspaces, whose sizes grow accordingly (info.ws_fwd, info.ws_bwd).
  */
 zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                         const int32_t* seq_heads, int32_t n_seg, const zl_segment* segs,
@@ -164,7 +171,9 @@ zl_status zl_plan_group(const zl_plan* plan, int32_t g, zl_group_info_t* info);
  * Each item is 4 int32: segment index, head, first row of the block, rows in the block.
  * which = 3 is the forward queue again with 8 int32 per item: the same 4, then the item's
  * key range [kv_begin, kv_end), the workspace slot of its piece 0 (-1 unless the item is a
- * piece of a split item) and its piece index | (pieces << 16).
+ * piece of a split item) and its piece index | (pieces << 16). which = 4 is the dQ queue with
+ * 8 int32 per item in the same form, the key range given as a range of 64-key blocks of the
+ * segment's key-range chain.
  * Writes min(cap, count) items to out (may be NULL when cap == 0); *count gets the total.
  */
 zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* out, int64_t cap, int64_t* count);
@@ -254,7 +263,8 @@ zl_status zl_plan_merge(const zl_plan* plan, const float* o_part, const float* l
  *                  gets the sum over its parts
  *   dk, dv         fp32 [kv_rows][d]: overwritten for every covered row
  *   workspace      device memory of info.ws_bwd bytes (queue counters, per-row -D and
- *                  -LSE / tau, sentinel rows), not shared with a concurrent call
+ *                  -LSE / tau, sentinel rows, split dQ partials), not shared with a
+ *                  concurrent call
  * Rows that no segment covers are left untouched. Pointers must be 16-B aligned. Plans with
  * more than 2^29 query rows are rejected (ZL_ERR_UNSUPPORTED).
  */

@@ -90,3 +90,54 @@ def test_split_running_merge(d):
     ref = H.oracle_pack(pack, ins)
     H.assert_close("O", H.f64(o), ref["o"])
     H.assert_close("LSE", H.f64(lse), ref["lse"])
+
+
+def _dq_split_run(pack):
+    ins = W.draw(pack)
+    print(f"[case] {pack.name} d={pack.d} seqs={pack.seq_q}/{pack.seq_kv} segs={len(pack.segments)}", flush=True)
+    out = H.run_pack(pack, ins)
+    assert out["plan"].info["dq_split_tiles"] > 0, "the dQ queue was meant to be split"
+    ref = H.oracle_pack(pack, ins)
+    H.compare_full(pack, ins, out, ref)
+    return out, ins
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dq_split_whole_sequence(d):
+    """One head of 5000 tokens: 40 dQ items, each cut into pieces of its 79 key blocks (the
+    last one ragged); the last piece of each item adds the pieces' partials."""
+    pack = W.Pack(f"dq_split{d}", (5000,), (5000,), (1,), ((0, 0, 1, 0, 5000, 0, 5000, -1),), d, 91 + d)
+    _dq_split_run(pack)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dq_split_ring_chain(d):
+    """A ring group of three uneven parts: the dQ items walk the parts' key blocks as one chain and
+    their pieces cut it across part boundaries (ragged blocks at every part's end)."""
+    seg = ((0, 0, 2, 0, 333, 0, 1900, 0), (0, 0, 2, 0, 333, 1900, 4100, 1), (0, 0, 2, 0, 333, 4100, 6000, 2))
+    _dq_split_run(W.Pack(f"dq_split_ring{d}", (333,), (6000,), (2,), seg, d, 95 + d))
+
+
+def test_dq_split_reproducible_and_close_to_unsplit():
+    """Pieces are added in piece order, so split dQ is bitwise the same on every run whatever
+    piece finishes last; it matches the unsplit plan's dQ within the oracle tolerance (the
+    summation order differs)."""
+    z = H.zl()
+    dev = torch.device("cuda:0")
+    pack = W.Pack("dq_split_repro", (3000,), (3000,), (2,), ((0, 0, 2, 0, 3000, 0, 3000, -1),), 128, 97)
+    ins = W.draw(pack)
+    q, k, v, do = (ins[n].to(dev) for n in ("q", "k", "v", "do"))
+    print("[case] dQ split: reproducible, close to unsplit", flush=True)
+    dqs = []
+    for split in (True, True, False):
+        plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, split=split)
+        assert (plan.info["dq_split_tiles"] > 0) == split
+        o, lse, _, _ = z.attn_fwd(plan, q, k, v)
+        dq, _, _ = z.attn_bwd(plan, q, k, v, o, lse, do)
+        dqs.append(dq)
+    torch.cuda.synchronize()
+    assert torch.equal(dqs[0], dqs[1]), "split dQ differs between two runs"
+    ref = H.oracle_pack(pack, ins)
+    for dq in dqs:
+        H.assert_close("dQ", H.f64(dq), ref["dq"])
+    H.assert_close("dQ split vs unsplit", H.f64(dqs[0]), H.f64(dqs[2]))

@@ -287,7 +287,7 @@ def test_split_kv_cuts_long_items_of_a_short_queue():
     assert nosplit.info["split_tiles"] == 0 and nosplit.info["fwd_tiles"] == 64
     extra = p.info["ws_fwd"] - nosplit.info["ws_fwd"]
     assert extra >= 512 * (4 + 128 * 128 * 4 + 128 * 4)
-    assert p.tiles(1) == nosplit.tiles(1) and p.tiles(2) == nosplit.tiles(2)  # backward untouched
+    assert p.tiles(1) == nosplit.tiles(1)  # the dK/dV queue is never split
 
 
 def test_split_kv_ragged_and_short_items():
@@ -319,3 +319,58 @@ def test_qkv_packed_plan():
     assert z.Plan((10, 6), (10, 6), (2, 3), seg, 64, host_only=True).info["qkv_rows"] == 0
     expect_error(ZL_ERR_INVALID, [10], [12], [2], [(0, 0, 2, 0, 10, 0, 12, -1)], match="equal query and key",
                  qkv_packed=True)
+
+
+def _dq_pieces(p):
+    """dQ queue (which = 4) grouped by item: (first block, end block, slot, piece, pieces)."""
+    items = {}
+    for (seg, h, r0, n, b0, b1, split, piece) in p.tiles(4):
+        items.setdefault((seg, h, r0, n), []).append((b0, b1, split, piece & 0xffff, piece >> 16))
+    return items
+
+
+def test_dq_split_cuts_items_of_a_short_queue():
+    """One head of 8192 tokens: 64 dQ items of 128 query rows over a chain of 128 key blocks, far
+    fewer than the 512 resident dQ workgroups assumed for a host-only plan: each item becomes 8
+    pieces of 16 blocks (1024 keys), contiguous, with one workspace slot per item."""
+    seg = ((0, 0, 1, 0, 8192, 0, 8192, -1),)
+    p = z.Plan((8192,), (8192,), (1,), seg, 128, host_only=True)
+    nosplit = z.Plan((8192,), (8192,), (1,), seg, 128, host_only=True, split=False)
+    assert p.info["dq_split_tiles"] == 64 and p.info["dq_split_pieces"] == 512 and p.info["dq_tiles"] == 512
+    assert nosplit.info["dq_split_tiles"] == 0 and nosplit.info["dq_tiles"] == 64
+    assert all(t[4:] == (0, 128, -1, 1 << 16) for t in nosplit.tiles(4))
+    items = _dq_pieces(p)
+    assert len(items) == 64
+    slots = set()
+    for key, pieces in items.items():
+        pieces.sort()
+        assert [x[3] for x in pieces] == list(range(8)) and all(x[4] == 8 for x in pieces)
+        assert pieces[0][0] == 0 and pieces[-1][1] == 128
+        assert all(a[1] == b[0] for a, b in zip(pieces[:-1], pieces[1:]))
+        assert all(x[1] - x[0] == 16 for x in pieces)
+        assert len({x[2] for x in pieces}) == 1
+        slots.add(pieces[0][2])
+    assert sorted(slots) == list(range(0, 512, 8))
+    # the workspace holds a counter and 128 rows of partial dQ per piece
+    assert p.info["ws_bwd"] - nosplit.info["ws_bwd"] >= 512 * (4 + 128 * 128 * 4)
+    # costs stay proportional to the keys: the queue still sorts by decreasing cost
+    t4 = p.tiles(4)
+    _per_queue_cost_order([(t[0], t[1], (t[2], t[4])) for t in t4], [t[3] * 64 * (t[5] - t[4]) for t in t4],
+                          p.queues(4))
+
+
+def test_dq_split_over_a_ring_chain():
+    """A ring group of 3 parts of 2000 keys: its dQ items walk a chain of 3 x 32 blocks, and the
+    pieces cut that chain into runs that may cross part boundaries; the 44-row tail item too."""
+    seg = tuple((0, 0, 1, 0, 300, 2000 * b, 2000 * (b + 1), b) for b in range(3))
+    p = z.Plan((300,), (6000,), (1,), seg, 64, host_only=True)
+    assert p.info["dq_split_tiles"] == 3
+    items = _dq_pieces(p)
+    assert sorted(k[2:] for k in items) == [(0, 128), (128, 128), (256, 44)]
+    for key, pieces in items.items():
+        pieces.sort()
+        n = pieces[0][4]
+        assert 2 <= n <= 96 * 64 // 1024 and len(pieces) == n
+        assert pieces[0][0] == 0 and pieces[-1][1] == 96
+        assert all(a[1] == b[0] for a, b in zip(pieces[:-1], pieces[1:]))
+        assert all(x[1] - x[0] >= 16 for x in pieces)
