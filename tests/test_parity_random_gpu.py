@@ -1,0 +1,32 @@
+"""HIP path vs the fp64 oracle on seeded random packs (see tests/random_packs.py): mixes of
+whole sequences, head subsets, query ranges and ring groups with uneven, out-of-order parts,
+ragged lengths at and around the tile sizes, d_head 64 and 128. Small packs leave the queues
+short, so these plans also cut forward and dQ items into pieces. Every covered row is checked
+element by element, ring partials included; uncovered rows must keep their NaN fill.
+
+Random shapes include many queries against a few keys, where a dV row sums over every query
+and reaches magnitudes of 10-20 (one pack: 88 queries, 2 keys, max |dV| = 17.8). The bf16
+rounding of P is relative to those magnitudes, so the max-abs bound is 2e-2 times the largest
+reference magnitude (at least 1), as for the stress inputs; the rel-L2 bound is unchanged.
+"""
+import pytest
+
+from tests import gpu_harness as H
+from tests import random_packs as R
+
+pytestmark = [pytest.mark.gpu, H.requires_gpu]
+
+
+@pytest.mark.parametrize("seed", R.SEEDS)
+def test_random_pack(seed):
+    pack = R.random_pack(seed)
+    import workloads as W
+    ins = W.draw(pack)
+    print(f"[case] {pack.name} d={pack.d} seqs={pack.seq_q}/{pack.seq_kv} heads={pack.heads} "
+          f"segs={pack.segments}", flush=True)
+    out = H.run_pack(pack, ins)
+    info = out["plan"].info
+    print(f"  split: fwd {info['split_tiles']} items / {info['split_pieces']} pieces, "
+          f"dQ {info['dq_split_tiles']} items / {info['dq_split_pieces']} pieces", flush=True)
+    ref = H.oracle_pack(pack, ins)
+    H.compare_full(pack, ins, out, ref, scaled_max_abs=True)

@@ -374,3 +374,17 @@ def test_dq_split_over_a_ring_chain():
         assert pieces[0][0] == 0 and pieces[-1][1] == 96
         assert all(a[1] == b[0] for a, b in zip(pieces[:-1], pieces[1:]))
         assert all(x[1] - x[0] >= 16 for x in pieces)
+
+
+def test_random_packs_build_valid_plans():
+    """Every seeded random pack of the GPU parity test is a valid segment list, and its queues
+    cover each (segment, head) block exactly once (host-only plans)."""
+    from tests import random_packs as R
+    for seed in R.SEEDS:
+        pack = R.random_pack(seed)
+        p = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, host_only=True)
+        assert p.info["q_rows"] == pack.q_rows() and p.info["kv_rows"] == pack.kv_rows()
+        n_fwd = sum((s[2] - s[1]) * -(-(s[4] - s[3]) // 128) for s in pack.segments)
+        assert len({t[:3] for t in p.tiles(0)}) == n_fwd
+        n_bwd = sum((s[2] - s[1]) * -(-(s[6] - s[5]) // 128) for s in pack.segments)
+        assert len(p.tiles(1)) == n_bwd
