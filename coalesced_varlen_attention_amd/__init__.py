@@ -47,7 +47,8 @@ class _PlanInfo(ctypes.Structure):
                 ("fwd_flops", ctypes.c_double), ("bwd_flops", ctypes.c_double), ("d_head", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("dq_tiles", ctypes.c_int64), ("split_tiles", ctypes.c_int32),
                 ("split_pieces", ctypes.c_int32), ("qkv_rows", ctypes.c_int64),
-                ("dq_split_tiles", ctypes.c_int32), ("dq_split_pieces", ctypes.c_int32)]
+                ("dq_split_tiles", ctypes.c_int32), ("dq_split_pieces", ctypes.c_int32),
+                ("kv_split_tiles", ctypes.c_int32), ("kv_split_pieces", ctypes.c_int32)]
 
 
 class _GroupInfo(ctypes.Structure):
@@ -161,7 +162,8 @@ class Plan:
     def tiles(self, which: int) -> List[Tuple[int, ...]]:
         """Work queue items (segment, head, first row, rows): 0 forward, 1 backward dK/dV, 2 backward dQ;
         3 forward with (key begin, key end, split slot, piece | pieces << 16) appended; 4 dQ with
-        (first block, end block of the key-block chain, split slot, piece | pieces << 16) appended."""
+        (first block, end block of the key-block chain, split slot, piece | pieces << 16) appended;
+        5 dK/dV in the same form over the segment's query blocks."""
         w = 8 if which >= 3 else 4
         cnt = ctypes.c_int64()
         _check(lib().zl_plan_tiles(self._h, which, None, 0, ctypes.byref(cnt)))

@@ -64,6 +64,14 @@ size_t dq_split_bytes(const zl_plan* plan) {
   return align256(n * sizeof(int32_t)) + align256(n * zl::kDqRows * plan->d * sizeof(float));
 }
 
+// Then, for split dK/dV items: one counter per piece slot, then each piece's partial tau dK and
+// dV rows.
+size_t kv_split_bytes(const zl_plan* plan) {
+  const size_t n = (size_t)plan->kv_split_pieces;
+  if (n == 0) return 0;
+  return align256(n * sizeof(int32_t)) + align256(n * zl::kBwdKeys * 2 * plan->d * sizeof(float));
+}
+
 size_t bwd_fixed_bytes(const zl_plan* plan) {
   return kCounterBytes + 2 * align256((size_t)plan->q_rows * sizeof(float)) + align256(kSentinelBytes);
 }
@@ -106,7 +114,7 @@ extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   if (!plan || !info) return fail(ZL_ERR_INVALID, "zl_plan_info: NULL argument");
   std::memset(info, 0, sizeof(*info));
   info->ws_fwd = kCounterBytes + split_bytes(plan);
-  info->ws_bwd = bwd_fixed_bytes(plan) + dq_split_bytes(plan);
+  info->ws_bwd = bwd_fixed_bytes(plan) + dq_split_bytes(plan) + kv_split_bytes(plan);
   info->q_rows = plan->q_rows;
   info->kv_rows = plan->kv_rows;
   info->qkv_rows = (plan->flags & ZL_PLAN_QKV_PACKED) ? 3 * plan->q_rows : 0;
@@ -124,6 +132,8 @@ extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   info->split_pieces = plan->split_pieces;
   info->dq_split_tiles = plan->dq_split_tiles;
   info->dq_split_pieces = plan->dq_split_pieces;
+  info->kv_split_tiles = plan->kv_split_tiles;
+  info->kv_split_pieces = plan->kv_split_pieces;
   return ZL_OK;
 }
 
@@ -137,8 +147,10 @@ extern "C" zl_status zl_plan_group(const zl_plan* plan, int32_t g, zl_group_info
 
 extern "C" zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* out, int64_t cap, int64_t* count) {
   if (!plan || !count) return fail(ZL_ERR_INVALID, "zl_plan_tiles: NULL argument");
-  if (which < 0 || which > 4) return fail(ZL_ERR_INVALID, "zl_plan_tiles: which must be 0 to 4");
-  const auto& v = which == 0 || which == 3 ? plan->fwd_tiles : which == 1 ? plan->bwd_tiles : plan->dq_tiles;
+  if (which < 0 || which > 5) return fail(ZL_ERR_INVALID, "zl_plan_tiles: which must be 0 to 5");
+  const auto& v = which == 0 || which == 3 ? plan->fwd_tiles
+                  : which == 1 || which == 5 ? plan->bwd_tiles
+                                             : plan->dq_tiles;
   const int w = which >= 3 ? 8 : 4;
   *count = (int64_t)v.size();
   if (cap < 0) return fail(ZL_ERR_INVALID, "zl_plan_tiles: negative capacity");
@@ -162,8 +174,10 @@ extern "C" zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* 
 extern "C" zl_status zl_plan_queues(const zl_plan* plan, int32_t which, int32_t* bounds, int32_t cap,
                                     int32_t* n_queues) {
   if (!plan || !n_queues) return fail(ZL_ERR_INVALID, "zl_plan_queues: NULL argument");
-  if (which < 0 || which > 4) return fail(ZL_ERR_INVALID, "zl_plan_queues: which must be 0 to 4");
-  const auto& b = which == 0 || which == 3 ? plan->fwd_bounds : which == 1 ? plan->bwd_bounds : plan->dq_bounds;
+  if (which < 0 || which > 5) return fail(ZL_ERR_INVALID, "zl_plan_queues: which must be 0 to 5");
+  const auto& b = which == 0 || which == 3 ? plan->fwd_bounds
+                  : which == 1 || which == 5 ? plan->bwd_bounds
+                                             : plan->dq_bounds;
   *n_queues = zl::kQueues;
   if (cap < 0 || (cap > 0 && !bounds)) return fail(ZL_ERR_INVALID, "zl_plan_queues: bad output buffer");
   for (int32_t i = 0; i < std::min<int32_t>(cap, (int32_t)b.size()); ++i) bounds[i] = b[i];
@@ -315,6 +329,12 @@ extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, cons
     char* base = (char*)workspace + bwd_fixed_bytes(plan);
     p.dq_split_cnt = (int32_t*)base;
     p.dq_split = (float*)(base + align256((size_t)p.n_dq_split * sizeof(int32_t)));
+  }
+  p.n_kv_split = plan->kv_split_pieces;
+  if (p.n_kv_split > 0) {
+    char* base = (char*)workspace + bwd_fixed_bytes(plan) + dq_split_bytes(plan);
+    p.kv_split_cnt = (int32_t*)base;
+    p.kv_split = (float*)(base + align256((size_t)p.n_kv_split * sizeof(int32_t)));
   }
   p.segs = plan->d_segs;
   p.pre_tiles = plan->d_pre;

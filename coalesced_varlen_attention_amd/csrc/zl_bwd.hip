@@ -47,6 +47,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
   if (blockIdx.x == 0 && threadIdx.x < 2 * kBwdRows) p.sentinel[threadIdx.x] = threadIdx.x < kBwdRows ? -INFINITY : 0.f;
   for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < p.n_dq_split; j += gridDim.x * blockDim.x)
     p.dq_split_cnt[j] = 0;  // pieces finished per split dQ item
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < p.n_kv_split; j += gridDim.x * blockDim.x)
+    p.kv_split_cnt[j] = 0;  // pieces finished per split dK/dV item
   const float neg_inv_tau = -1.0f / p.scale;
   constexpr int kPer = D / 16;  // elements per lane
   const int sub = threadIdx.x & 15;
@@ -317,6 +319,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[C::kStages * C::kStageBytes];
   __shared__ int32_t s_item;
+  __shared__ int32_t s_last;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(ZL_LDS char*)smem;
 
   const int tid = threadIdx.x;
@@ -377,7 +380,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
     dm.lane_col = dma_col;
     dm.lane_off = (uint32_t)dma_row * (uint32_t)dm.rs_bytes + dma_col;
     dm.lane_off_do = (uint32_t)dma_row * (uint32_t)dm.rs_do + dma_col;
-    const int nqb = (dm.n_q + C::kBq - 1) / C::kBq;
+    // The item's query blocks [qb0, qb1): all of the segment's, or one piece's run.
+    const int qb0 = tile.kv_begin, qb1 = tile.kv_end;
     const int64_t hmbase = sg.q_row0 + (int64_t)h * sg.lq + sg.q_begin;  // head-major row of local token 0
 
     // This wave's 32 keys in registers (B operands, lane = key column); clamped past the end.
@@ -404,11 +408,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
     // Steps 0 and 1 into stages 0 and 1, then wait for everything: the key registers must be
     // complete before the step loop in the compiler's own accounting too (the fake uses below),
     // or it would wait inside every step; waiting for step 1 as well costs once per item.
-    kv_dma<D>(dm, lds0, 0, wave_u);
-    kv_dma_rows(lds0 + 2 * C::kTileBytes, p, hmbase, 0, dm.n_q, wave_u, lane);
-    if (nqb > 1) {
-      kv_dma<D>(dm, lds0 + C::kStageBytes, 1, wave_u);
-      kv_dma_rows(lds0 + C::kStageBytes + 2 * C::kTileBytes, p, hmbase, 1, dm.n_q, wave_u, lane);
+    kv_dma<D>(dm, lds0, qb0, wave_u);
+    kv_dma_rows(lds0 + 2 * C::kTileBytes, p, hmbase, qb0, dm.n_q, wave_u, lane);
+    if (qb0 + 1 < qb1) {
+      kv_dma<D>(dm, lds0 + C::kStageBytes, qb0 + 1, wave_u);
+      kv_dma_rows(lds0 + C::kStageBytes + 2 * C::kTileBytes, p, hmbase, qb0 + 1, dm.n_q, wave_u, lane);
     }
     dma_wait();
 #pragma unroll
@@ -416,9 +420,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
     __syncthreads();
 
     uint32_t cur = lds0, ahead = lds0 + 2 * C::kStageBytes;  // stages of steps qb and qb + 2
-    for (int qb = 0; qb < nqb; ++qb) {
+    for (int qb = qb0; qb < qb1; ++qb) {
       // Step qb + 2 goes to the stage step qb - 1 read (every wave passed the barrier after it).
-      if (qb + 2 < nqb) {
+      if (qb + 2 < qb1) {
         kv_dma<D>(dm, ahead, qb + 2, wave_u);
         kv_dma_rows(ahead + 2 * C::kTileBytes, p, hmbase, qb + 2, dm.n_q, wave_u, lane);
       }
@@ -459,8 +463,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
       // Step qb + 1's loads (issued a step ago) have landed once only step qb + 2's are
       // outstanding.
-      if (qb + 1 < nqb) {
-        if (qb + 2 < nqb) {
+      if (qb + 1 < qb1) {
+        if (qb + 2 < qb1) {
           if (wave_u < 2)
             dma_wait_all_but<C::kDmaPerStep + 1>();
           else
@@ -474,9 +478,68 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
       ahead = ahead + C::kStageBytes == lds0 + C::kStages * C::kStageBytes ? lds0 : ahead + C::kStageBytes;
     }
 
-    // dK = tau dK^T, dV = dV^T, written once: lane = key, 4 consecutive columns per store.
+    // dK = tau dK^T, dV = dV^T, written once: lane = key, 4 consecutive columns per store. A
+    // piece of a split item publishes its partial tau dK and dV (device-coherent stores) and
+    // counts itself done; the last piece adds every piece's partial in piece order, its own
+    // included, and stores the item's rows.
     kv_acc_settle();
-    if (k_valid) {
+    float ksc = p.scale;
+    bool store = true;
+    if (tile.split >= 0) {
+      const int n_pieces = tile.piece >> 16;
+      const int64_t slot = tile.split + (tile.piece & 0xffff);
+      if (k_valid) {
+        float* sp = p.kv_split + (slot * kBwdKeys + key_local) * (2 * D);
+#pragma unroll
+        for (int cb = 0; cb < C::kCb; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = cb * 32 + 8 * g + 4 * hi;
+            store_dev16(sp + c, f32x4{dk_acc[cb][4 * g] * ksc, dk_acc[cb][4 * g + 1] * ksc,
+                                      dk_acc[cb][4 * g + 2] * ksc, dk_acc[cb][4 * g + 3] * ksc});
+            store_dev16(sp + D + c, f32x4{dv_acc[cb][4 * g], dv_acc[cb][4 * g + 1], dv_acc[cb][4 * g + 2],
+                                          dv_acc[cb][4 * g + 3]});
+          }
+      }
+      store_dev_wait();
+      __syncthreads();
+      if (tid == 0)
+        s_last = __hip_atomic_fetch_add(p.kv_split_cnt + tile.split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 n_pieces - 1;
+      __syncthreads();
+      store = s_last;
+      if (store && k_valid) {
+#pragma unroll
+        for (int cb = 0; cb < C::kCb; ++cb) {
+          dk_acc[cb] = f32x16{};
+          dv_acc[cb] = f32x16{};
+        }
+        for (int c = 0; c < n_pieces; ++c) {
+          const float* sp = p.kv_split + (((int64_t)tile.split + c) * kBwdKeys + key_local) * (2 * D) + 4 * hi;
+          // this lane's D/2 values of each row: D/8 chunks of 16 bytes, 8 floats apart; chunk k
+          // holds (column block k/4, group k%4)
+          f32x4 x[D / 8];
+          if constexpr (D == 128)
+            load_dev16x16(sp, x);
+          else
+            load_dev16x8(sp, x);
+#pragma unroll
+          for (int k = 0; k < D / 8; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dk_acc[k / 4][4 * (k % 4) + e] += x[k][e];
+          if constexpr (D == 128)
+            load_dev16x16(sp + D, x);
+          else
+            load_dev16x8(sp + D, x);
+#pragma unroll
+          for (int k = 0; k < D / 8; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dv_acc[k / 4][4 * (k % 4) + e] += x[k][e];
+        }
+        ksc = 1.0f;
+      }
+    }
+    if (store && k_valid) {
       const int64_t row = kp0 + (int64_t)ktok * tstr + h;
       float* dkr = p.dk + row * D;
       float* dvr = p.dv + (row + voff) * D;
@@ -485,8 +548,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int c = cb * 32 + 8 * g + 4 * hi;
-          *(f32x4*)(dkr + c) = f32x4{dk_acc[cb][4 * g] * p.scale, dk_acc[cb][4 * g + 1] * p.scale,
-                                     dk_acc[cb][4 * g + 2] * p.scale, dk_acc[cb][4 * g + 3] * p.scale};
+          *(f32x4*)(dkr + c) = f32x4{dk_acc[cb][4 * g] * ksc, dk_acc[cb][4 * g + 1] * ksc,
+                                     dk_acc[cb][4 * g + 2] * ksc, dk_acc[cb][4 * g + 3] * ksc};
           *(f32x4*)(dvr + c) = f32x4{dv_acc[cb][4 * g], dv_acc[cb][4 * g + 1], dv_acc[cb][4 * g + 2],
                                      dv_acc[cb][4 * g + 3]};
         }

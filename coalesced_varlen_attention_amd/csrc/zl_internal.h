@@ -30,8 +30,10 @@ constexpr int kSplitTargetWaves = 1;  // about one piece per resident workgroup:
                                       // costs a partial write and its share of a merge
 constexpr int kMaxPieces = 16;
 constexpr int kMinPieceKeys = 1024;
-// Resident forward workgroups assumed by a host-only plan (256 CUs x 2).
+// Resident workgroups assumed by a host-only plan: 256 CUs x 2 for the forward and dQ kernels,
+// x 1 for the dK/dV kernel.
 constexpr int kHostOnlySlots = 512;
+constexpr int kHostOnlyKvSlots = 256;
 constexpr int kBwdKeys = 128;
 constexpr int kBwdRows = 64;
 // Rows (token, head pairs) per item of the backward pre-pass.
@@ -153,6 +155,9 @@ struct BwdParams {
   int32_t n_dq_split;     // pieces of split dQ items (slots of dq_split_cnt, dq_split)
   int32_t* dq_split_cnt;  // per split dQ item (at its piece-0 slot): pieces finished
   float* dq_split;        // [n_dq_split][kDqRows][D] scaled partial dQ of each piece
+  int32_t n_kv_split;     // pieces of split dK/dV items (slots of kv_split_cnt, kv_split)
+  int32_t* kv_split_cnt;  // per split dK/dV item (at its piece-0 slot): pieces finished
+  float* kv_split;        // [n_kv_split][kBwdKeys][2][D] partial tau dK and dV of each piece
 };
 
 // Kernel launchers (defined next to their kernels). They return the launch status.
@@ -192,6 +197,8 @@ struct zl_plan {
   int32_t split_pieces = 0;  // pieces of those items (slots of the split workspace)
   int32_t dq_split_tiles = 0;   // dQ items cut into pieces of their key-block chain
   int32_t dq_split_pieces = 0;  // pieces of those items (slots of the backward split workspace)
+  int32_t kv_split_tiles = 0;   // dK/dV items cut into pieces of their query blocks
+  int32_t kv_split_pieces = 0;  // pieces of those items
   // device copies (one allocation, carved into the three tables)
   void* dev_block = nullptr;
   const zl::SegDev* d_segs = nullptr;

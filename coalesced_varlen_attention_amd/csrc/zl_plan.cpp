@@ -164,13 +164,14 @@ void split_forward(int64_t slots, std::vector<Item>* fwd, std::vector<int64_t>* 
   unit->swap(out_unit);
 }
 
-// Split-KV of the dQ queue, for the same reason: with fewer dQ items than resident dQ
-// workgroups, every item above the fair share is cut into pieces of its key-block chain (at
-// most kMaxPieces, each at least kMinPieceKeys keys). A piece's key range is a block range
-// [kv_begin, kv_end) of the chain; its partial dQ is a plain sum term (every piece uses the
-// final LSE), and the item's last piece to finish adds the pieces in order.
-void split_dq(int64_t slots, std::vector<Item>* dq, std::vector<int64_t>* unit, int32_t* n_tiles,
-              int32_t* n_pieces) {
+// Split of the backward queues, for the same reason: with fewer items than resident workgroups,
+// every item above the fair share is cut into pieces of the 64-row blocks it loops over (at most
+// kMaxPieces, each at least kMinPieceKeys rows). A dQ item loops over the key blocks of its
+// segment's key-range chain, a dK/dV item over its segment's query blocks; a piece is a run
+// [kv_begin, kv_end) of those blocks. Its partial gradient is a plain sum term (every piece uses
+// the final LSE and D), and the item's last piece to finish adds the pieces in order.
+void split_runs(int64_t slots, std::vector<Item>* dq, std::vector<int64_t>* unit, int32_t* n_tiles,
+                int32_t* n_pieces) {
   *n_tiles = 0;
   *n_pieces = 0;
   if (dq->empty() || (int64_t)dq->size() >= (int64_t)zl::kSplitWaves * slots) return;
@@ -445,7 +446,9 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
         }
       for (int64_t r = g.kv_begin; r < g.kv_end; r += zl::kBwdKeys) {
         const int32_t n = (int32_t)std::min<int64_t>(zl::kBwdKeys, g.kv_end - r);
-        bwd.push_back({{i, h, (int32_t)r, n, (int32_t)r, (int32_t)r + n, -1, 1 << 16}, (int64_t)n * nq});
+        // A dK/dV item's range is its run [0, query blocks) of the segment's 64-row query blocks.
+        bwd.push_back({{i, h, (int32_t)r, n, 0, (int32_t)((nq + zl::kBwdRows - 1) / zl::kBwdRows), -1, 1 << 16},
+                       (int64_t)n * nq});
         bwd_unit.push_back(unit);
       }
     }
@@ -478,7 +481,14 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
       if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_plan_build: dQ kernel cannot be resident");
       dq_slots = (int64_t)plan->n_cu * per_cu;
     }
-    split_dq(dq_slots, &dq, &dq_unit, &plan->dq_split_tiles, &plan->dq_split_pieces);
+    split_runs(dq_slots, &dq, &dq_unit, &plan->dq_split_tiles, &plan->dq_split_pieces);
+    int64_t kv_slots = zl::kHostOnlyKvSlots;
+    if (!(flags & ZL_PLAN_HOST_ONLY)) {
+      const int per_cu = zl::bwd_blocks_per_cu(d_head);
+      if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_plan_build: dK/dV kernel cannot be resident");
+      kv_slots = (int64_t)plan->n_cu * per_cu;
+    }
+    split_runs(kv_slots, &bwd, &bwd_unit, &plan->kv_split_tiles, &plan->kv_split_pieces);
   }
   if (fwd.size() > (size_t)INT32_MAX || bwd.size() > (size_t)INT32_MAX || dq.size() > (size_t)INT32_MAX ||
       plan->pre_tiles.size() > (size_t)INT32_MAX)

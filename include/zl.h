@@ -90,6 +90,8 @@ typedef struct {
                              ZL_PLAN_QKV_PACKED */
   int32_t dq_split_tiles;  /* dQ items cut into pieces of their key blocks (split-KV backward) */
   int32_t dq_split_pieces; /* pieces of those items */
+  int32_t kv_split_tiles;  /* dK/dV items cut into pieces of their query blocks */
+  int32_t kv_split_pieces; /* pieces of those items */
 } zl_plan_info_t;
 
 /*
@@ -115,7 +117,7 @@ typedef struct {
 /* Flags for zl_plan_build. */
 #define ZL_PLAN_HOST_ONLY 1u /* build and validate on the host only; no device tables, so the
                                 plan can be inspected but not run (used by CPU-only tests) */
-#define ZL_PLAN_NO_SPLIT 2u  /* never cut forward or dQ items into key pieces (see zl_plan_build) */
+#define ZL_PLAN_NO_SPLIT 2u  /* never cut work items into pieces (see zl_plan_build) */
 #define ZL_PLAN_QKV_PACKED 4u /* Q, K, V share one buffer, per sequence [tokens][Q, K, V][heads][d]
                                  (the layout of a QKV-packed all-to-all, §IV-D / Table II), and so
                                  do dQ, dK, dV; needs equal query and key lengths. Sequence s starts
@@ -147,13 +149,14 @@ typedef struct {
  * (the queue's total cost over the resident workgroups) is cut into block-aligned key pieces
  * of about that share (at most 16, each at least 1024 keys). Each piece is a normalised partial over its keys; the
  * last piece of an item to finish merges them exactly (the ring merge, §II-B) and stores the
- * item's result. The dQ queue is split the same way when it holds fewer items than there are
- * resident dQ workgroups: a dQ item's keys are the 64-key blocks of its segment's key ranges
- * (all parts of a ring group, in part order), and a piece takes a contiguous run of them. A
- * piece's partial dQ is a plain sum term (every piece uses the final LSE); the last piece of
- * an item to finish adds the pieces in piece order, so the result does not depend on which
- * piece finishes last. ZL_PLAN_NO_SPLIT turns both off. The pieces' partials live in the
- * forward and backward workspaces, whose sizes grow accordingly (info.ws_fwd, info.ws_bwd).
+ * item's result. The backward queues are split the same way when they hold fewer items than
+ * there are resident workgroups of their kernel: a dQ item loops over the 64-key blocks of its
+ * segment's key ranges (all parts of a ring group, in part order), a dK/dV item over the
+ * segment's 64-row query blocks, and a piece takes a contiguous run of those blocks. A piece's
+ * partial gradient is a plain sum term (every piece uses the final LSE and D); the last piece
+ * of an item to finish adds the pieces in piece order, so the result does not depend on which
+ * piece finishes last. ZL_PLAN_NO_SPLIT turns all of this off. The pieces' partials live in
+ * the forward and backward workspaces, whose sizes grow accordingly (info.ws_fwd, info.ws_bwd).
  */
 zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                         const int32_t* seq_heads, int32_t n_seg, const zl_segment* segs,
@@ -173,7 +176,8 @@ zl_status zl_plan_group(const zl_plan* plan, int32_t g, zl_group_info_t* info);
  * key range [kv_begin, kv_end), the workspace slot of its piece 0 (-1 unless the item is a
  * piece of a split item) and its piece index | (pieces << 16). which = 4 is the dQ queue with
  * 8 int32 per item in the same form, the key range given as a range of 64-key blocks of the
- * segment's key-range chain.
+ * segment's key-range chain; which = 5 is the dK/dV queue in the same form, the range given as
+ * a range of the segment's 64-row query blocks.
  * Writes min(cap, count) items to out (may be NULL when cap == 0); *count gets the total.
  */
 zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* out, int64_t cap, int64_t* count);
@@ -263,8 +267,8 @@ zl_status zl_plan_merge(const zl_plan* plan, const float* o_part, const float* l
  *                  gets the sum over its parts
  *   dk, dv         fp32 [kv_rows][d]: overwritten for every covered row
  *   workspace      device memory of info.ws_bwd bytes (queue counters, per-row -D and
- *                  -LSE / tau, sentinel rows, split dQ partials), not shared with a
- *                  concurrent call
+ *                  -LSE / tau, sentinel rows, split dQ and dK/dV partials), not shared
+ *                  with a concurrent call
  * Rows that no segment covers are left untouched. Pointers must be 16-B aligned. Plans with
  * more than 2^29 query rows are rejected (ZL_ERR_UNSUPPORTED).
  */

@@ -119,8 +119,8 @@ def test_dq_split_ring_chain(d):
 
 
 def test_dq_split_reproducible_and_close_to_unsplit():
-    """Pieces are added in piece order, so split dQ is bitwise the same on every run whatever
-    piece finishes last; it matches the unsplit plan's dQ within the oracle tolerance (the
+    """Pieces are added in piece order, so split dQ, dK and dV are bitwise the same on every run
+    whatever piece finishes last; they match the unsplit plan's within the oracle tolerance (the
     summation order differs)."""
     z = H.zl()
     dev = torch.device("cuda:0")
@@ -128,16 +128,30 @@ def test_dq_split_reproducible_and_close_to_unsplit():
     ins = W.draw(pack)
     q, k, v, do = (ins[n].to(dev) for n in ("q", "k", "v", "do"))
     print("[case] dQ split: reproducible, close to unsplit", flush=True)
-    dqs = []
+    grads = []
     for split in (True, True, False):
         plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, split=split)
-        assert (plan.info["dq_split_tiles"] > 0) == split
+        assert (plan.info["dq_split_tiles"] > 0) == split and (plan.info["kv_split_tiles"] > 0) == split
         o, lse, _, _ = z.attn_fwd(plan, q, k, v)
-        dq, _, _ = z.attn_bwd(plan, q, k, v, o, lse, do)
-        dqs.append(dq)
+        grads.append(z.attn_bwd(plan, q, k, v, o, lse, do))
     torch.cuda.synchronize()
-    assert torch.equal(dqs[0], dqs[1]), "split dQ differs between two runs"
     ref = H.oracle_pack(pack, ins)
-    for dq in dqs:
-        H.assert_close("dQ", H.f64(dq), ref["dq"])
-    H.assert_close("dQ split vs unsplit", H.f64(dqs[0]), H.f64(dqs[2]))
+    for i, name in enumerate(("dq", "dk", "dv")):
+        assert torch.equal(grads[0][i], grads[1][i]), f"split {name} differs between two runs"
+        for g in grads:
+            H.assert_close(name, H.f64(g[i]), ref[name])
+        H.assert_close(f"{name} split vs unsplit", H.f64(grads[0][i]), H.f64(grads[2][i]))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dkdv_split_many_queries(d):
+    """Few keys, many queries: the dK/dV items (128 keys each) loop over 47 query blocks of 64
+    rows (the last one ragged) and are cut into runs of them; the last piece of each item adds
+    the partial dK and dV. dV sums over 3000 queries, so its magnitude is well above 1 and the
+    max-abs bound scales with it (rel-L2 unchanged)."""
+    pack = W.Pack(f"kv_split{d}", (3000,), (500,), (2,), ((0, 0, 2, 0, 3000, 0, 500, -1),), d, 101 + d)
+    ins = W.draw(pack)
+    print(f"[case] {pack.name} d={pack.d} seqs={pack.seq_q}/{pack.seq_kv}", flush=True)
+    out = H.run_pack(pack, ins)
+    assert out["plan"].info["kv_split_tiles"] > 0, "the dK/dV queue was meant to be split"
+    H.compare_full(pack, ins, out, H.oracle_pack(pack, ins), scaled_max_abs=True)

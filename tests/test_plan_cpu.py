@@ -287,7 +287,6 @@ def test_split_kv_cuts_long_items_of_a_short_queue():
     assert nosplit.info["split_tiles"] == 0 and nosplit.info["fwd_tiles"] == 64
     extra = p.info["ws_fwd"] - nosplit.info["ws_fwd"]
     assert extra >= 512 * (4 + 128 * 128 * 4 + 128 * 4)
-    assert p.tiles(1) == nosplit.tiles(1)  # the dK/dV queue is never split
 
 
 def test_split_kv_ragged_and_short_items():
@@ -387,4 +386,33 @@ def test_random_packs_build_valid_plans():
         n_fwd = sum((s[2] - s[1]) * -(-(s[4] - s[3]) // 128) for s in pack.segments)
         assert len({t[:3] for t in p.tiles(0)}) == n_fwd
         n_bwd = sum((s[2] - s[1]) * -(-(s[6] - s[5]) // 128) for s in pack.segments)
-        assert len(p.tiles(1)) == n_bwd
+        assert len({t[:3] for t in p.tiles(1)}) == n_bwd
+
+
+def test_dkdv_split_cuts_items_of_a_short_queue():
+    """One head of 8192 tokens: 64 dK/dV items of 128 keys over 128 query blocks of 64 rows, fewer
+    than the 256 resident dK/dV workgroups assumed for a host-only plan (one per CU): each item
+    becomes 4 pieces of 32 query blocks with one workspace slot per item; the unsplit plan's
+    items span all 128 blocks."""
+    seg = ((0, 0, 1, 0, 8192, 0, 8192, -1),)
+    p = z.Plan((8192,), (8192,), (1,), seg, 128, host_only=True)
+    nosplit = z.Plan((8192,), (8192,), (1,), seg, 128, host_only=True, split=False)
+    assert p.info["kv_split_tiles"] == 64 and p.info["kv_split_pieces"] == 256 and p.info["bwd_tiles"] == 256
+    assert nosplit.info["kv_split_tiles"] == 0 and nosplit.info["bwd_tiles"] == 64
+    assert all(t[4:] == (0, 128, -1, 1 << 16) for t in nosplit.tiles(5))
+    items = {}
+    for (seg_, h, r0, n, b0, b1, split, piece) in p.tiles(5):
+        items.setdefault((seg_, h, r0, n), []).append((b0, b1, split, piece & 0xffff, piece >> 16))
+    assert len(items) == 64
+    slots = set()
+    for key, pieces in items.items():
+        pieces.sort()
+        assert [x[3] for x in pieces] == list(range(4)) and all(x[4] == 4 for x in pieces)
+        assert pieces[0][0] == 0 and pieces[-1][1] == 128
+        assert all(a[1] == b[0] for a, b in zip(pieces[:-1], pieces[1:]))
+        assert len({x[2] for x in pieces}) == 1
+        slots.add(pieces[0][2])
+    assert sorted(slots) == list(range(0, 256, 4))
+    # a counter and 128 keys x (dK, dV) rows of partials per piece
+    assert p.info["ws_bwd"] - nosplit.info["ws_bwd"] >= 256 * (4 + 128 * 2 * 128 * 4)
+    assert sorted(t[:4] for t in nosplit.tiles(1)) == sorted(set(t[:4] for t in p.tiles(1)))
