@@ -9,8 +9,8 @@
 //
 // Pre-pass: -D and -LSE / tau for every covered query row, stored head-major (row
 //   q_row0 + h * Lq + t of the sequence) so that the key-major kernel loads the 64 rows of a
-//   step as one contiguous 256-byte run; both queue counters zeroed; the sentinel rows
-//   (-inf, 0) that stand in for rows past a segment's end written.
+//   step as one contiguous 256-byte run; both queue counters and the split-item counters
+//   zeroed; the sentinel rows (-inf, 0) that stand in for rows past a segment's end written.
 // dK/dV kernel: one item = 128 key rows of one (segment, head); 4 waves x 32 keys. Each wave
 //   keeps its K and V rows in registers as B operands of S = Q K^T and dP = dO V^T (lane = one
 //   key column), so P and dS come out of the MFMA already in the B-operand layout of
@@ -24,8 +24,13 @@
 //   query rows, the forward's shape: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers
 //   (lane = one query row, whose LSE and D are then per-lane scalars), and
 //   dQ^T += K^T dS^T with K^T from transposed LDS reads. K and V blocks reach LDS by direct
-//   global-to-LDS loads in the key-major kernel's layout, one block ahead. dQ is written
-//   once: no atomics.
+//   global-to-LDS loads in the key-major kernel's layout, one block ahead, walking the chain
+//   of the segment's key ranges (all parts of a ring group). dQ is written once: no atomics.
+// Split items (short queues): an item of either kernel may cover only a run of the blocks it
+//   loops over (query blocks for dK/dV, key blocks for dQ). Each piece stores its partial
+//   gradient rows to the workspace with device-coherent stores and counts itself done; the
+//   last piece to finish adds all pieces' partials in piece order and writes the rows, so the
+//   result does not depend on which piece finished last.
 //   Computing dQ in its own query-major pass costs S and dP a second time, but fp32 atomics
 //   into dQ from every key block were measured to cost more than the whole key-major pass.
 #include "zl_device.hpp"
