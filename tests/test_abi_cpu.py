@@ -1,4 +1,5 @@
-"""CPU-side checks of the C ABI: the library loads and exports every symbol zl.h declares."""
+"""CPU-side checks of the C ABI: the library loads and exports every symbol zl.h declares, and the
+binding's ctypes structs have the header's layout."""
 import ctypes
 import os
 import re
@@ -29,3 +30,34 @@ def test_library_exports_every_declared_symbol():
 
 def test_last_error_is_a_string():
     assert isinstance(z.lib().zl_last_error(), bytes)
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    """The ctypes mirrors of zl_segment, zl_plan_info_t and zl_group_info_t have the header's size
+    and field offsets (zl_plan_info fills sizeof(zl_plan_info_t) bytes of the caller's struct):
+    a C program compiled against include/zl.h prints them."""
+    import ctypes
+    import subprocess
+    import coalesced_varlen_attention_amd as z
+    structs = {"zl_segment": z._Segment, "zl_plan_info_t": z._PlanInfo, "zl_group_info_t": z._GroupInfo}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "zl.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(ROOT, "include")
+    subprocess.run(["gcc", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, stdout=subprocess.PIPE, text=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line:
+            cname, field, val = line.split()
+            got[(cname, field)] = int(val)
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), f"{cname}: size differs from the binding"
+        for field, _ in cls._fields_:
+            assert got[(cname, field)] == getattr(cls, field).offset, f"{cname}.{field}: offset differs"
