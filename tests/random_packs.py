@@ -57,4 +57,4 @@ def random_pack(seed: int) -> W.Pack:
     return W.Pack(f"random{seed}", tuple(seq_q), tuple(seq_kv), tuple(heads), tuple(segs), d, 1000 + seed)
 
 
-SEEDS = tuple(range(12))
+SEEDS = tuple(range(32))
