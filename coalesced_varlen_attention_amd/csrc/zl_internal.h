@@ -93,9 +93,11 @@ static_assert(sizeof(GroupDev) == 48, "GroupDev must stay 48 bytes");
 // Rows one merge workgroup (256 lanes, d/4 lanes per row) handles per pass.
 constexpr int merge_rows(int d) { return 256 / (d / 4); }
 
-// One work item: segment index, head, first row (token) of the block, rows in the block.
-// Forward items also carry their key range (the segment's, or a piece of it) and, for a
-// piece of a split item, the slot of its piece 0 (split, -1 otherwise) and
+// One work item: segment index, head, first row (token) of the block, rows in the block, and
+// the range it loops over: for a forward item its keys [kv_begin, kv_end) (the segment's, or a
+// piece of them); for a dQ item a run [kv_begin, kv_end) of the 64-key blocks of its segment's
+// key-range chain; for a dK/dV item a run of the segment's 64-row query blocks. A piece of a
+// split item carries the workspace slot of its piece 0 (split, -1 otherwise) and
 // piece = index | (pieces << 16).
 struct alignas(16) Tile {
   int32_t seg, head, row0, nrows;
