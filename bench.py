@@ -214,30 +214,46 @@ def price_table(reps: int, out_path) -> int:
     return 0
 
 
-def sample_power(done_event, period_s: float = 0.5) -> dict:
-    """Socket power and graphics clocks from `amd-smi metric -p -c --json`, sampled until
-    `done_event` has completed (the GPU runs the queued steps meanwhile)."""
+def start_power_sampler(period_s: float = 0.5):
+    """Sample socket power and graphics clocks (`amd-smi metric -p -c --json`) on a background
+    thread while the GPU runs the queued timed steps. Returns a function that stops the sampler
+    and summarises the samples; call it after the timed region, so that the region's wall clock
+    never waits for a sample in flight."""
     import subprocess
-    watts, mhz, n = [], [], 0
-    while not done_event.query() and n < 200:
-        n += 1
-        try:
-            out = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
-                                 timeout=10).stdout
-            gpu = json.loads(out[out.index("{"):])["gpu_data"][0]
-            watts.append(float(gpu["power"]["socket_power"]["value"]))
-            clk = [float(v["clk"]["value"]) for k, v in gpu["clock"].items()
-                   if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
-            if clk:
-                mhz.append(sum(clk) / len(clk))
-        except Exception:
-            pass
-        time.sleep(period_s)
-    if not watts:
-        return {"samples": 0}
-    return {"samples": len(watts), "socket_w_mean": round(sum(watts) / len(watts), 1), "socket_w_max": max(watts),
-            "gfx_mhz_mean": round(sum(mhz) / len(mhz), 1) if mhz else None,
-            "source": "amd-smi metric -p -c, sampled during the timed steps"}
+    import threading
+    watts, mhz = [], []
+    stop = threading.Event()
+
+    def run():
+        while not stop.is_set():
+            try:
+                out = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                                     timeout=10).stdout
+                gpu = json.loads(out[out.index("{"):])["gpu_data"][0]
+                w = float(gpu["power"]["socket_power"]["value"])
+                clk = [float(v["clk"]["value"]) for k, v in gpu["clock"].items()
+                       if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+                if not stop.is_set():  # a sample that ends after the timed steps is not theirs
+                    watts.append(w)
+                    if clk:
+                        mhz.append(sum(clk) / len(clk))
+            except Exception:
+                pass
+            stop.wait(period_s)
+
+    thread = threading.Thread(target=run, daemon=True)
+    thread.start()
+
+    def finish() -> dict:
+        stop.set()
+        thread.join(timeout=15)
+        if not watts:
+            return {"samples": 0}
+        return {"samples": len(watts), "socket_w_mean": round(sum(watts) / len(watts), 1), "socket_w_max": max(watts),
+                "gfx_mhz_mean": round(sum(mhz) / len(mhz), 1) if mhz else None,
+                "source": "amd-smi metric -p -c, sampled during the timed steps"}
+
+    return finish
 
 
 def main() -> int:
@@ -344,13 +360,13 @@ def main() -> int:
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    finish_power = start_power_sampler() if args.power else None
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
-    # The steps are queued; the host samples power and clocks until the last one has finished.
-    smi = sample_power(events[-1][5]) if args.power else None
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    smi = finish_power() if finish_power else None
     if args.graph:
         # Capture on a side stream (the library launches on the current stream, which the
         # capture makes the side stream), then time replays on the default stream.
@@ -410,7 +426,8 @@ def main() -> int:
                        "ring_forward": (f"running merge, {len(fold_plans)} launches" if fold_plans
                                         else "partials + LSE merge" if has_groups else "none"),
                        "split_kv": {"fwd_items_split": info["split_tiles"], "pieces": info["split_pieces"],
-                                    "dq_items_split": info["dq_split_tiles"], "dq_pieces": info["dq_split_pieces"]}},
+                                    "dq_items_split": info["dq_split_tiles"], "dq_pieces": info["dq_split_pieces"],
+                                    "dkdv_items_split": info["kv_split_tiles"], "dkdv_pieces": info["kv_split_pieces"]}},
             "roofline": roof}
     if smi is not None:
         line["config"]["power"] = smi
