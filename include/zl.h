@@ -189,7 +189,12 @@ zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* out, int64_
  */
 zl_status zl_plan_queues(const zl_plan* plan, int32_t which, int32_t* bounds, int32_t cap, int32_t* n_queues);
 
-/* Free a plan and its device tables. NULL is ignored. */
+/*
+ * Free a plan and its device tables. NULL is ignored. The tables are released with hipFree,
+ * which first waits for all work queued on the device (an implicit device synchronisation):
+ * a plan may be destroyed while launches that use it are still queued, but not while a
+ * stream of its device is being captured into a graph.
+ */
 void zl_plan_destroy(zl_plan* plan);
 
 /*
