@@ -905,19 +905,18 @@ int occupancy(K kernel, int threads) {
 
 }  // namespace
 
+// Resident workgroups per compute unit, queried once per kernel (function-local statics, so
+// concurrent first calls are safe); 0 if the query fails.
 int bwd_blocks_per_cu(int d) {
-  static int c64 = -1, c128 = -1;
-  int& c = d == 64 ? c64 : c128;
-  if (c < 0) c = d == 64 ? occupancy(dkdv_kernel<64, false>, 256) : occupancy(dkdv_kernel<128, false>, 256);
-  return c;
+  static const int c64 = occupancy(dkdv_kernel<64, false>, 256);
+  static const int c128 = occupancy(dkdv_kernel<128, false>, 256);
+  return d == 64 ? c64 : c128;
 }
 
 int dq_blocks_per_cu(int d) {
-  static int c64 = -1, c128 = -1;
-  int& c = d == 64 ? c64 : c128;
-  if (c < 0)
-    c = d == 64 ? occupancy(dq_kernel<64, false>, DqCfg<64>::kThreads) : occupancy(dq_kernel<128, false>, DqCfg<128>::kThreads);
-  return c;
+  static const int c64 = occupancy(dq_kernel<64, false>, DqCfg<64>::kThreads);
+  static const int c128 = occupancy(dq_kernel<128, false>, DqCfg<128>::kThreads);
+  return d == 64 ? c64 : c128;
 }
 
 template <int D, bool kPacked>

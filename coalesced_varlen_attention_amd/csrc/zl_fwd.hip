@@ -615,14 +615,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   }
 }
 
+// Resident forward workgroups per compute unit, queried once (a function-local static, so
+// concurrent first calls are safe); 0 if the query fails.
 template <int D>
 int blocks_per_cu_impl() {
-  static int cached = -1;
-  if (cached < 0) {
+  static const int cached = [] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<D, false>, 256, 0) != hipSuccess) n = 0;
-    cached = n;
-  }
+    return n;
+  }();
   return cached;
 }
 
