@@ -4,7 +4,8 @@
 The kernels only address rows differently, so the packed run must reproduce the planar run bit
 for bit: O, LSE, every ring partial and, unpacked, dQ, dK and dV, with untouched rows left
 untouched. The planar run is itself checked against the fp64 oracle. Covers whole sequences,
-head subsets, a query range, a ring group and split-KV items at d_head 64 and 128.
+head subsets, a query range, a ring group and split-KV items at d_head 64 and 128, and the
+seeded random packs whose sequences have equal query and key lengths.
 """
 import numpy as np
 import pytest
@@ -12,6 +13,7 @@ import torch
 
 import workloads as W
 from tests import gpu_harness as H
+from tests import random_packs as R
 
 pytestmark = [pytest.mark.gpu, H.requires_gpu]
 
@@ -44,6 +46,36 @@ def _same(name, a, b):
     assert torch.equal(a[~nan_a], b[~nan_b]), f"{name}: values differ"
 
 
+def _packed_matches(pack, ins, planar):
+    """Run `pack` in the QKV-packed layout and compare every output with the planar run bit for bit."""
+    z = H.zl()
+    dev = torch.device("cuda:0")
+    d = pack.d
+    plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, d, qkv_packed=True)
+    info = plan.info
+    assert info["qkv_rows"] == 3 * info["q_rows"]
+    qkv = _pack_qkv(pack, ins["q"], ins["k"], ins["v"]).to(dev)
+    do = ins["do"].to(dev)
+    nan = float("nan")
+    o = torch.full((info["q_rows"], d), nan, dtype=torch.float32, device=dev)
+    lse = torch.full((info["q_rows"],), nan, dtype=torch.float32, device=dev)
+    o, lse, o_part, lse_part = z.attn_fwd(plan, qkv, qkv, qkv, o=o, lse=lse)
+    if info["n_groups"]:
+        z.merge_groups(plan, o_part, lse_part, o, lse)
+    dqkv = torch.full((info["qkv_rows"], d), nan, dtype=torch.float32, device=dev)
+    z.attn_bwd(plan, qkv, qkv, qkv, o, lse, do, dq=dqkv, dk=dqkv, dv=dqkv)
+    torch.cuda.synchronize()
+    _same("o", o, planar["o"])
+    _same("lse", lse, planar["lse"])
+    if planar["o_part"] is not None:
+        _same("o_part", o_part, planar["o_part"])
+        _same("lse_part", lse_part, planar["lse_part"])
+    dq, dk, dv = _unpack(pack, dqkv)
+    _same("dq", dq, planar["dq"])
+    _same("dk", dk, planar["dk"])
+    _same("dv", dv, planar["dv"])
+
+
 CASES = {
     "mixed_segments": (
         (200, 333, 700, 5000), (4, 4, 2, 1),
@@ -56,8 +88,6 @@ CASES = {
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_packed_matches_planar_bitwise(d):
-    z = H.zl()
-    dev = torch.device("cuda:0")
     lens, heads, seg = CASES["mixed_segments"]
     pack = W.Pack(f"packed{d}", lens, lens, heads, seg, d, 90 + d)
     ins = W.draw(pack)
@@ -66,28 +96,7 @@ def test_packed_matches_planar_bitwise(d):
     assert planar["plan"].info["split_tiles"] > 0
     ref = H.oracle_pack(pack, ins)
     H.compare_full(pack, ins, planar, ref)
-
-    plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, d, qkv_packed=True)
-    info = plan.info
-    assert info["qkv_rows"] == 3 * info["q_rows"]
-    qkv = _pack_qkv(pack, ins["q"], ins["k"], ins["v"]).to(dev)
-    do = ins["do"].to(dev)
-    nan = float("nan")
-    o = torch.full((info["q_rows"], d), nan, dtype=torch.float32, device=dev)
-    lse = torch.full((info["q_rows"],), nan, dtype=torch.float32, device=dev)
-    o, lse, o_part, lse_part = z.attn_fwd(plan, qkv, qkv, qkv, o=o, lse=lse)
-    z.merge_groups(plan, o_part, lse_part, o, lse)
-    dqkv = torch.full((info["qkv_rows"], d), nan, dtype=torch.float32, device=dev)
-    z.attn_bwd(plan, qkv, qkv, qkv, o, lse, do, dq=dqkv, dk=dqkv, dv=dqkv)
-    torch.cuda.synchronize()
-    _same("o", o, planar["o"])
-    _same("lse", lse, planar["lse"])
-    _same("o_part", o_part, planar["o_part"])
-    _same("lse_part", lse_part, planar["lse_part"])
-    dq, dk, dv = _unpack(pack, dqkv)
-    _same("dq", dq, planar["dq"])
-    _same("dk", dk, planar["dk"])
-    _same("dv", dv, planar["dv"])
+    _packed_matches(pack, ins, planar)
 
 
 def test_packed_rejects_distinct_pointers():
@@ -98,3 +107,17 @@ def test_packed_rejects_distinct_pointers():
     other = torch.zeros(3 * 64, 64, dtype=torch.bfloat16, device=dev)
     with pytest.raises(z.ZlError, match="q == k == v"):
         z.attn_fwd(plan, qkv, other, qkv)
+
+
+PACKED_SEEDS = tuple(seed for seed in R.SEEDS if R.random_pack(seed).seq_q == R.random_pack(seed).seq_kv)
+
+
+@pytest.mark.parametrize("seed", PACKED_SEEDS)
+def test_random_packs_packed_match_planar(seed):
+    """The seeded random packs whose sequences have equal query and key lengths (ring groups with
+    out-of-order parts, head subsets, query ranges, split items), packed vs planar bit for bit."""
+    pack = R.random_pack(seed)
+    ins = W.draw(pack)
+    print(f"[case] packed vs planar {pack.name} d={pack.d} seqs={pack.seq_q} heads={pack.heads}", flush=True)
+    planar = H.run_pack(pack, ins)
+    _packed_matches(pack, ins, planar)
