@@ -4,8 +4,8 @@ Ring accumulation: each call folds one key/value block of a query chunk into the
 (O, LSE) at the chunk's rows. After the last block, in any order, the rows must hold
 attention over the whole key range, element by element within the usual tolerance; after
 the first block they must hold that block's own result. Covers d_head 64 and 128, blocks of
-one key and of ragged lengths, two ring groups folded in the same calls, and whole segments
-written in the same launch.
+one key and of ragged lengths, two ring groups folded in the same calls, whole segments
+written in the same launch, and the seeded random packs that hold ring groups.
 """
 import numpy as np
 import pytest
@@ -14,6 +14,7 @@ import torch
 import oracle
 import workloads as W
 from tests import gpu_harness as H
+from tests import random_packs as R
 
 pytestmark = [pytest.mark.gpu, H.requires_gpu]
 
@@ -121,3 +122,35 @@ def test_head_subset_group_folded(d):
     H.assert_close("O", go[cov], ref["o"][cov])
     H.assert_close("LSE", gl[cov], ref["lse"][cov])
     assert np.isnan(go[~cov]).all() and np.isnan(gl[~cov]).all(), "rows outside the head subset were written"
+
+
+ACC_SEEDS = tuple(seed for seed in R.SEEDS if any(sg[7] >= 0 for sg in R.random_pack(seed).segments))
+
+
+@pytest.mark.parametrize("seed", ACC_SEEDS)
+def test_random_packs_folded_part_by_part(seed):
+    """The seeded random packs with ring groups, forward by running merge: launch b folds part b
+    of every group (renumbered part 0 of a one-part plan) into O and LSE, whole segments go with
+    launch 0, and every row starts at LSE = -inf. After the last launch every covered row must
+    hold the oracle's merged result."""
+    z = H.zl()
+    dev = torch.device("cuda:0")
+    pack = R.random_pack(seed)
+    ins = W.draw(pack)
+    q, k, v = (ins[n].to(dev) for n in ("q", "k", "v"))
+    n_q = pack.q_rows()
+    o = torch.full((n_q, pack.d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((n_q,), float("-inf"), dtype=torch.float32, device=dev)
+    n_launch = 1 + max(sg[7] for sg in pack.segments)
+    print(f"[case] running merge {pack.name} d={pack.d} launches={n_launch}", flush=True)
+    for b in range(n_launch):
+        segs = tuple(sg[:7] + (0,) for sg in pack.segments if sg[7] == b)
+        if b == 0:
+            segs += tuple(sg for sg in pack.segments if sg[7] < 0)
+        plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, segs, pack.d)
+        z.attn_fwd_accumulate(plan, q, k, v, o, lse)
+    torch.cuda.synchronize()
+    ref = H.oracle_pack(pack, ins)
+    cov = ~np.isnan(ref["lse"])
+    H.assert_close("O", H.f64(o)[cov], ref["o"][cov])
+    H.assert_close("LSE", H.f64(lse)[cov], ref["lse"][cov])
