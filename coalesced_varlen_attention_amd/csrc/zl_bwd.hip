@@ -20,8 +20,8 @@
 //   loads into a ring of three stages, issued two steps ahead, so a step costs one barrier and
 //   waits only for loads issued a step earlier. dK and dV accumulate in registers and are
 //   written once.
-// dQ kernel: one item = 128 query rows of one (segment or ring group, head); 4 waves x 32
-//   query rows, the forward's shape: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers
+// dQ kernel: one item = kDqRows (256) query rows of one (segment or ring group, head);
+//   kDqWaves (8) waves x 32 query rows, the forward's shape per wave: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers
 //   (lane = one query row, whose LSE and D are then per-lane scalars), and
 //   dQ^T += K^T dS^T with K^T from transposed LDS reads. K and V blocks reach LDS by direct
 //   global-to-LDS loads in the key-major kernel's layout, one block ahead, walking the chain

@@ -15,7 +15,7 @@ namespace zl {
 // Backward dQ queue item: kDqRows query rows of one (final segment or ring group, head),
 // looping over every key range of the segment (all parts of a ring group).
 constexpr int kFwdRows = 128;
-constexpr int kDqWaves = 4;                // waves per dQ workgroup, 32 query rows each
+constexpr int kDqWaves = 8;                // waves per dQ workgroup, 32 query rows each
 constexpr int kDqRows = 32 * kDqWaves;
 constexpr int kFwdKeys = 64;  // keys per forward step
 // Split-KV of forward items (short queues leave compute units idle): a plan whose forward
@@ -30,10 +30,11 @@ constexpr int kSplitTargetWaves = 1;  // about one piece per resident workgroup:
                                       // costs a partial write and its share of a merge
 constexpr int kMaxPieces = 16;
 constexpr int kMinPieceKeys = 1024;
-// Resident workgroups assumed by a host-only plan: 256 CUs x 2 for the forward and dQ kernels,
-// x 1 for the dK/dV kernel.
+// Resident workgroups assumed by a host-only plan: 256 CUs x 2 for the forward kernel, x 1 for
+// the dK/dV kernel, and one 8-wave (two 4-wave) dQ workgroups per CU.
 constexpr int kHostOnlySlots = 512;
 constexpr int kHostOnlyKvSlots = 256;
+constexpr int kHostOnlyDqSlots = 256 * (8 / kDqWaves);
 constexpr int kBwdKeys = 128;
 constexpr int kBwdRows = 64;
 // Rows (token, head pairs) per item of the backward pre-pass.

@@ -475,7 +475,7 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
       slots = (int64_t)plan->n_cu * per_cu;
     }
     split_forward(slots, &fwd, &fwd_unit, &plan->split_tiles, &plan->split_pieces);
-    int64_t dq_slots = zl::kHostOnlySlots;
+    int64_t dq_slots = zl::kHostOnlyDqSlots;
     if (!(flags & ZL_PLAN_HOST_ONLY)) {
       const int per_cu = zl::dq_blocks_per_cu(d_head);
       if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_plan_build: dQ kernel cannot be resident");

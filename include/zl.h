@@ -139,7 +139,7 @@ typedef struct {
  * device) and nothing else. The forward queue holds one item per (segment, head, block of
  * 128 query rows); the backward has a dK/dV queue with one item per (segment, head, block
  * of 128 key rows) and a dQ queue with one item per (final segment or ring group, head,
- * block of 128 query rows). Each is split into one queue per XCD (zl_plan_queues): chunks of
+ * block of 256 query rows). Each is split into one queue per XCD (zl_plan_queues): chunks of
  * consecutive items of one (segment, head) go to the least-loaded queue, largest first, and
  * each queue is sorted by decreasing cost (rows x length of the other side), ties kept in
  * (segment, head, block) order. A workgroup drains its own XCD's queue, then the others.

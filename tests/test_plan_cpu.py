@@ -329,17 +329,22 @@ def _dq_pieces(p):
 
 
 def test_dq_split_cuts_items_of_a_short_queue():
-    """One head of 8192 tokens: 64 dQ items of 128 query rows over a chain of 128 key blocks, far
-    fewer than the 512 resident dQ workgroups assumed for a host-only plan: each item becomes 8
-    pieces of 16 blocks (1024 keys), contiguous, with one workspace slot per item."""
+    """One head of 8192 tokens: 8192 / R dQ items of R query rows over a chain of 128 key blocks,
+    far fewer than the resident dQ workgroups a host-only plan assumes (one per CU x 256 CUs for
+    8-wave workgroups): each item becomes 8 pieces of 16 blocks (1024 keys), contiguous, with one
+    workspace slot per item."""
     seg = ((0, 0, 1, 0, 8192, 0, 8192, -1),)
     p = z.Plan((8192,), (8192,), (1,), seg, 128, host_only=True)
     nosplit = z.Plan((8192,), (8192,), (1,), seg, 128, host_only=True, split=False)
-    assert p.info["dq_split_tiles"] == 64 and p.info["dq_split_pieces"] == 512 and p.info["dq_tiles"] == 512
-    assert nosplit.info["dq_split_tiles"] == 0 and nosplit.info["dq_tiles"] == 64
+    rows = max(t[3] for t in nosplit.tiles(2))
+    assert rows in (128, 256)
+    n_items = 8192 // rows
+    assert p.info["dq_split_tiles"] == n_items and p.info["dq_split_pieces"] == 8 * n_items
+    assert p.info["dq_tiles"] == 8 * n_items and nosplit.info["dq_split_tiles"] == 0
+    assert nosplit.info["dq_tiles"] == n_items
     assert all(t[4:] == (0, 128, -1, 1 << 16) for t in nosplit.tiles(4))
     items = _dq_pieces(p)
-    assert len(items) == 64
+    assert len(items) == n_items
     slots = set()
     for key, pieces in items.items():
         pieces.sort()
@@ -349,9 +354,9 @@ def test_dq_split_cuts_items_of_a_short_queue():
         assert all(x[1] - x[0] == 16 for x in pieces)
         assert len({x[2] for x in pieces}) == 1
         slots.add(pieces[0][2])
-    assert sorted(slots) == list(range(0, 512, 8))
-    # the workspace holds a counter and 128 rows of partial dQ per piece
-    assert p.info["ws_bwd"] - nosplit.info["ws_bwd"] >= 512 * (4 + 128 * 128 * 4)
+    assert sorted(slots) == list(range(0, 8 * n_items, 8))
+    # the workspace holds a counter and `rows` rows of partial dQ per piece
+    assert p.info["ws_bwd"] - nosplit.info["ws_bwd"] >= 8 * n_items * (4 + rows * 128 * 4)
     # costs stay proportional to the keys: the queue still sorts by decreasing cost
     t4 = p.tiles(4)
     _per_queue_cost_order([(t[0], t[1], (t[2], t[4])) for t in t4], [t[3] * 64 * (t[5] - t[4]) for t in t4],
@@ -360,12 +365,13 @@ def test_dq_split_cuts_items_of_a_short_queue():
 
 def test_dq_split_over_a_ring_chain():
     """A ring group of 3 parts of 2000 keys: its dQ items walk a chain of 3 x 32 blocks, and the
-    pieces cut that chain into runs that may cross part boundaries; the 44-row tail item too."""
+    pieces cut that chain into runs that may cross part boundaries; the ragged tail item too."""
     seg = tuple((0, 0, 1, 0, 300, 2000 * b, 2000 * (b + 1), b) for b in range(3))
     p = z.Plan((300,), (6000,), (1,), seg, 64, host_only=True)
-    assert p.info["dq_split_tiles"] == 3
     items = _dq_pieces(p)
-    assert sorted(k[2:] for k in items) == [(0, 128), (128, 128), (256, 44)]
+    assert p.info["dq_split_tiles"] == len(items)
+    rows = max(k[3] for k in items)
+    assert sorted(k[2:] for k in items) == [(r, min(rows, 300 - r)) for r in range(0, 300, rows)]
     for key, pieces in items.items():
         pieces.sort()
         n = pieces[0][4]
