@@ -8,6 +8,20 @@ the computation runs in the HIP kernels behind the C ABI of ``include/zl.h``. Py
 provides device memory and the current stream.
 
 If ``libzl.so`` is missing, the first call raises: there is no fallback.
+
+Example: two sequences (1024 tokens at 24 heads, and a 4096-token one at 24 heads whose keys
+are split into two ring parts), d_head 128::
+
+    import torch, coalesced_varlen_attention_amd as zl
+    segs = [(0, 0, 24, 0, 1024, 0, 1024, -1),                 # whole sequence, final rows
+            (1, 0, 24, 0, 4096, 0, 2048, 0),                  # ring part 0
+            (1, 0, 24, 0, 4096, 2048, 4096, 1)]               # ring part 1
+    plan = zl.Plan([1024, 4096], [1024, 4096], [24, 24], segs, 128)
+    rows = plan.info["q_rows"]                                 # (1024 + 4096) * 24
+    q, k, v, do = (torch.randn(rows, 128, device="cuda").bfloat16() for _ in range(4))
+    o, lse, o_part, lse_part = zl.attn_fwd(plan, q, k, v)
+    zl.merge_groups(plan, o_part, lse_part, o, lse)            # exact merge of the ring parts
+    dq, dk, dv = zl.attn_bwd(plan, q, k, v, o, lse, do)
 """
 from __future__ import annotations
 
@@ -15,8 +29,8 @@ import ctypes
 import os
 from typing import List, Optional, Sequence, Tuple
 
-__all__ = ["Plan", "ZlError", "attn_fwd", "attn_bwd", "lse_merge", "merge_groups", "lib", "lib_path",
-           "SEGMENT_FIELDS"]
+__all__ = ["Plan", "ZlError", "attn_fwd", "attn_fwd_accumulate", "attn_bwd", "lse_merge", "merge_groups", "lib",
+           "lib_path", "SEGMENT_FIELDS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libzl.so")
