@@ -61,3 +61,15 @@ def test_binding_structs_match_the_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(cls), f"{cname}: size differs from the binding"
         for field, _ in cls._fields_:
             assert got[(cname, field)] == getattr(cls, field).offset, f"{cname}.{field}: offset differs"
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    """Without libzl.so the binding raises on first use (plan building included): there is no
+    fallback path."""
+    import pytest
+    monkeypatch.setattr(z, "_LIB", None)
+    monkeypatch.setattr(z, "_LIB_PATH", str(tmp_path / "libzl.so"))
+    with pytest.raises(ImportError, match="no fallback"):
+        z.lib()
+    with pytest.raises(ImportError, match="no fallback"):
+        z.Plan([64], [64], [1], [(0, 0, 1, 0, 64, 0, 64, -1)], 64, host_only=True)
