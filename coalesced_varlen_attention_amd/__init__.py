@@ -38,6 +38,7 @@ _LIB_PATH = os.path.join(_HERE, "libzl.so")
 ZL_PLAN_HOST_ONLY = 1
 ZL_PLAN_NO_SPLIT = 2
 ZL_PLAN_QKV_PACKED = 4
+ZL_PLAN_COUNT_VISITS = 8
 BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 SEGMENT_FIELDS = ("seq", "head_begin", "head_end", "q_begin", "q_end", "kv_begin", "kv_end", "part")
 
@@ -62,7 +63,8 @@ class _PlanInfo(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float), ("dq_tiles", ctypes.c_int64), ("split_tiles", ctypes.c_int32),
                 ("split_pieces", ctypes.c_int32), ("qkv_rows", ctypes.c_int64),
                 ("dq_split_tiles", ctypes.c_int32), ("dq_split_pieces", ctypes.c_int32),
-                ("kv_split_tiles", ctypes.c_int32), ("kv_split_pieces", ctypes.c_int32)]
+                ("kv_split_tiles", ctypes.c_int32), ("kv_split_pieces", ctypes.c_int32),
+                ("visits_fwd", ctypes.c_int64), ("visits_dkdv", ctypes.c_int64), ("visits_dq", ctypes.c_int64)]
 
 
 class _GroupInfo(ctypes.Structure):
@@ -135,11 +137,12 @@ class Plan:
 
     ``seq_q``/``seq_kv``: tokens per sequence; ``heads``: stored heads per sequence;
     ``segments``: tuples ``(seq, head_begin, head_end, q_begin, q_end, kv_begin, kv_end, part)``.
+    ``count_visits``: the scheduler check of ``ZL_PLAN_COUNT_VISITS`` (read with ``visits``).
     """
 
     def __init__(self, seq_q: Sequence[int], seq_kv: Sequence[int], heads: Sequence[int], segments, d: int,
                  scale: Optional[float] = None, host_only: bool = False, split: bool = True,
-                 qkv_packed: bool = False):
+                 qkv_packed: bool = False, count_visits: bool = False):
         n = len(seq_q)
         if len(seq_kv) != n or len(heads) != n:
             raise ValueError("seq_q, seq_kv and heads must have the same length")
@@ -155,7 +158,7 @@ class Plan:
                 setattr(segs[i], name, int(val))
         self._h = ctypes.c_void_p()
         flags = ((ZL_PLAN_HOST_ONLY if host_only else 0) | (0 if split else ZL_PLAN_NO_SPLIT) |
-                 (ZL_PLAN_QKV_PACKED if qkv_packed else 0))
+                 (ZL_PLAN_QKV_PACKED if qkv_packed else 0) | (ZL_PLAN_COUNT_VISITS if count_visits else 0))
         _check(lib().zl_plan_build(n, ctypes.cast(cu_q, ctypes.c_void_p), ctypes.cast(cu_kv, ctypes.c_void_p),
                                   ctypes.cast(hs, ctypes.c_void_p), len(segments), ctypes.cast(segs, ctypes.c_void_p),
                                   int(d), float(scale) if scale else 0.0, flags, ctypes.byref(self._h)))
@@ -192,6 +195,21 @@ class Plan:
         _check(lib().zl_plan_queues(self._h, which, ctypes.cast(buf, ctypes.c_void_p), 64, ctypes.byref(n)))
         return list(buf[: n.value + 1])
 
+    def visits(self, ws_fwd=None, ws_bwd=None) -> dict:
+        """Per-item visit counters of a ``count_visits`` plan, read from the workspaces of the last
+        forward (``ws_fwd``) and backward (``ws_bwd``) launches: {"fwd" | "dkdv" | "dq": int32 tensor}."""
+        import torch
+        info = self.info
+        if info["visits_fwd"] < 0:
+            raise ValueError("the plan was not built with count_visits=True")
+        out = {}
+        for key, ws, off, n in (("fwd", ws_fwd, info["visits_fwd"], info["fwd_tiles"]),
+                                ("dkdv", ws_bwd, info["visits_dkdv"], info["bwd_tiles"]),
+                                ("dq", ws_bwd, info["visits_dq"], info["dq_tiles"])):
+            if ws is not None:
+                out[key] = ws[off:off + 4 * n].view(torch.int32).cpu()
+        return out
+
     def close(self) -> None:
         if getattr(self, "_h", None) and self._h.value:
             lib().zl_plan_destroy(self._h)
@@ -211,16 +229,37 @@ def _input_rows(info):
     return info["q_rows"], info["kv_rows"]
 
 
-def _check_tensor(t, name, dtype, rows, d, device):
+def _gpu_device(t, name):
+    """The device of ``t``, which must be a GPU tensor: the kernels dereference every pointer
+    on the device, so a host pointer would fault there instead of failing here."""
     import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} is on {t.device}: the library needs device tensors")
+    return t.device
+
+
+def _check_tensor(t, name, dtype, rows, d, device):
+    if _gpu_device(t, name) != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if t.numel() != rows * d:
         raise ValueError(f"{name} has {t.numel()} elements, expected {rows} x {d}")
+
+
+def _check_workspace(ws, need, device):
+    """A byte buffer on ``device`` of at least ``need`` bytes (its dtype fixes the byte count)."""
+    import torch
+    if _gpu_device(ws, "workspace") != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise TypeError("workspace must be a contiguous torch.uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"workspace has {ws.numel()} bytes, the plan needs {need}")
 
 
 def attn_fwd(plan: Plan, q, k, v, o=None, lse=None, o_part=None, lse_part=None, workspace=None, stream=None):
@@ -231,7 +270,7 @@ def attn_fwd(plan: Plan, q, k, v, o=None, lse=None, o_part=None, lse_part=None, 
     Ring groups still need ``merge_groups`` (or ``lse_merge``) to produce their final rows.
     """
     import torch
-    info, d, dev = plan.info, plan.d, q.device
+    info, d, dev = plan.info, plan.d, _gpu_device(q, "q")
     rq, rkv = _input_rows(info)
     _check_tensor(q, "q", torch.bfloat16, rq, d, dev)
     _check_tensor(k, "k", torch.bfloat16, rkv, d, dev)
@@ -251,8 +290,7 @@ def attn_fwd(plan: Plan, q, k, v, o=None, lse=None, o_part=None, lse_part=None, 
     _check_tensor(lse, "lse", torch.float32, info["q_rows"], 1, dev)
     if workspace is None:
         workspace = torch.empty(info["ws_fwd"], dtype=torch.uint8, device=dev)
-    if workspace.numel() < info["ws_fwd"]:
-        raise ValueError("workspace too small")
+    _check_workspace(workspace, info["ws_fwd"], dev)
     _check(lib().zl_attn_fwd(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             _ptr(o_part), _ptr(lse_part), workspace.data_ptr(), _stream_handle(stream)))
     return o, lse, o_part, lse_part
@@ -264,7 +302,7 @@ def attn_fwd_accumulate(plan: Plan, q, k, v, o, lse, workspace=None, stream=None
     a group's first block); ``part == -1`` segments are written as in ``attn_fwd``. The plan
     may hold at most one part per group. Returns ``(o, lse)``."""
     import torch
-    info, d, dev = plan.info, plan.d, q.device
+    info, d, dev = plan.info, plan.d, _gpu_device(q, "q")
     rq, rkv = _input_rows(info)
     _check_tensor(q, "q", torch.bfloat16, rq, d, dev)
     _check_tensor(k, "k", torch.bfloat16, rkv, d, dev)
@@ -273,8 +311,7 @@ def attn_fwd_accumulate(plan: Plan, q, k, v, o, lse, workspace=None, stream=None
     _check_tensor(lse, "lse", torch.float32, info["q_rows"], 1, dev)
     if workspace is None:
         workspace = torch.empty(info["ws_fwd"], dtype=torch.uint8, device=dev)
-    if workspace.numel() < info["ws_fwd"]:
-        raise ValueError("workspace too small")
+    _check_workspace(workspace, info["ws_fwd"], dev)
     _check(lib().zl_attn_fwd_accumulate(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                         lse.data_ptr(), workspace.data_ptr(), _stream_handle(stream)))
     return o, lse
@@ -286,9 +323,16 @@ def lse_merge(n_parts: int, n_rows: int, d: int, o_part, lse_part, o, lse, strea
     ``o_part``: ``n_parts*n_rows*d`` floats, ``lse_part``: ``n_parts*n_rows``; results to
     ``o`` (``n_rows*d``) and ``lse`` (``n_rows``). Views must be contiguous.
     """
-    for t, n in ((o_part, n_parts * n_rows * d), (lse_part, n_parts * n_rows), (o, n_rows * d), (lse, n_rows)):
+    import torch
+    dev = _gpu_device(o_part, "o_part")
+    for t, name, n in ((o_part, "o_part", n_parts * n_rows * d), (lse_part, "lse_part", n_parts * n_rows),
+                       (o, "o", n_rows * d), (lse, "lse", n_rows)):
+        if _gpu_device(t, name) != dev:
+            raise ValueError(f"lse_merge: {name} is on {t.device}, expected {dev}")
+        if t.dtype != torch.float32:
+            raise TypeError(f"lse_merge: {name} must be torch.float32, got {t.dtype}")
         if not t.is_contiguous() or t.numel() < n:
-            raise ValueError("lse_merge: tensor too small or not contiguous")
+            raise ValueError(f"lse_merge: {name} has {t.numel()} elements (needs {n}) or is not contiguous")
     _check(lib().zl_lse_merge(int(n_parts), int(n_rows), int(d), o_part.data_ptr(), lse_part.data_ptr(),
                              o.data_ptr(), lse.data_ptr(), _stream_handle(stream)))
 
@@ -300,7 +344,7 @@ def merge_groups(plan: Plan, o_part, lse_part, o, lse, stream=None) -> None:
     info, d = plan.info, plan.d
     if info["n_groups"] == 0:
         return
-    dev = o.device
+    dev = _gpu_device(o, "o")
     _check_tensor(o_part, "o_part", torch.float32, info["part_rows"], d, dev)
     _check_tensor(lse_part, "lse_part", torch.float32, info["part_rows"], 1, dev)
     _check_tensor(o, "o", torch.float32, info["q_rows"], d, dev)
@@ -316,7 +360,7 @@ def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspa
     ``stages`` selects launches (BWD_PRE, BWD_DKDV, BWD_DQ); DKDV and DQ need a PRE before
     each of them on the same workspace."""
     import torch
-    info, d, dev = plan.info, plan.d, q.device
+    info, d, dev = plan.info, plan.d, _gpu_device(q, "q")
     rq, rkv = _input_rows(info)
     _check_tensor(q, "q", torch.bfloat16, rq, d, dev)
     _check_tensor(k, "k", torch.bfloat16, rkv, d, dev)
@@ -341,8 +385,7 @@ def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspa
     _check_tensor(dv, "dv", torch.float32, rkv, d, dev)
     if workspace is None:
         workspace = torch.empty(info["ws_bwd"], dtype=torch.uint8, device=dev)
-    if workspace.numel() < info["ws_bwd"]:
-        raise ValueError("workspace too small")
+    _check_workspace(workspace, info["ws_bwd"], dev)
     _check(lib().zl_attn_bwd_stages(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                    lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                    workspace.data_ptr(), int(stages), _stream_handle(stream)))

@@ -76,6 +76,28 @@ size_t bwd_fixed_bytes(const zl_plan* plan) {
   return kCounterBytes + 2 * align256((size_t)plan->q_rows * sizeof(float)) + align256(kSentinelBytes);
 }
 
+// Scheduler check (ZL_PLAN_COUNT_VISITS): one int32 per work item at the end of each workspace.
+bool counts_visits(const zl_plan* plan) { return (plan->flags & ZL_PLAN_COUNT_VISITS) != 0; }
+size_t fwd_visit_offset(const zl_plan* plan) { return kCounterBytes + split_bytes(plan); }
+size_t bwd_visit_offset(const zl_plan* plan) {
+  return bwd_fixed_bytes(plan) + dq_split_bytes(plan) + kv_split_bytes(plan);
+}
+size_t fwd_visit_bytes(const zl_plan* plan) {
+  return counts_visits(plan) ? align256(plan->fwd_tiles.size() * sizeof(int32_t)) : 0;
+}
+// dK/dV counters, then dQ counters.
+size_t bwd_visit_bytes(const zl_plan* plan) {
+  return counts_visits(plan) ? align256(plan->bwd_tiles.size() * sizeof(int32_t)) +
+                                   align256(plan->dq_tiles.size() * sizeof(int32_t))
+                             : 0;
+}
+
+void set_fwd_visits(const zl_plan* plan, void* workspace, zl::FwdParams* p) {
+  if (!counts_visits(plan)) return;
+  p->visits = (int32_t*)((char*)workspace + fwd_visit_offset(plan));
+  p->n_visits = (int32_t)plan->fwd_tiles.size();
+}
+
 zl_status check_runnable(const zl_plan* plan, const char* who) {
   if (!plan) return fail(ZL_ERR_INVALID, std::string(who) + ": plan is NULL");
   if (!plan->dev_block) return fail(ZL_ERR_INVALID, std::string(who) + ": plan was built host-only and cannot run");
@@ -113,8 +135,8 @@ extern "C" const char* zl_last_error(void) { return zl::g_last_error.c_str(); }
 extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   if (!plan || !info) return fail(ZL_ERR_INVALID, "zl_plan_info: NULL argument");
   std::memset(info, 0, sizeof(*info));
-  info->ws_fwd = kCounterBytes + split_bytes(plan);
-  info->ws_bwd = bwd_fixed_bytes(plan) + dq_split_bytes(plan) + kv_split_bytes(plan);
+  info->ws_fwd = fwd_visit_offset(plan) + fwd_visit_bytes(plan);
+  info->ws_bwd = bwd_visit_offset(plan) + bwd_visit_bytes(plan);
   info->q_rows = plan->q_rows;
   info->kv_rows = plan->kv_rows;
   info->qkv_rows = (plan->flags & ZL_PLAN_QKV_PACKED) ? 3 * plan->q_rows : 0;
@@ -134,6 +156,12 @@ extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   info->dq_split_pieces = plan->dq_split_pieces;
   info->kv_split_tiles = plan->kv_split_tiles;
   info->kv_split_pieces = plan->kv_split_pieces;
+  info->visits_fwd = info->visits_dkdv = info->visits_dq = -1;
+  if (counts_visits(plan)) {
+    info->visits_fwd = (int64_t)fwd_visit_offset(plan);
+    info->visits_dkdv = (int64_t)bwd_visit_offset(plan);
+    info->visits_dq = (int64_t)(bwd_visit_offset(plan) + align256(plan->bwd_tiles.size() * sizeof(int32_t)));
+  }
   return ZL_OK;
 }
 
@@ -209,6 +237,7 @@ extern "C" zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void*
   p.queue = {plan->d_fwd, plan->d_bounds, (int32_t*)workspace};
   p.scale_log2 = plan->scale * 1.4426950408889634f;
   set_split(plan, workspace, &p);
+  set_fwd_visits(plan, workspace, &p);
   p.packed = (plan->flags & ZL_PLAN_QKV_PACKED) ? 1 : 0;
   const int per_cu = zl::fwd_blocks_per_cu(plan->d);
   if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_fwd: forward kernel cannot be resident");
@@ -245,6 +274,7 @@ extern "C" zl_status zl_attn_fwd_accumulate(const zl_plan* plan, const void* q, 
   p.scale_log2 = plan->scale * 1.4426950408889634f;
   p.accumulate = 1;
   set_split(plan, workspace, &p);
+  set_fwd_visits(plan, workspace, &p);
   p.packed = (plan->flags & ZL_PLAN_QKV_PACKED) ? 1 : 0;
   const int per_cu = zl::fwd_blocks_per_cu(plan->d);
   if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_fwd_accumulate: forward kernel cannot be resident");
@@ -335,6 +365,12 @@ extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, cons
     char* base = (char*)workspace + bwd_fixed_bytes(plan) + dq_split_bytes(plan);
     p.kv_split_cnt = (int32_t*)base;
     p.kv_split = (float*)(base + align256((size_t)p.n_kv_split * sizeof(int32_t)));
+  }
+  if (counts_visits(plan)) {
+    p.kv_visits = (int32_t*)((char*)workspace + bwd_visit_offset(plan));
+    p.dq_visits = (int32_t*)((char*)p.kv_visits + align256(plan->bwd_tiles.size() * sizeof(int32_t)));
+    p.n_kv_visits = (int32_t)plan->bwd_tiles.size();
+    p.n_dq_visits = (int32_t)plan->dq_tiles.size();
   }
   p.segs = plan->d_segs;
   p.pre_tiles = plan->d_pre;

@@ -54,6 +54,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
     p.dq_split_cnt[j] = 0;  // pieces finished per split dQ item
   for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < p.n_kv_split; j += gridDim.x * blockDim.x)
     p.kv_split_cnt[j] = 0;  // pieces finished per split dK/dV item
+  if (p.kv_visits) {      // scheduler check: visits per item of both queues
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < p.n_kv_visits; j += gridDim.x * blockDim.x)
+      p.kv_visits[j] = 0;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < p.n_dq_visits; j += gridDim.x * blockDim.x)
+      p.dq_visits[j] = 0;
+  }
   const float neg_inv_tau = -1.0f / p.scale;
   constexpr int kPer = D / 16;  // elements per lane
   const int sub = threadIdx.x & 15;
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   const int home = blockIdx.x % kQueues;
   int drained = 0;
   for (;;) {
-    if (tid == 0) s_item = take_item(p.kvq, home, drained);
+    if (tid == 0) s_item = take_item(p.kvq, home, drained, p.kv_visits);
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item);  // the same for every lane
     if (item < 0) break;
@@ -741,7 +747,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
   const int home = blockIdx.x % kQueues;
   int drained = 0;
   for (;;) {
-    if (tid == 0) s_item = take_item(p.dqq, home, drained);
+    if (tid == 0) s_item = take_item(p.dqq, home, drained, p.dq_visits);
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item);  // the same for every lane
     if (item < 0) break;

@@ -180,11 +180,15 @@ __device__ __forceinline__ void load_dev16x16(const float* p, f32x4 (&x)[16]) {
 // Next work item for a workgroup (called by one thread): its own XCD's queue first, then the
 // others in order. `drained` counts the queues found empty and only grows, so every
 // workgroup stops after at most (its items + kQueues) atomics. Returns -1 when all are empty.
-__device__ __forceinline__ int take_item(const Queues& q, int home, int& drained) {
+// With `visits` (the scheduler check), the item taken is also counted there.
+__device__ __forceinline__ int take_item(const Queues& q, int home, int& drained, int32_t* visits) {
   while (drained < kQueues) {
     const int k = (home + drained) & (kQueues - 1);
     const int idx = q.bounds[k] + atomicAdd(&q.counters[k * kCounterStride], 1);
-    if (idx < q.bounds[k + 1]) return idx;
+    if (idx < q.bounds[k + 1]) {
+      if (visits) atomicAdd(visits + idx, 1);
+      return idx;
+    }
     ++drained;
   }
   return -1;

@@ -137,11 +137,14 @@ __device__ __forceinline__ void dma_v(const FwdCtx<D>& cx, uint32_t v_lds, int b
   }
 }
 
-// Clears the queue counters and the split-item counters before a launch.
-__global__ __launch_bounds__(256) void zero_counters_kernel(int32_t* counters, int32_t* split_cnt, int32_t n_split) {
+// Clears the queue counters, the split-item counters and the visit counters before a launch.
+__global__ __launch_bounds__(256) void zero_counters_kernel(int32_t* counters, int32_t* split_cnt, int32_t n_split,
+                                                            int32_t* visits, int32_t n_visits) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < kQueues) counters[i * kCounterStride] = 0;
   for (int j = i; j < n_split; j += gridDim.x * 256) split_cnt[j] = 0;
+  if (visits)
+    for (int j = i; j < n_visits; j += gridDim.x * 256) visits[j] = 0;
 }
 
 // S^T[key][q] of one block: kKb tiles of 32 keys, each a chain of k-steps over d.
@@ -445,7 +448,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   const int home = blockIdx.x % kQueues;
   int drained = 0;
   for (;;) {
-    if (tid == 0) s_item = take_item(p.queue, home, drained);
+    if (tid == 0) s_item = take_item(p.queue, home, drained, p.visits);
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item);  // the same for every lane
     if (item < 0) break;
@@ -633,8 +636,10 @@ int fwd_blocks_per_cu(int d) { return d == 64 ? blocks_per_cu_impl<64>() : block
 
 int launch_fwd(int d, const FwdParams& p, int grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const int zgrid = p.n_split > 0 ? (int)std::min<int64_t>(64, ((int64_t)p.n_split + 255) / 256) : 1;
-  hipLaunchKernelGGL(zero_counters_kernel, dim3(zgrid), dim3(256), 0, s, p.queue.counters, p.split_cnt, p.n_split);
+  const int64_t nz = std::max<int64_t>(p.n_split, p.visits ? p.n_visits : 0);
+  const int zgrid = nz > 0 ? (int)std::min<int64_t>(64, (nz + 255) / 256) : 1;
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(zgrid), dim3(256), 0, s, p.queue.counters, p.split_cnt, p.n_split,
+                     p.visits, p.n_visits);
   if (d == 64 && p.packed)
     hipLaunchKernelGGL((fwd_kernel<64, true>), dim3(grid), dim3(256), 0, s, p);
   else if (d == 64)

@@ -131,6 +131,8 @@ struct FwdParams {
   float* split_o;      // [n_split][kFwdRows][D] normalised piece results
   float* split_lse;    // [n_split][kFwdRows]
   int32_t packed;      // Q, K, V in the QKV-packed layout (selects the kernel instance)
+  int32_t* visits;     // per forward item: workgroups that took it (ZL_PLAN_COUNT_VISITS), or null
+  int32_t n_visits;    // forward items (counters cleared before the launch)
 };
 
 struct BwdParams {
@@ -161,6 +163,9 @@ struct BwdParams {
   int32_t n_kv_split;     // pieces of split dK/dV items (slots of kv_split_cnt, kv_split)
   int32_t* kv_split_cnt;  // per split dK/dV item (at its piece-0 slot): pieces finished
   float* kv_split;        // [n_kv_split][kBwdKeys][2][D] partial tau dK and dV of each piece
+  int32_t* kv_visits;     // per dK/dV item, per dQ item: workgroups that took it (ZL_PLAN_COUNT_VISITS),
+  int32_t* dq_visits;     // or null; both cleared by the pre-pass
+  int32_t n_kv_visits, n_dq_visits;
 };
 
 // Kernel launchers (defined next to their kernels). They return the launch status.

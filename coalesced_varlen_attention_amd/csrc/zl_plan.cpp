@@ -218,7 +218,8 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   *out = nullptr;
   if (d_head != 64 && d_head != 128)
     return fail(ZL_ERR_UNSUPPORTED, "zl_plan_build: d_head " + std::to_string(d_head) + " is not 64 or 128");
-  if (flags & ~(ZL_PLAN_HOST_ONLY | ZL_PLAN_NO_SPLIT | ZL_PLAN_QKV_PACKED)) return fail(ZL_ERR_INVALID, "zl_plan_build: unknown flag bits");
+  if (flags & ~(ZL_PLAN_HOST_ONLY | ZL_PLAN_NO_SPLIT | ZL_PLAN_QKV_PACKED | ZL_PLAN_COUNT_VISITS))
+    return fail(ZL_ERR_INVALID, "zl_plan_build: unknown flag bits");
   if (n_seq < 1) return fail(ZL_ERR_INVALID, "zl_plan_build: n_seq must be >= 1");
   if (!cu_q || !cu_kv || !seq_heads) return fail(ZL_ERR_INVALID, "zl_plan_build: NULL sequence array");
   if (n_seg < 1 || !segs) return fail(ZL_ERR_INVALID, "zl_plan_build: need at least one segment");

@@ -92,6 +92,11 @@ typedef struct {
   int32_t dq_split_pieces; /* pieces of those items */
   int32_t kv_split_tiles;  /* dK/dV items cut into pieces of their query blocks */
   int32_t kv_split_pieces; /* pieces of those items */
+  int64_t visits_fwd;      /* with ZL_PLAN_COUNT_VISITS: byte offset in the forward workspace of one
+                              int32 per forward work item (zl_plan_tiles order, which = 0) that
+                              counts the workgroups that took the item; -1 without the flag */
+  int64_t visits_dkdv;     /* the same in the backward workspace for the dK/dV queue (which = 1) */
+  int64_t visits_dq;       /* ... and for the dQ queue (which = 2) */
 } zl_plan_info_t;
 
 /*
@@ -123,6 +128,11 @@ typedef struct {
                                  do dQ, dK, dV; needs equal query and key lengths. Sequence s starts
                                  at packed row 3 * (its first planar row); O, LSE, dO stay planar.
                                  Pass the packed buffer as q, k and v (and as dq, dk, dv). */
+#define ZL_PLAN_COUNT_VISITS 8u /* scheduler check: every kernel also counts, per work item, the
+                                   workgroups that took it, in int32 counters the workspace gains at
+                                   the offsets zl_plan_info reports (visits_*). The forward launch
+                                   clears the forward's, the backward pre-pass the backward's. After
+                                   a forward and a backward every counter must read exactly 1. */
 
 /*
  * Validate the segment list and lower it into device work queues.
@@ -133,7 +143,8 @@ typedef struct {
  *   n_seg, segs           host array of segments (see zl_segment), n_seg >= 1
  *   d_head                64 or 128 (else ZL_ERR_UNSUPPORTED)
  *   softmax_scale         tau in softmax(tau * Q K^T); <= 0 selects 1/sqrt(d_head)
- *   flags                 0 or an OR of ZL_PLAN_HOST_ONLY, ZL_PLAN_NO_SPLIT, ZL_PLAN_QKV_PACKED
+ *   flags                 0 or an OR of ZL_PLAN_HOST_ONLY, ZL_PLAN_NO_SPLIT, ZL_PLAN_QKV_PACKED,
+ *                         ZL_PLAN_COUNT_VISITS
  *   out                   receives the plan; the caller frees it with zl_plan_destroy
  * The host arrays are copied; the plan owns its device tables (allocated on the current
  * device) and nothing else. The forward queue holds one item per (segment, head, block of

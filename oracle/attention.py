@@ -102,6 +102,12 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> T
     return o, lse
 
 
+def head_delta(o: np.ndarray, do: np.ndarray) -> np.ndarray:
+    """D_i = sum_c dO_ic O_ic for every query row: the row term of the exact softmax
+    backward (§V-A), taken from the final output rows O_i."""
+    return (do * o).sum(axis=1)
+
+
 def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, o: np.ndarray, lse: np.ndarray,
                   do: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Exact gradients of f = sum_i dO_i . O_i for one head (the exact backward of §V-A).
@@ -118,12 +124,21 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, o: np.ndarray, ls
     Passing a subset of the keys gives exact dK/dV rows for that subset; passing a
     subset of the queries (with their own O and LSE) gives exact dQ rows for them.
     """
+    return head_backward_delta(q, k, v, lse, head_delta(o, do), do, scale)
+
+
+def head_backward_delta(q: np.ndarray, k: np.ndarray, v: np.ndarray, lse: np.ndarray, dd: np.ndarray,
+                        do: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """``head_backward`` given each query row's ``D_i`` (``dd``) instead of its output row.
+
+    dK/dV of a key need every query row's LSE and D; this form lets a caller keep those two
+    numbers per row instead of whole output rows.
+    """
     lq = q.shape[0]
     nk = k.shape[0]
     dq = np.empty((lq, k.shape[1]), dtype=np.float64)
     dk = np.zeros(k.shape, dtype=np.float64)
     dv = np.zeros(v.shape, dtype=np.float64)
-    dd = (do * o).sum(axis=1)
     blk = _row_block(nk)
     buf_p = np.empty((min(blk, lq), nk), dtype=np.float64)
     buf_s = np.empty((min(blk, lq), nk), dtype=np.float64)

@@ -1,0 +1,101 @@
+"""Write tests/golden/long_rows_<pack>.npz: the fp64 oracle's per-row LSE and D of long heads.
+
+dK and dV of one key need every query row's log-sum-exp LSE_i and D_i = dO_i . O_i (the exact
+backward, Zellige page §V-A). For the longest heads of the benchmark packs the oracle needs
+minutes per head to produce them, too long for a test, so this script computes them once and
+the full-size parity test reads them back:
+  * mixed pack (seed 3): the 5 heads of the 75,600-token Ulysses shard (sequence 22);
+  * long pack (seed 5): heads 0 and 4 of the 497,760-token shard (sequence 0).
+Per head it stores LSE and D of every query row (rounded to float32 for storage: a relative
+error of 6e-8 in LSE or D moves p_ij and dS_ij by about that much, far inside the parity bar)
+and the sha256 of the head's bf16 Q, K, V and dO rows, so that the test uses the cache only
+on the inputs it was made from.
+
+Calls only ``oracle/`` (``head_forward``, ``head_delta``) and the seeded input generator of
+``workloads/``. The oracle is row-wise, so query rows are split into chunks that worker
+processes evaluate independently.
+
+Run from the repository root:  python tests/golden/make_long_rows.py [mixed|long] [--workers N]
+"""
+import argparse
+import hashlib
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+# (pack, sequence, heads) of the cached heads
+TARGETS = {"mixed": (22, (0, 1, 2, 3, 4)), "long": (0, (0, 4))}
+CHUNK = 2048
+
+_G = {}
+
+
+def path_for(name: str) -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), f"long_rows_{name}.npz")
+
+
+def head_rows(pack, ins, s: int, h: int):
+    """The bf16 Q, K, V, dO rows of (sequence s, head h) over the whole sequence."""
+    import oracle
+    lay = oracle.PackLayout(pack.seq_q, pack.seq_kv, pack.heads)
+    qi = lay.q_index(s, 0, pack.seq_q[s], h)
+    ki = lay.kv_index(s, 0, pack.seq_kv[s], h)
+    return {"q": ins["q"][qi], "k": ins["k"][ki], "v": ins["v"][ki], "do": ins["do"][qi]}
+
+
+def digest(rows: dict) -> dict:
+    return {n: hashlib.sha256(rows[n].contiguous().view(dtype=__import__("torch").uint8).numpy().tobytes()).hexdigest()
+            for n in ("q", "k", "v", "do")}
+
+
+def _chunk(i0: int):
+    import oracle
+    q, k, v, do, tau = _G["q"], _G["k"], _G["v"], _G["do"], _G["tau"]
+    i1 = min(q.shape[0], i0 + CHUNK)
+    o, lse = oracle.head_forward(q[i0:i1], k, v, tau)
+    return i0, lse, oracle.head_delta(o, do[i0:i1])
+
+
+def compute(name: str, workers: int) -> None:
+    import torch
+    import workloads as W
+    pack = W.config(name)
+    ins = W.draw(pack)
+    s, heads = TARGETS[name]
+    out = {"pack": np.array(name), "seed": np.array(pack.seed), "seq": np.array(s), "heads": np.array(heads)}
+    for h in heads:
+        rows = head_rows(pack, ins, s, h)
+        f64 = lambda t: t.to(torch.float64).numpy()
+        _G.update(q=f64(rows["q"]), k=f64(rows["k"]), v=f64(rows["v"]), do=f64(rows["do"]), tau=pack.softmax_scale())
+        n = _G["q"].shape[0]
+        lse = np.empty(n)
+        dd = np.empty(n)
+        t0 = time.time()
+        with mp.get_context("fork").Pool(workers) as pool:
+            for k, (i0, l, d) in enumerate(pool.imap_unordered(_chunk, range(0, n, CHUNK))):
+                lse[i0:i0 + l.size] = l
+                dd[i0:i0 + d.size] = d
+                if k % 50 == 0:
+                    print(f"  {name} head {h}: {k * CHUNK}/{n} rows, {time.time() - t0:.0f} s", flush=True)
+        for key, val in digest(rows).items():
+            out[f"sha_{key}_{h}"] = np.array(val)
+        out[f"lse_{h}"] = lse.astype(np.float32)
+        out[f"d_{h}"] = dd.astype(np.float32)
+        print(f"{name} head {h}: {n} rows in {time.time() - t0:.0f} s", flush=True)
+    np.savez_compressed(path_for(name), **out)
+    print("wrote", path_for(name))
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("packs", nargs="*", default=["mixed", "long"])
+    ap.add_argument("--workers", type=int, default=max(1, (os.cpu_count() or 2) - 1))
+    args = ap.parse_args()
+    for p in args.packs:
+        compute(p, args.workers)

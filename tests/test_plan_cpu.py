@@ -205,7 +205,7 @@ def test_bad_sequence_arrays():
                            ctypes.addressof(seg), 64, 0.0, 1, ctypes.byref(out))
     assert st == ZL_ERR_INVALID and b"seq_heads" in lib.zl_last_error()
     st = lib.zl_plan_build(1, ctypes.addressof(cu), ctypes.addressof(cu), ctypes.addressof(heads), 1,
-                           ctypes.addressof(seg), 64, 0.0, 8, ctypes.byref(out))
+                           ctypes.addressof(seg), 64, 0.0, 16, ctypes.byref(out))
     assert st == ZL_ERR_INVALID and b"flag" in lib.zl_last_error()
     assert lib.zl_plan_build(1, None, None, None, 1, None, 64, 0.0, 1, ctypes.byref(out)) == ZL_ERR_INVALID
 
@@ -422,3 +422,21 @@ def test_dkdv_split_cuts_items_of_a_short_queue():
     # a counter and 128 keys x (dK, dV) rows of partials per piece
     assert p.info["ws_bwd"] - nosplit.info["ws_bwd"] >= 256 * (4 + 128 * 2 * 128 * 4)
     assert sorted(t[:4] for t in nosplit.tiles(1)) == sorted(set(t[:4] for t in p.tiles(1)))
+
+
+def test_visit_counters_layout():
+    """ZL_PLAN_COUNT_VISITS adds one int32 per work item of each queue at the end of the
+    workspaces, at the offsets the plan reports; without the flag the offsets are -1 and the
+    workspaces keep their size."""
+    pack = W.config("mixed")
+    plain = host_plan(pack)
+    p = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale, host_only=True,
+               count_visits=True)
+    a, b = plain.info, p.info
+    assert a["visits_fwd"] == a["visits_dkdv"] == a["visits_dq"] == -1
+    assert b["visits_fwd"] == a["ws_fwd"] and b["visits_dkdv"] == a["ws_bwd"]
+    assert b["ws_fwd"] >= b["visits_fwd"] + 4 * b["fwd_tiles"]
+    assert b["visits_dq"] >= b["visits_dkdv"] + 4 * b["bwd_tiles"]
+    assert b["ws_bwd"] >= b["visits_dq"] + 4 * b["dq_tiles"]
+    assert all(x % 256 == 0 for x in (b["visits_fwd"], b["visits_dkdv"], b["visits_dq"]))
+    assert p.tiles(0) == plain.tiles(0) and p.tiles(1) == plain.tiles(1) and p.tiles(2) == plain.tiles(2)

@@ -1,0 +1,72 @@
+"""Scheduler check on the GPU: every work item of every queue is taken by exactly one workgroup.
+
+The three persistent kernels pull items from per-XCD queues with one atomic per take and steal
+from the other queues once their own is empty (the lowering of a rank-local schedule into one
+launch, Zellige page §IV-D). A plan built with ZL_PLAN_COUNT_VISITS counts, per item, the
+workgroups that took it. Covering every output row (the NaN fills of the parity tests) shows
+"at least once"; the counters show "exactly once", which the split items rely on: their
+last-piece counters finish only if every piece runs once.
+
+Packs: the mixed image-video pack (the benchmark's), one head of a 32,760-token video (forward
+and dQ items split into pieces), one head of 8,192 tokens (forward, dQ and dK/dV items split),
+and the ring shard (dQ items walking 8-part key chains). The counting plan's outputs must also equal a plain plan's bit for bit: the items and
+their order are the same, and every output is written once by one workgroup.
+"""
+import pytest
+import torch
+
+import workloads as W
+from tests import gpu_harness as H
+
+pytestmark = [pytest.mark.gpu, H.requires_gpu]
+
+
+def _run(plan, pack, ins, dev):
+    z = H.zl()
+    info = plan.info
+    q, k, v, do = (ins[n].to(dev) for n in ("q", "k", "v", "do"))
+    ws_f = torch.zeros(info["ws_fwd"], dtype=torch.uint8, device=dev)
+    ws_b = torch.zeros(info["ws_bwd"], dtype=torch.uint8, device=dev)
+    o, lse, o_part, lse_part = z.attn_fwd(plan, q, k, v, workspace=ws_f)
+    if info["n_groups"]:
+        z.merge_groups(plan, o_part, lse_part, o, lse)
+    dq, dk, dv = z.attn_bwd(plan, q, k, v, o, lse, do, workspace=ws_b)
+    torch.cuda.synchronize()
+    return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, ws_f, ws_b
+
+
+def _pack(name):
+    if name == "head8k":  # one head of 8,192 tokens: forward, dQ and dK/dV items all split
+        return W.Pack("head8k", (8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, 8)
+    return W.config(name)
+
+
+@pytest.mark.parametrize("name", ["mixed", "head1", "head8k", "ring"])
+def test_every_item_taken_exactly_once(name):
+    z = H.zl()
+    pack = _pack(name)
+    print(f"[case] visits {name}", flush=True)
+    dev = torch.device("cuda:0")
+    ins = W.draw(pack)
+    plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale, count_visits=True)
+    info = plan.info
+    if name == "head1":
+        assert info["split_tiles"] > 0 and info["dq_split_tiles"] > 0
+    if name == "head8k":
+        assert info["split_tiles"] > 0 and info["dq_split_tiles"] > 0 and info["kv_split_tiles"] > 0
+    out, ws_f, ws_b = _run(plan, pack, ins, dev)
+    counts = plan.visits(ws_f, ws_b)
+    for key, n_items in (("fwd", info["fwd_tiles"]), ("dkdv", info["bwd_tiles"]), ("dq", info["dq_tiles"])):
+        c = counts[key]
+        assert c.numel() == n_items
+        print(f"  {key}: {n_items} items, visits min {int(c.min())} max {int(c.max())}", flush=True)
+        assert bool((c == 1).all()), f"{key}: items taken {int((c == 0).sum())} x never, {int((c > 1).sum())} x more than once"
+    # the same plan without counters gives the same bits
+    plain = H.make_plan(pack)
+    ref, _, _ = _run(plain, pack, ins, dev)
+    for n in out:
+        assert torch.equal(out[n], ref[n]), f"{n}: the counting plan's output differs from the plain plan's"
+    # a second forward + backward on the same workspaces: the launches clear the counters
+    out2, _, _ = _run(plan, pack, ins, dev)
+    counts = plan.visits(ws_f, ws_b)
+    assert all(bool((c == 1).all()) for c in counts.values())

@@ -144,3 +144,25 @@ def draw(pack: Pack, seed: Optional[int] = None) -> dict:
 
 def sha256(t: torch.Tensor) -> str:
     return hashlib.sha256(t.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()
+
+
+def draw_partials(n_parts: int, n_rows: int, d: int, seed: int, empty_frac: float = 0.0,
+                  empty_rows: int = 0) -> dict:
+    """A synthetic ring partial slab: ``o_part`` fp32 ``[n_parts, n_rows, d]`` and ``lse_part``
+    fp32 ``[n_parts, n_rows]``, shaped like what ring parts of long sequences emit.
+
+    Values: normalised partial outputs of a long block are averages of many unit-variance value
+    rows, so ``o_part`` is N(0, 0.05^2); a part's log-sum-exp is about ln(block keys) plus a
+    spread, so ``lse_part`` is 9 + 2 N(0, 1). ``empty_frac`` of the (part, row) entries get
+    ``lse = -inf`` (a part that contributed no keys to the row), and the last ``empty_rows``
+    rows are -inf in every part. Draw order: o_part, lse_part, then the empty mask.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    o = 0.05 * torch.randn(n_parts, n_rows, d, generator=g, dtype=torch.float32)
+    lse = 9.0 + 2.0 * torch.randn(n_parts, n_rows, generator=g, dtype=torch.float32)
+    if empty_frac > 0:
+        lse[torch.rand(n_parts, n_rows, generator=g) < empty_frac] = float("-inf")
+    if empty_rows > 0:
+        lse[:, n_rows - empty_rows:] = float("-inf")
+    return {"o_part": o, "lse_part": lse}
