@@ -29,8 +29,8 @@ import ctypes
 import os
 from typing import List, Optional, Sequence, Tuple
 
-__all__ = ["Plan", "ZlError", "attn_fwd", "attn_fwd_accumulate", "attn_bwd", "lse_merge", "merge_groups", "lib",
-           "lib_path", "SEGMENT_FIELDS"]
+__all__ = ["Plan", "ZlError", "attn_fwd", "attn_fwd_accumulate", "attn_bwd", "attn_bwd_noalloc", "lse_merge",
+           "merge_groups", "lib", "lib_path", "SEGMENT_FIELDS", "NOALLOC_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libzl.so")
@@ -40,6 +40,7 @@ ZL_PLAN_NO_SPLIT = 2
 ZL_PLAN_QKV_PACKED = 4
 ZL_PLAN_COUNT_VISITS = 8
 BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ZL_NOALLOC_SCRATCH_BYTES
 SEGMENT_FIELDS = ("seq", "head_begin", "head_end", "q_begin", "q_end", "kv_begin", "kv_end", "part")
 
 
@@ -93,6 +94,7 @@ def _load() -> ctypes.CDLL:
         "zl_plan_merge": (I32, [P, P, P, P, P, P]),
         "zl_attn_bwd": (I32, [P, P, P, P, P, P, P, P, P, P, P, P]),
         "zl_attn_bwd_stages": (I32, [P, P, P, P, P, P, P, P, P, P, P, U32, P]),
+        "zl_attn_bwd_noalloc": (I32, [P, P, P, P, P, P, P, P, P, P, P]),
         "zl_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -389,4 +391,26 @@ def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspa
     _check(lib().zl_attn_bwd_stages(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                    lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                    workspace.data_ptr(), int(stages), _stream_handle(stream)))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(plan: Plan, q, k, v, o, lse, do, dq, dk, dv, stream=None):
+    """The backward with the library's fixed device scratch (``zl_attn_bwd_noalloc``): for
+    callers that cannot allocate. The caller passes every output; calls on one device must
+    not overlap. Returns ``(dq, dk, dv)``."""
+    import torch
+    info, d, dev = plan.info, plan.d, _gpu_device(q, "q")
+    rq, rkv = _input_rows(info)
+    _check_tensor(q, "q", torch.bfloat16, rq, d, dev)
+    _check_tensor(k, "k", torch.bfloat16, rkv, d, dev)
+    _check_tensor(v, "v", torch.bfloat16, rkv, d, dev)
+    _check_tensor(do, "do", torch.bfloat16, info["q_rows"], d, dev)
+    _check_tensor(o, "o", torch.float32, info["q_rows"], d, dev)
+    _check_tensor(lse, "lse", torch.float32, info["q_rows"], 1, dev)
+    _check_tensor(dq, "dq", torch.float32, rq, d, dev)
+    _check_tensor(dk, "dk", torch.float32, rkv, d, dev)
+    _check_tensor(dv, "dv", torch.float32, rkv, d, dev)
+    _check(lib().zl_attn_bwd_noalloc(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                     lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                     _stream_handle(stream)))
     return dq, dk, dv

@@ -309,6 +309,24 @@ zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, const void* k, 
                              const float* o, const float* lse, const void* d_o,
                              float* dq, float* dk, float* dv, void* workspace, uint32_t stages, void* stream);
 
+/*
+ * The backward of zl_attn_bwd with no workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The scratch zl_attn_bwd keeps in its workspace (queue counters, -D and -LSE / tau
+ * per query row, sentinel rows, split partials) lives instead in a fixed device array of
+ * ZL_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on until the process
+ * ends; its address is looked up on the first call on each device. Nothing is allocated or
+ * freed. Plans whose info.ws_bwd exceeds ZL_NOALLOC_SCRATCH_BYTES are rejected with
+ * ZL_ERR_UNSUPPORTED. Every call on a device shares that device's array: calls that overlap
+ * on one device (two streams, or two threads) race and must be ordered by the caller. Each
+ * call rewrites what it reads of the array, so no clearing is needed between calls. Arguments
+ * and results as for zl_attn_bwd; the same kernels run.
+ */
+#define ZL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+zl_status zl_attn_bwd_noalloc(const zl_plan* plan, const void* q, const void* k, const void* v,
+                              const float* o, const float* lse, const void* d_o,
+                              float* dq, float* dk, float* dv, void* stream);
+
 /* Thread-local message describing the last failure on this thread ("" if none). */
 const char* zl_last_error(void);
 
