@@ -339,6 +339,21 @@ def main() -> int:
                                       split=not args.no_split))
         ws_f = torch.empty(max(fp.info["ws_fwd"] for fp in fold_plans), dtype=torch.uint8, device=dev)
     group_rows = [(g["o_row"], g["n_rows"]) for g in plan.groups]
+    # The exact merge of ring partials: zl_lse_merge per group when every group covers all of its
+    # sequence's stored heads (its O/LSE rows are then contiguous), else zl_plan_merge (one launch
+    # for every group, head subsets at their strided rows).
+    lse_merge_calls = None
+    if has_groups and all(g["head_end"] - g["head_begin"] == g["n_heads"] for g in plan.groups):
+        lse_merge_calls = [(g["n_parts"], g["n_rows"], o_part[g["part_row"]:], lse_part[g["part_row"]:],
+                            o[g["o_row"]:g["o_row"] + g["n_rows"]], lse[g["o_row"]:g["o_row"] + g["n_rows"]])
+                           for g in plan.groups]
+
+    def merge():
+        if lse_merge_calls is not None:
+            for (n_parts, n_rows, op, lp, oo, ll) in lse_merge_calls:
+                zl.lse_merge(n_parts, n_rows, pack.d, op, lp, oo, ll)
+        else:
+            zl.merge_groups(plan, o_part, lse_part, o, lse)
 
     def forward():
         if fold_plans:
@@ -356,7 +371,7 @@ def main() -> int:
         forward()
         rec(1)
         if has_groups and not fold_plans:
-            zl.merge_groups(plan, o_part, lse_part, o, lse)
+            merge()
         rec(2)
         zl.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b, stages=zl.BWD_PRE)
         rec(3)
@@ -455,7 +470,8 @@ def main() -> int:
                        "step_ms_events": {"median": round(per_step[len(per_step) // 2], 3),
                                           "min": round(per_step[0], 3), "max": round(per_step[-1], 3)},
                        "ring_forward": (f"running merge, {len(fold_plans)} launches" if fold_plans
-                                        else "partials + LSE merge" if has_groups else "none"),
+                                        else ("partials + zl_lse_merge" if lse_merge_calls is not None
+                                              else "partials + zl_plan_merge") if has_groups else "none"),
                        "split_kv": {"fwd_items_split": info["split_tiles"], "pieces": info["split_pieces"],
                                     "dq_items_split": info["dq_split_tiles"], "dq_pieces": info["dq_split_pieces"],
                                     "dkdv_items_split": info["kv_split_tiles"], "dkdv_pieces": info["kv_split_pieces"]}},

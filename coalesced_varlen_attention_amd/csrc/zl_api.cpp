@@ -292,13 +292,9 @@ extern "C" zl_status zl_lse_merge(int32_t n_parts, int64_t n_rows, int32_t d_hea
   if (!o_part || !lse_part || !o || !lse) return fail(ZL_ERR_INVALID, "zl_lse_merge: NULL pointer");
   if (!aligned(o_part, 16) || !aligned(o, 16) || !aligned(lse_part, 4) || !aligned(lse, 4))
     return fail(ZL_ERR_INVALID, "zl_lse_merge: o_part and o must be 16-byte aligned, lse 4-byte");
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
-    return fail(ZL_ERR_HIP, "zl_lse_merge: cannot query the device");
-  const int rows_per_block = 256 / (d_head / 4);
+  const int rows_per_block = zl::merge_rows(d_head);
   const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
-  const int grid = (int)std::min<int64_t>(blocks, (int64_t)n_cu * 16);
+  const int grid = (int)std::min<int64_t>(blocks, zl::kMergeMaxGrid);
   return launch_status(zl::launch_merge(d_head, n_parts, n_rows, o_part, lse_part, o, lse, grid, stream),
                        "zl_lse_merge");
 }
@@ -311,7 +307,7 @@ extern "C" zl_status zl_plan_merge(const zl_plan* plan, const float* o_part, con
   if (!o_part || !lse_part || !o || !lse) return fail(ZL_ERR_INVALID, "zl_plan_merge: NULL pointer");
   if (!aligned(o_part, 16) || !aligned(o, 16) || !aligned(lse_part, 4) || !aligned(lse, 4))
     return fail(ZL_ERR_INVALID, "zl_plan_merge: o_part and o must be 16-byte aligned, lse 4-byte");
-  const int grid = (int)std::min<int64_t>(plan->merge_blocks, (int64_t)plan->n_cu * 16);
+  const int grid = (int)std::min<int64_t>(plan->merge_blocks, zl::kMergeMaxGrid);
   return launch_status(zl::launch_plan_merge(plan->d, plan->d_groups, (int32_t)plan->gdev.size(), plan->merge_blocks,
                                              o_part, lse_part, o, lse, grid, stream),
                        "zl_plan_merge");

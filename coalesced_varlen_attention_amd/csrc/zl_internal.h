@@ -91,8 +91,10 @@ struct alignas(16) GroupDev {
 };
 static_assert(sizeof(GroupDev) == 48, "GroupDev must stay 48 bytes");
 
-// Rows one merge workgroup (256 lanes, d/4 lanes per row) handles per pass.
+// Rows one merge workgroup (256 lanes, d/4 lanes per row) handles per pass; merge launches use
+// one workgroup per pass up to kMergeMaxGrid workgroups.
 constexpr int merge_rows(int d) { return 256 / (d / 4); }
+constexpr int64_t kMergeMaxGrid = INT64_C(1) << 20;
 
 // One work item: segment index, head, first row (token) of the block, rows in the block, and
 // the range it loops over: for a forward item its keys [kv_begin, kv_end) (the segment's, or a

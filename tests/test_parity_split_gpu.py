@@ -147,11 +147,11 @@ def test_dq_split_reproducible_and_close_to_unsplit():
 def test_dkdv_split_many_queries(d):
     """Few keys, many queries: the dK/dV items (128 keys each) loop over 47 query blocks of 64
     rows (the last one ragged) and are cut into runs of them; the last piece of each item adds
-    the partial dK and dV. dV sums over 3000 queries, so its magnitude is well above 1 and the
-    max-abs bound scales with it (rel-L2 unchanged)."""
+    the partial dK and dV. dV sums over 3000 queries, so its rows' magnitudes are well above 1:
+    each element's max-abs bound scales with its own row's magnitude (rel-L2 unchanged)."""
     pack = W.Pack(f"kv_split{d}", (3000,), (500,), (2,), ((0, 0, 2, 0, 3000, 0, 500, -1),), d, 101 + d)
     ins = W.draw(pack)
     print(f"[case] {pack.name} d={pack.d} seqs={pack.seq_q}/{pack.seq_kv}", flush=True)
     out = H.run_pack(pack, ins)
     assert out["plan"].info["kv_split_tiles"] > 0, "the dK/dV queue was meant to be split"
-    H.compare_full(pack, ins, out, H.oracle_pack(pack, ins), scaled_max_abs=True)
+    H.compare_full(pack, ins, out, H.oracle_pack(pack, ins), row_scaled=True)
