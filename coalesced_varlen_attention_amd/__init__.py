@@ -39,6 +39,7 @@ ZL_PLAN_HOST_ONLY = 1
 ZL_PLAN_NO_SPLIT = 2
 ZL_PLAN_QKV_PACKED = 4
 ZL_PLAN_COUNT_VISITS = 8
+ZL_PLAN_DEFERRED_UPLOAD = 16
 BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ZL_NOALLOC_SCRATCH_BYTES
 SEGMENT_FIELDS = ("seq", "head_begin", "head_end", "q_begin", "q_end", "kv_begin", "kv_end", "part")
@@ -65,7 +66,8 @@ class _PlanInfo(ctypes.Structure):
                 ("split_pieces", ctypes.c_int32), ("qkv_rows", ctypes.c_int64),
                 ("dq_split_tiles", ctypes.c_int32), ("dq_split_pieces", ctypes.c_int32),
                 ("kv_split_tiles", ctypes.c_int32), ("kv_split_pieces", ctypes.c_int32),
-                ("visits_fwd", ctypes.c_int64), ("visits_dkdv", ctypes.c_int64), ("visits_dq", ctypes.c_int64)]
+                ("visits_fwd", ctypes.c_int64), ("visits_dkdv", ctypes.c_int64), ("visits_dq", ctypes.c_int64),
+                ("dev_bytes", ctypes.c_size_t)]
 
 
 class _GroupInfo(ctypes.Structure):
@@ -88,6 +90,7 @@ def _load() -> ctypes.CDLL:
         "zl_plan_tiles": (I32, [P, I32, P, I64, ctypes.POINTER(I64)]),
         "zl_plan_queues": (I32, [P, I32, P, I32, ctypes.POINTER(I32)]),
         "zl_plan_destroy": (None, [P]),
+        "zl_plan_upload": (I32, [P, P, ctypes.c_size_t, P]),
         "zl_attn_fwd": (I32, [P, P, P, P, P, P, P, P, P, P]),
         "zl_attn_fwd_accumulate": (I32, [P, P, P, P, P, P, P, P]),
         "zl_lse_merge": (I32, [I32, I64, I32, P, P, P, P, P]),
@@ -140,11 +143,12 @@ class Plan:
     ``seq_q``/``seq_kv``: tokens per sequence; ``heads``: stored heads per sequence;
     ``segments``: tuples ``(seq, head_begin, head_end, q_begin, q_end, kv_begin, kv_end, part)``.
     ``count_visits``: the scheduler check of ``ZL_PLAN_COUNT_VISITS`` (read with ``visits``).
+    ``deferred``: ``ZL_PLAN_DEFERRED_UPLOAD``; the plan runs after ``upload()``.
     """
 
     def __init__(self, seq_q: Sequence[int], seq_kv: Sequence[int], heads: Sequence[int], segments, d: int,
                  scale: Optional[float] = None, host_only: bool = False, split: bool = True,
-                 qkv_packed: bool = False, count_visits: bool = False):
+                 qkv_packed: bool = False, count_visits: bool = False, deferred: bool = False):
         n = len(seq_q)
         if len(seq_kv) != n or len(heads) != n:
             raise ValueError("seq_q, seq_kv and heads must have the same length")
@@ -160,7 +164,9 @@ class Plan:
                 setattr(segs[i], name, int(val))
         self._h = ctypes.c_void_p()
         flags = ((ZL_PLAN_HOST_ONLY if host_only else 0) | (0 if split else ZL_PLAN_NO_SPLIT) |
-                 (ZL_PLAN_QKV_PACKED if qkv_packed else 0) | (ZL_PLAN_COUNT_VISITS if count_visits else 0))
+                 (ZL_PLAN_QKV_PACKED if qkv_packed else 0) | (ZL_PLAN_COUNT_VISITS if count_visits else 0) |
+                 (ZL_PLAN_DEFERRED_UPLOAD if deferred else 0))
+        self._tables = None
         _check(lib().zl_plan_build(n, ctypes.cast(cu_q, ctypes.c_void_p), ctypes.cast(cu_kv, ctypes.c_void_p),
                                   ctypes.cast(hs, ctypes.c_void_p), len(segments), ctypes.cast(segs, ctypes.c_void_p),
                                   int(d), float(scale) if scale else 0.0, flags, ctypes.byref(self._h)))
@@ -196,6 +202,19 @@ class Plan:
         buf = (ctypes.c_int32 * 64)()
         _check(lib().zl_plan_queues(self._h, which, ctypes.cast(buf, ctypes.c_void_p), 64, ctypes.byref(n)))
         return list(buf[: n.value + 1])
+
+    def upload(self, buffer=None, stream=None):
+        """Copy a deferred plan's device tables into ``buffer`` (a device uint8 tensor of at least
+        ``info["dev_bytes"]`` bytes, allocated here if None) on ``stream`` (default: the current
+        stream), without waiting for the device (``zl_plan_upload``). The plan keeps a reference to
+        the buffer. Returns the buffer."""
+        import torch
+        if buffer is None:
+            buffer = torch.empty(self.info["dev_bytes"], dtype=torch.uint8, device="cuda")
+        _check_workspace(buffer, self.info["dev_bytes"], _gpu_device(buffer, "buffer"))
+        _check(lib().zl_plan_upload(self._h, buffer.data_ptr(), buffer.numel(), _stream_handle(stream)))
+        self._tables = buffer
+        return buffer
 
     def visits(self, ws_fwd=None, ws_bwd=None) -> dict:
         """Per-item visit counters of a ``count_visits`` plan, read from the workspaces of the last

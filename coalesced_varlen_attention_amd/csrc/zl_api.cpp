@@ -100,7 +100,10 @@ void set_fwd_visits(const zl_plan* plan, void* workspace, zl::FwdParams* p) {
 
 zl_status check_runnable(const zl_plan* plan, const char* who) {
   if (!plan) return fail(ZL_ERR_INVALID, std::string(who) + ": plan is NULL");
-  if (!plan->dev_block) return fail(ZL_ERR_INVALID, std::string(who) + ": plan was built host-only and cannot run");
+  if (!plan->d_segs)
+    return fail(ZL_ERR_INVALID, std::string(who) + ((plan->flags & ZL_PLAN_DEFERRED_UPLOAD)
+                                                        ? ": the plan's tables were not uploaded (zl_plan_upload)"
+                                                        : ": plan was built host-only and cannot run"));
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(ZL_ERR_HIP, std::string(who) + ": hipGetDevice failed");
   if (dev != plan->device)
@@ -156,6 +159,7 @@ extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   info->dq_split_pieces = plan->dq_split_pieces;
   info->kv_split_tiles = plan->kv_split_tiles;
   info->kv_split_pieces = plan->kv_split_pieces;
+  info->dev_bytes = plan->dev_bytes;
   info->visits_fwd = info->visits_dkdv = info->visits_dq = -1;
   if (counts_visits(plan)) {
     info->visits_fwd = (int64_t)fwd_visit_offset(plan);

@@ -186,6 +186,11 @@ void set_error(const std::string& msg);
 
 }  // namespace zl
 
+struct zl_plan;
+namespace zl {
+void set_table_pointers(zl_plan* plan, void* block);
+}  // namespace zl
+
 struct zl_plan {
   int32_t d = 0;
   int32_t n_seq = 0;
@@ -209,7 +214,13 @@ struct zl_plan {
   int32_t dq_split_pieces = 0;  // pieces of those items (slots of the backward split workspace)
   int32_t kv_split_tiles = 0;   // dK/dV items cut into pieces of their query blocks
   int32_t kv_split_pieces = 0;  // pieces of those items
-  // device copies (one allocation, carved into the three tables)
+  // device copies: one block carved into the tables at table_off (segments, forward, dK/dV,
+  // pre-pass and dQ items, key-range chains, queue bounds, groups); owned (dev_block) unless the
+  // plan was built with ZL_PLAN_DEFERRED_UPLOAD, whose tables zl_plan_upload copies into caller
+  // memory from `image` (kept until then)
+  size_t dev_bytes = 0;
+  size_t table_off[8] = {};
+  std::vector<char> image;
   void* dev_block = nullptr;
   const zl::SegDev* d_segs = nullptr;
   const zl::Tile* d_fwd = nullptr;

@@ -19,10 +19,28 @@
 #include <cstring>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <new>
 #include <tuple>
 
 #include "zl_internal.h"
+
+namespace zl {
+
+// Point the plan's device table pointers into a block laid out as the plan's image.
+void set_table_pointers(zl_plan* plan, void* block) {
+  char* b = (char*)block;
+  plan->d_segs = (const SegDev*)(b + plan->table_off[0]);
+  plan->d_fwd = (const Tile*)(b + plan->table_off[1]);
+  plan->d_bwd = (const Tile*)(b + plan->table_off[2]);
+  plan->d_pre = (const Tile*)(b + plan->table_off[3]);
+  plan->d_dq = (const Tile*)(b + plan->table_off[4]);
+  plan->d_ranges = (const int32_t*)(b + plan->table_off[5]);
+  plan->d_bounds = (const int32_t*)(b + plan->table_off[6]);
+  plan->d_groups = (const GroupDev*)(b + plan->table_off[7]);
+}
+
+}  // namespace zl
 
 namespace {
 
@@ -218,7 +236,8 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   *out = nullptr;
   if (d_head != 64 && d_head != 128)
     return fail(ZL_ERR_UNSUPPORTED, "zl_plan_build: d_head " + std::to_string(d_head) + " is not 64 or 128");
-  if (flags & ~(ZL_PLAN_HOST_ONLY | ZL_PLAN_NO_SPLIT | ZL_PLAN_QKV_PACKED | ZL_PLAN_COUNT_VISITS))
+  if (flags & ~(ZL_PLAN_HOST_ONLY | ZL_PLAN_NO_SPLIT | ZL_PLAN_QKV_PACKED | ZL_PLAN_COUNT_VISITS |
+                ZL_PLAN_DEFERRED_UPLOAD))
     return fail(ZL_ERR_INVALID, "zl_plan_build: unknown flag bits");
   if (n_seq < 1) return fail(ZL_ERR_INVALID, "zl_plan_build: n_seq must be >= 1");
   if (!cu_q || !cu_kv || !seq_heads) return fail(ZL_ERR_INVALID, "zl_plan_build: NULL sequence array");
@@ -499,55 +518,46 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   distribute(dq, dq_unit, &plan->dq_tiles, &plan->dq_bounds);
 
   if (!(flags & ZL_PLAN_HOST_ONLY)) {
+    // One image of every device table, carved at 256-byte aligned offsets.
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t b_segs = align(plan->segs.size() * sizeof(zl::SegDev));
-    const size_t b_fwd = align(plan->fwd_tiles.size() * sizeof(zl::Tile));
-    const size_t b_bwd = align(plan->bwd_tiles.size() * sizeof(zl::Tile));
-    const size_t b_pre = align(plan->pre_tiles.size() * sizeof(zl::Tile));
-    const size_t b_dq = align(plan->dq_tiles.size() * sizeof(zl::Tile));
-    const size_t b_rng = align(plan->kv_ranges.size() * sizeof(int32_t));
-    const size_t b_bnd = align(3 * (zl::kQueues + 1) * sizeof(int32_t));
-    const size_t b_grp = align(plan->gdev.size() * sizeof(zl::GroupDev));
-    const size_t total = b_segs + b_fwd + b_bwd + b_pre + b_dq + b_rng + b_bnd + b_grp;
-    if (hipMalloc(&plan->dev_block, total) != hipSuccess) {
-      plan->dev_block = nullptr;
-      (void)hipGetLastError();
-      return fail(ZL_ERR_NOMEM, "zl_plan_build: hipMalloc of " + std::to_string(total) + " bytes failed");
-    }
-    char* base = (char*)plan->dev_block;
-    size_t off = 0;
-    auto carve = [&](size_t bytes) {
-      char* p = base + off;
-      off += bytes;
-      return (void*)p;
-    };
-    plan->d_segs = (const zl::SegDev*)carve(b_segs);
-    plan->d_fwd = (const zl::Tile*)carve(b_fwd);
-    plan->d_bwd = (const zl::Tile*)carve(b_bwd);
-    plan->d_pre = (const zl::Tile*)carve(b_pre);
-    plan->d_dq = (const zl::Tile*)carve(b_dq);
-    plan->d_ranges = (const int32_t*)carve(b_rng);
-    plan->d_bounds = (const int32_t*)carve(b_bnd);
-    plan->d_groups = (const zl::GroupDev*)carve(b_grp);
-    hipError_t e = hipSuccess;
-    auto up = [&](const void* dst, const void* src, size_t bytes) {
-      if (e == hipSuccess && bytes) e = hipMemcpy((void*)dst, src, bytes, hipMemcpyHostToDevice);
-    };
-    up(plan->d_segs, plan->segs.data(), plan->segs.size() * sizeof(zl::SegDev));
-    up(plan->d_fwd, plan->fwd_tiles.data(), plan->fwd_tiles.size() * sizeof(zl::Tile));
-    up(plan->d_bwd, plan->bwd_tiles.data(), plan->bwd_tiles.size() * sizeof(zl::Tile));
-    up(plan->d_pre, plan->pre_tiles.data(), plan->pre_tiles.size() * sizeof(zl::Tile));
-    up(plan->d_dq, plan->dq_tiles.data(), plan->dq_tiles.size() * sizeof(zl::Tile));
-    up(plan->d_ranges, plan->kv_ranges.data(), plan->kv_ranges.size() * sizeof(int32_t));
     std::vector<int32_t> all_bounds;
     for (const auto* b : {&plan->fwd_bounds, &plan->bwd_bounds, &plan->dq_bounds})
       all_bounds.insert(all_bounds.end(), b->begin(), b->end());
-    up(plan->d_bounds, all_bounds.data(), all_bounds.size() * sizeof(int32_t));
-    up(plan->d_groups, plan->gdev.data(), plan->gdev.size() * sizeof(zl::GroupDev));
-    if (e != hipSuccess) {
-      (void)hipFree(plan->dev_block);
-      plan->dev_block = nullptr;
-      return fail(ZL_ERR_HIP, std::string("zl_plan_build: upload failed: ") + hipGetErrorString(e));
+    const struct {
+      const void* src;
+      size_t bytes;
+    } parts[] = {{plan->segs.data(), plan->segs.size() * sizeof(zl::SegDev)},
+                 {plan->fwd_tiles.data(), plan->fwd_tiles.size() * sizeof(zl::Tile)},
+                 {plan->bwd_tiles.data(), plan->bwd_tiles.size() * sizeof(zl::Tile)},
+                 {plan->pre_tiles.data(), plan->pre_tiles.size() * sizeof(zl::Tile)},
+                 {plan->dq_tiles.data(), plan->dq_tiles.size() * sizeof(zl::Tile)},
+                 {plan->kv_ranges.data(), plan->kv_ranges.size() * sizeof(int32_t)},
+                 {all_bounds.data(), all_bounds.size() * sizeof(int32_t)},
+                 {plan->gdev.data(), plan->gdev.size() * sizeof(zl::GroupDev)}};
+    size_t total = 0;
+    for (int i = 0; i < 8; ++i) {
+      plan->table_off[i] = total;
+      total += align(parts[i].bytes);
+    }
+    plan->dev_bytes = total;
+    plan->image.assign(total, 0);
+    for (int i = 0; i < 8; ++i)
+      if (parts[i].bytes) std::memcpy(plan->image.data() + plan->table_off[i], parts[i].src, parts[i].bytes);
+    if (!(flags & ZL_PLAN_DEFERRED_UPLOAD)) {
+      if (hipMalloc(&plan->dev_block, total) != hipSuccess) {
+        plan->dev_block = nullptr;
+        (void)hipGetLastError();
+        return fail(ZL_ERR_NOMEM, "zl_plan_build: hipMalloc of " + std::to_string(total) + " bytes failed");
+      }
+      const hipError_t e = hipMemcpy(plan->dev_block, plan->image.data(), total, hipMemcpyHostToDevice);
+      if (e != hipSuccess) {
+        (void)hipFree(plan->dev_block);
+        plan->dev_block = nullptr;
+        return fail(ZL_ERR_HIP, std::string("zl_plan_build: upload failed: ") + hipGetErrorString(e));
+      }
+      plan->image.clear();
+      plan->image.shrink_to_fit();
+      zl::set_table_pointers(plan, plan->dev_block);
     }
   }
   *out = guard.release();
@@ -556,6 +566,72 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
 
 extern "C" void zl_plan_destroy(zl_plan* plan) {
   if (!plan) return;
-  if (plan->dev_block) (void)hipFree(plan->dev_block);
+  if (plan->dev_block) (void)hipFree(plan->dev_block);  // a deferred plan owns no device memory
   delete plan;
+}
+
+namespace {
+
+// Pinned host staging for zl_plan_upload, recycled across plans: an entry is reused once the copy
+// that last read it has completed (its event), so neither an upload nor a plan's destruction
+// waits for the device. Entries live until the process ends.
+struct Staging {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;  // recorded after the last copy from this entry
+  bool recorded = false;
+};
+std::mutex g_staging_mu;
+std::vector<Staging>* g_staging = new std::vector<Staging>();  // never destroyed: see above
+
+}  // namespace
+
+extern "C" zl_status zl_plan_upload(zl_plan* plan, void* dev_tables, size_t bytes, void* stream) {
+  if (!plan) return fail(ZL_ERR_INVALID, "zl_plan_upload: plan is NULL");
+  if (!(plan->flags & ZL_PLAN_DEFERRED_UPLOAD) || (plan->flags & ZL_PLAN_HOST_ONLY))
+    return fail(ZL_ERR_INVALID, "zl_plan_upload: the plan was not built with ZL_PLAN_DEFERRED_UPLOAD");
+  if (plan->d_segs) return fail(ZL_ERR_INVALID, "zl_plan_upload: the plan's tables were already uploaded");
+  if (!dev_tables || ((uintptr_t)dev_tables & 255))
+    return fail(ZL_ERR_INVALID, "zl_plan_upload: dev_tables must be a non-NULL, 256-byte aligned device pointer");
+  if (bytes < plan->dev_bytes)
+    return fail(ZL_ERR_INVALID, "zl_plan_upload: " + std::to_string(bytes) + " bytes given, the tables need " +
+                                    std::to_string(plan->dev_bytes));
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+    return fail(ZL_ERR_INVALID, "zl_plan_upload: the current device is not the plan's device");
+  hipStream_t s = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lock(g_staging_mu);
+  Staging* st = nullptr;
+  for (Staging& e : *g_staging)
+    if (e.cap >= plan->dev_bytes && (!e.recorded || hipEventQuery(e.done) == hipSuccess)) {
+      st = &e;
+      break;
+    }
+  if (!st) {
+    Staging e;
+    e.cap = std::max<size_t>(plan->dev_bytes, (size_t)1 << 20);
+    if (hipHostMalloc(&e.host, e.cap, hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(ZL_ERR_NOMEM, "zl_plan_upload: pinned staging of " + std::to_string(e.cap) + " bytes failed");
+    }
+    if (hipEventCreateWithFlags(&e.done, hipEventDisableTiming) != hipSuccess) {
+      (void)hipHostFree(e.host);
+      (void)hipGetLastError();
+      return fail(ZL_ERR_HIP, "zl_plan_upload: event creation failed");
+    }
+    g_staging->push_back(e);
+    st = &g_staging->back();
+  }
+  std::memcpy(st->host, plan->image.data(), plan->dev_bytes);
+  hipError_t e = hipMemcpyAsync(dev_tables, st->host, plan->dev_bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipEventRecord(st->done, s);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ZL_ERR_HIP, std::string("zl_plan_upload: copy failed: ") + hipGetErrorString(e));
+  }
+  st->recorded = true;
+  zl::set_table_pointers(plan, dev_tables);
+  plan->image.clear();
+  plan->image.shrink_to_fit();
+  return ZL_OK;
 }

@@ -97,6 +97,8 @@ typedef struct {
                               counts the workgroups that took the item; -1 without the flag */
   int64_t visits_dkdv;     /* the same in the backward workspace for the dK/dV queue (which = 1) */
   int64_t visits_dq;       /* ... and for the dQ queue (which = 2) */
+  size_t dev_bytes;        /* bytes of the plan's device tables (0 for a host-only plan): what
+                              zl_plan_upload needs for a ZL_PLAN_DEFERRED_UPLOAD plan */
 } zl_plan_info_t;
 
 /*
@@ -128,6 +130,10 @@ typedef struct {
                                  do dQ, dK, dV; needs equal query and key lengths. Sequence s starts
                                  at packed row 3 * (its first planar row); O, LSE, dO stay planar.
                                  Pass the packed buffer as q, k and v (and as dq, dk, dv). */
+#define ZL_PLAN_DEFERRED_UPLOAD 16u /* build everything but the device tables; zl_plan_upload then
+                                       copies them into caller memory on the caller's stream, so a
+                                       per-batch plan neither allocates device memory nor waits
+                                       for the device (see zl_plan_upload) */
 #define ZL_PLAN_COUNT_VISITS 8u /* scheduler check: every kernel also counts, per work item, the
                                    workgroups that took it, in int32 counters the workspace gains at
                                    the offsets zl_plan_info reports (visits_*). The forward launch
@@ -144,7 +150,7 @@ typedef struct {
  *   d_head                64 or 128 (else ZL_ERR_UNSUPPORTED)
  *   softmax_scale         tau in softmax(tau * Q K^T); <= 0 selects 1/sqrt(d_head)
  *   flags                 0 or an OR of ZL_PLAN_HOST_ONLY, ZL_PLAN_NO_SPLIT, ZL_PLAN_QKV_PACKED,
- *                         ZL_PLAN_COUNT_VISITS
+ *                         ZL_PLAN_COUNT_VISITS, ZL_PLAN_DEFERRED_UPLOAD
  *   out                   receives the plan; the caller frees it with zl_plan_destroy
  * The host arrays are copied; the plan owns its device tables (allocated on the current
  * device) and nothing else. The forward queue holds one item per (segment, head, block of
@@ -172,6 +178,23 @@ typedef struct {
 zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                         const int32_t* seq_heads, int32_t n_seg, const zl_segment* segs,
                         int32_t d_head, float softmax_scale, uint32_t flags, zl_plan** out);
+
+/*
+ * Copy the device tables of a plan built with ZL_PLAN_DEFERRED_UPLOAD into caller memory, on
+ * `stream` (the lowering of §IV-D done per rank per step without stalling the device):
+ *   dev_tables   device memory of at least info.dev_bytes bytes, 256-B aligned, owned by the
+ *                caller; it must stay allocated, and unmodified, while any launch that uses the
+ *                plan may still run
+ *   bytes        its size
+ *   stream       hipStream_t (NULL = default): the copy is ordered on it; launches with the plan on
+ *                another stream must be ordered after it (an event)
+ * The tables go through pinned host staging that the library recycles once the copy that read it
+ * has completed, so the call returns without waiting for the device, and zl_plan_destroy of such
+ * a plan frees no device memory and does not synchronise. Once per plan; ZL_ERR_INVALID for a
+ * plan built otherwise or already uploaded, or for a short or misaligned buffer. Not for use while
+ * the stream is being captured into a graph (the staging would be reused under the graph).
+ */
+zl_status zl_plan_upload(zl_plan* plan, void* dev_tables, size_t bytes, void* stream);
 
 /* Sizes and counts of a plan. */
 zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info);
@@ -201,10 +224,11 @@ zl_status zl_plan_tiles(const zl_plan* plan, int32_t which, int32_t* out, int64_
 zl_status zl_plan_queues(const zl_plan* plan, int32_t which, int32_t* bounds, int32_t cap, int32_t* n_queues);
 
 /*
- * Free a plan and its device tables. NULL is ignored. The tables are released with hipFree,
- * which first waits for all work queued on the device (an implicit device synchronisation):
- * a plan may be destroyed while launches that use it are still queued, but not while a
- * stream of its device is being captured into a graph.
+ * Free a plan and its device tables. NULL is ignored. The tables of a plan built without
+ * ZL_PLAN_DEFERRED_UPLOAD are released with hipFree, which first waits for all work queued on the
+ * device (an implicit device synchronisation): such a plan may be destroyed while launches that
+ * use it are still queued, but not while a stream of its device is being captured into a graph.
+ * A deferred plan owns no device memory; destroying it neither frees nor waits.
  */
 void zl_plan_destroy(zl_plan* plan);
 

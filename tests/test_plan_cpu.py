@@ -205,7 +205,7 @@ def test_bad_sequence_arrays():
                            ctypes.addressof(seg), 64, 0.0, 1, ctypes.byref(out))
     assert st == ZL_ERR_INVALID and b"seq_heads" in lib.zl_last_error()
     st = lib.zl_plan_build(1, ctypes.addressof(cu), ctypes.addressof(cu), ctypes.addressof(heads), 1,
-                           ctypes.addressof(seg), 64, 0.0, 16, ctypes.byref(out))
+                           ctypes.addressof(seg), 64, 0.0, 32, ctypes.byref(out))
     assert st == ZL_ERR_INVALID and b"flag" in lib.zl_last_error()
     assert lib.zl_plan_build(1, None, None, None, 1, None, 64, 0.0, 1, ctypes.byref(out)) == ZL_ERR_INVALID
 
@@ -440,3 +440,12 @@ def test_visit_counters_layout():
     assert b["ws_bwd"] >= b["visits_dq"] + 4 * b["dq_tiles"]
     assert all(x % 256 == 0 for x in (b["visits_fwd"], b["visits_dkdv"], b["visits_dq"]))
     assert p.tiles(0) == plain.tiles(0) and p.tiles(1) == plain.tiles(1) and p.tiles(2) == plain.tiles(2)
+
+
+def test_deferred_upload_needs_a_device_plan():
+    """zl_plan_upload refuses a plan built without ZL_PLAN_DEFERRED_UPLOAD (here a host-only one)
+    before touching the device."""
+    p = host_plan(W.config("tiny"))
+    assert p.info["dev_bytes"] == 0
+    st = z.lib().zl_plan_upload(p.handle, None, 0, None)
+    assert st == ZL_ERR_INVALID and b"DEFERRED" in z.lib().zl_last_error()
