@@ -40,10 +40,10 @@ def _unpack(pack, t):
 
 
 def _same(name, a, b):
-    a, b = a.cpu(), b.cpu()
+    """Bit-for-bit equality (NaN fills included), compared where the tensors live."""
     nan_a, nan_b = torch.isnan(a), torch.isnan(b)
     assert torch.equal(nan_a, nan_b), f"{name}: written rows differ"
-    assert torch.equal(a[~nan_a], b[~nan_b]), f"{name}: values differ"
+    assert torch.equal(torch.nan_to_num(a), torch.nan_to_num(b)), f"{name}: values differ"
 
 
 def _packed_matches(pack, ins, planar):
@@ -54,7 +54,7 @@ def _packed_matches(pack, ins, planar):
     plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, d, qkv_packed=True)
     info = plan.info
     assert info["qkv_rows"] == 3 * info["q_rows"]
-    qkv = _pack_qkv(pack, ins["q"], ins["k"], ins["v"]).to(dev)
+    qkv = _pack_qkv(pack, ins["q"].to(dev), ins["k"].to(dev), ins["v"].to(dev))
     do = ins["do"].to(dev)
     nan = float("nan")
     o = torch.full((info["q_rows"], d), nan, dtype=torch.float32, device=dev)
@@ -120,4 +120,16 @@ def test_random_packs_packed_match_planar(seed):
     ins = W.draw(pack)
     print(f"[case] packed vs planar {pack.name} d={pack.d} seqs={pack.seq_q} heads={pack.heads}", flush=True)
     planar = H.run_pack(pack, ins)
+    _packed_matches(pack, ins, planar)
+
+
+def test_packed_matches_planar_at_full_size():
+    """The mixed image-video pack in the QKV-packed layout: 4.3 M query rows, so the packed bf16
+    buffer (3.3 GB) and the packed fp32 gradients (6.6 GB) are addressed past 2^31 bytes; every
+    output bit for bit against the planar run (itself checked against the oracle at full size)."""
+    pack = W.config("mixed")
+    ins = W.draw(pack)
+    print(f"[case] packed vs planar, mixed pack: {pack.q_rows()} rows", flush=True)
+    planar = H.run_pack(pack, ins)
+    assert 3 * pack.q_rows() * pack.d * 2 > 2 ** 31
     _packed_matches(pack, ins, planar)
