@@ -216,6 +216,16 @@ extern "C" zl_status zl_plan_queues(const zl_plan* plan, int32_t which, int32_t*
   return ZL_OK;
 }
 
+// A queue set for a launch: the plan's items on the device, counters in the workspace, and the
+// host copy of the bounds as kernel arguments.
+zl::Queues make_queues(const zl::Tile* items, int32_t* counters, const std::vector<int32_t>& bounds) {
+  zl::Queues q{};
+  q.items = items;
+  q.counters = counters;
+  for (int k = 0; k <= zl::kQueues; ++k) q.bounds[k] = bounds[k];
+  return q;
+}
+
 extern "C" zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void* k, const void* v, float* o,
                                  float* lse, float* o_part, float* lse_part, void* workspace, void* stream) {
   zl_status st = check_runnable(plan, "zl_attn_fwd");
@@ -238,7 +248,7 @@ extern "C" zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void*
   p.o_part = o_part;
   p.lse_part = lse_part;
   p.segs = plan->d_segs;
-  p.queue = {plan->d_fwd, plan->d_bounds, (int32_t*)workspace};
+  p.queue = make_queues(plan->d_fwd, (int32_t*)workspace, plan->fwd_bounds);
   p.scale_log2 = plan->scale * 1.4426950408889634f;
   set_split(plan, workspace, &p);
   set_fwd_visits(plan, workspace, &p);
@@ -274,7 +284,7 @@ extern "C" zl_status zl_attn_fwd_accumulate(const zl_plan* plan, const void* q, 
   p.o = o;
   p.lse = lse;
   p.segs = plan->d_segs;
-  p.queue = {plan->d_fwd, plan->d_bounds, (int32_t*)workspace};
+  p.queue = make_queues(plan->d_fwd, (int32_t*)workspace, plan->fwd_bounds);
   p.scale_log2 = plan->scale * 1.4426950408889634f;
   p.accumulate = 1;
   set_split(plan, workspace, &p);
@@ -348,9 +358,8 @@ extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, cons
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.kvq = {plan->d_bwd, plan->d_bounds + (zl::kQueues + 1), (int32_t*)workspace};
-  p.dqq = {plan->d_dq, plan->d_bounds + 2 * (zl::kQueues + 1),
-           (int32_t*)workspace + zl::kQueues * zl::kCounterStride};
+  p.kvq = make_queues(plan->d_bwd, (int32_t*)workspace, plan->bwd_bounds);
+  p.dqq = make_queues(plan->d_dq, (int32_t*)workspace + zl::kQueues * zl::kCounterStride, plan->dq_bounds);
   p.dneg = (float*)((char*)workspace + kCounterBytes);
   p.lsec = (float*)((char*)workspace + kCounterBytes + align256((size_t)plan->q_rows * sizeof(float)));
   p.sentinel = (float*)((char*)workspace + kCounterBytes + 2 * align256((size_t)plan->q_rows * sizeof(float)));
@@ -385,5 +394,7 @@ extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, cons
   const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, (int64_t)plan->bwd_tiles.size());
   const int grid_dq = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu_dq, (int64_t)plan->dq_tiles.size());
   const int grid_pre = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)plan->n_cu * 8, p.n_pre));
+  p.kv_grid = grid;
+  p.dq_grid = grid_dq;
   return launch_status(zl::launch_bwd(plan->d, p, grid_pre, grid, grid_dq, stages, stream), "zl_attn_bwd");
 }

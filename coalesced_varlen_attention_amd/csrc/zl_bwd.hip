@@ -9,8 +9,8 @@
 //
 // Pre-pass: -D and -LSE / tau for every covered query row, stored head-major (row
 //   q_row0 + h * Lq + t of the sequence) so that the key-major kernel loads the 64 rows of a
-//   step as one contiguous 256-byte run; both queue counters and the split-item counters
-//   zeroed; the sentinel rows (-inf, 0) that stand in for rows past a segment's end written.
+//   step as one contiguous 256-byte run; both queues' counters set past the static first
+//   items of their launches and the split-item counters zeroed; the sentinel rows (-inf, 0) that stand in for rows past a segment's end written.
 // dK/dV kernel: one item = 128 key rows of one (segment, head); 4 waves x 32 keys. Each wave
 //   keeps its K and V rows in registers as B operands of S = Q K^T and dP = dO V^T (lane = one
 //   key column), so P and dS come out of the MFMA already in the B-operand layout of
@@ -45,9 +45,9 @@ namespace {
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
-  if (blockIdx.x == 0 && threadIdx.x < kQueues) {
-    p.kvq.counters[threadIdx.x * kCounterStride] = 0;
-    p.dqq.counters[threadIdx.x * kCounterStride] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < kQueues) {  // past the static first items of each launch
+    p.kvq.counters[threadIdx.x * kCounterStride] = home_count(p.kv_grid, threadIdx.x);
+    p.dqq.counters[threadIdx.x * kCounterStride] = home_count(p.dq_grid, threadIdx.x);
   }
   if (blockIdx.x == 0 && threadIdx.x < 2 * kBwdRows) p.sentinel[threadIdx.x] = threadIdx.x < kBwdRows ? -INFINITY : 0.f;
   for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < p.n_dq_split; j += gridDim.x * blockDim.x)
@@ -62,6 +62,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
   }
   const float neg_inv_tau = -1.0f / p.scale;
   constexpr int kPer = D / 16;  // elements per lane
+  constexpr int kPreUnroll = kPreRows / 16;
   const int sub = threadIdx.x & 15;
   const int rsel = threadIdx.x >> 4;
   const bf16* gdo = (const bf16*)p.d_o;
@@ -70,24 +71,42 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
     const SegDev sg = p.segs[t.seg];
     const int nhr = sg.head_end - sg.head_begin;
     const int rows = t.nrows * nhr;
-    for (int r = rsel; r < rows; r += 16) {
-      const int tok = t.row0 + r / nhr;
-      const int h = sg.head_begin + r % nhr;
-      const int64_t row = sg.q_row0 + (int64_t)tok * sg.nh + h;
-      const int64_t e0 = row * D + sub * kPer;
-      float acc = 0.f;
+    // kPreUnroll rows per 16-lane group per pass, every row's loads issued before the first
+    // sum (a short pack is a few passes of dependent loads). Rows past the tile's end repeat
+    // its last row's loads and store nothing.
+    for (int r0 = rsel; r0 < rows; r0 += kPreUnroll * 16) {
+      f32x4 o4[kPreUnroll][kPer / 4];
+      bf16x4 d4[kPreUnroll][kPer / 4];
+      float lse[kPreUnroll];
+      int64_t hm[kPreUnroll];
 #pragma unroll
-      for (int u = 0; u < kPer; u += 4) {
-        const f32x4 o4 = *(const f32x4*)(p.o + e0 + u);
-        const bf16x4 d4 = *(const bf16x4*)(gdo + e0 + u);
-        acc += (float)d4[0] * o4[0] + (float)d4[1] * o4[1] + (float)d4[2] * o4[2] + (float)d4[3] * o4[3];
+      for (int j = 0; j < kPreUnroll; ++j) {
+        const int r = min(r0 + 16 * j, rows - 1);
+        const int tok = t.row0 + r / nhr;
+        const int h = sg.head_begin + r % nhr;
+        const int64_t row = sg.q_row0 + (int64_t)tok * sg.nh + h;
+        const int64_t e0 = row * D + sub * kPer;
+#pragma unroll
+        for (int u = 0; u < kPer / 4; ++u) {
+          o4[j][u] = *(const f32x4*)(p.o + e0 + 4 * u);
+          d4[j][u] = *(const bf16x4*)(gdo + e0 + 4 * u);
+        }
+        lse[j] = p.lse[row];
+        hm[j] = sg.q_row0 + (int64_t)h * sg.lq + tok;
       }
 #pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-      if (sub == 0) {
-        const int64_t hm = sg.q_row0 + (int64_t)h * sg.lq + tok;
-        p.dneg[hm] = -acc;
-        p.lsec[hm] = p.lse[row] * neg_inv_tau;
+      for (int j = 0; j < kPreUnroll; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < kPer / 4; ++u)
+          acc += (float)d4[j][u][0] * o4[j][u][0] + (float)d4[j][u][1] * o4[j][u][1] +
+                 (float)d4[j][u][2] * o4[j][u][2] + (float)d4[j][u][3] * o4[j][u][3];
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+        if (sub == 0 && r0 + 16 * j < rows) {
+          p.dneg[hm[j]] = -acc;
+          p.lsec[hm[j]] = lse[j] * neg_inv_tau;
+        }
       }
     }
   }
@@ -330,6 +349,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[C::kStages * C::kStageBytes];
   __shared__ int32_t s_item;
+  __shared__ int32_t s_queue_mem[kQueues + 2];  // queue state of thread 0: bounds, then take_item's state
+  ZL_LDS int32_t* const s_bounds = (ZL_LDS int32_t*)s_queue_mem;
+  ZL_LDS int32_t* const s_taker = s_bounds + kQueues + 1;
   __shared__ int32_t s_last;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(ZL_LDS char*)smem;
 
@@ -365,9 +387,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
   const int dma_col = 16 * ((lane % C::kRowChunks) ^ qt_x<D>(dma_row));
 
   const int home = blockIdx.x % kQueues;
-  int drained = 0;
+  if (tid == 0) {
+    stage_bounds(p.kvq, s_bounds);
+    *s_taker = home << 8;
+  }
   for (;;) {
-    if (tid == 0) s_item = take_item(p.kvq, home, drained, p.kv_visits);
+    if (tid == 0) s_item = take_item(p.kvq, s_bounds, s_taker, p.kv_visits);
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item);  // the same for every lane
     if (item < 0) break;
@@ -713,6 +738,9 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
   using L = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
   __shared__ int32_t s_item;
+  __shared__ int32_t s_queue_mem[kQueues + 2];  // queue state of thread 0: bounds, then take_item's state
+  ZL_LDS int32_t* const s_bounds = (ZL_LDS int32_t*)s_queue_mem;
+  ZL_LDS int32_t* const s_taker = s_bounds + kQueues + 1;
   __shared__ int32_t s_last;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(ZL_LDS char*)smem;
 
@@ -745,9 +773,12 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
   const int dma_col = 16 * ((lane % L::kRowChunks) ^ qt_x<D>(dma_row));
 
   const int home = blockIdx.x % kQueues;
-  int drained = 0;
+  if (tid == 0) {
+    stage_bounds(p.dqq, s_bounds);
+    *s_taker = home << 8;
+  }
   for (;;) {
-    if (tid == 0) s_item = take_item(p.dqq, home, drained, p.dq_visits);
+    if (tid == 0) s_item = take_item(p.dqq, s_bounds, s_taker, p.dq_visits);
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item);  // the same for every lane
     if (item < 0) break;

@@ -177,21 +177,70 @@ __device__ __forceinline__ void load_dev16x16(const float* p, f32x4 (&x)[16]) {
       : "memory");
 }
 
-// Next work item for a workgroup (called by one thread): its own XCD's queue first, then the
-// others in order. `drained` counts the queues found empty and only grows, so every
-// workgroup stops after at most (its items + kQueues) atomics. Returns -1 when all are empty.
-// With `visits` (the scheduler check), the item taken is also counted there.
-__device__ __forceinline__ int take_item(const Queues& q, int home, int& drained, int32_t* visits) {
-  while (drained < kQueues) {
-    const int k = (home + drained) & (kQueues - 1);
-    const int idx = q.bounds[k] + atomicAdd(&q.counters[k * kCounterStride], 1);
-    if (idx < q.bounds[k + 1]) {
-      if (visits) atomicAdd(visits + idx, 1);
-      return idx;
-    }
-    ++drained;
+// Copies a queue set's bounds (kernel arguments) into LDS, where take_item reads them: held in
+// scalar registers they would stay live through every item. Called by the thread that calls
+// take_item, which alone reads the copy, so no barrier is needed.
+__device__ __forceinline__ void stage_bounds(const Queues& q, ZL_LDS int32_t* lds) {
+#pragma unroll
+  for (int k = 0; k <= kQueues; ++k) lds[k] = q.bounds[k];
+}
+
+// Next work item for a workgroup, called by one thread; returns -1 once every queue is drained.
+// The workgroup's queue state lives in LDS, so that nothing holds registers for it during an
+// item: `bounds` is the copy of the queue bounds and `state` packs the queues known to be
+// drained (bits 0-7; counters only grow, so a drained queue stays drained), the queue to try
+// first (bits 8-10) and whether the static first item was taken (bit 11); the kernel sets
+// `state` to its home queue (home << 8) before the first call.
+//   * The first call takes the workgroup's static item, item blockIdx.x / kQueues of its home
+//     queue (the launch set that queue's counter to home_count, past those items).
+//   * Later calls pop the current queue (home, or the queue the last item was stolen from).
+//   * When it is drained, the counters of all other queues are read at once (one round trip),
+//     and only queues that still hold items are popped, nearest to home first. A workgroup
+//     that finds every queue drained leaves after two round trips instead of one atomic per
+//     queue.
+// Every call ends after at most kQueues + 1 atomics. With `visits` (the scheduler check), the
+// item taken is also counted there.
+__device__ __forceinline__ int take_item(const Queues& q, const ZL_LDS int32_t* bounds, ZL_LDS int32_t* state,
+                                         int32_t* visits) {
+  constexpr uint32_t kAll = (1u << kQueues) - 1;
+  const uint32_t st = (uint32_t)*state;
+  uint32_t empty = st & kAll;
+  int cur = (int)(st >> 8) & (kQueues - 1);
+  const int home = (int)(blockIdx.x % kQueues);
+  int idx = -1;
+  if (!(st & (1u << 11))) {
+    const int j = bounds[home] + (int)(blockIdx.x / kQueues);
+    if (j < bounds[home + 1]) idx = j;
+    else empty |= 1u << home;
   }
-  return -1;
+  if (idx < 0 && !(empty >> cur & 1)) {
+    const int j = bounds[cur] + atomicAdd(&q.counters[cur * kCounterStride], 1);
+    if (j < bounds[cur + 1]) idx = j;
+    else empty |= 1u << cur;
+  }
+  if (idx < 0 && empty != kAll) {
+    int c[kQueues];
+#pragma unroll
+    for (int k = 0; k < kQueues; ++k)
+      c[k] = __hip_atomic_load(&q.counters[k * kCounterStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int k = 0; k < kQueues; ++k)
+      if (bounds[k] + c[k] >= bounds[k + 1]) empty |= 1u << k;
+    for (int i = 1; i < kQueues && idx < 0; ++i) {
+      const int k = (home + i) & (kQueues - 1);
+      if (empty >> k & 1) continue;
+      const int j = bounds[k] + atomicAdd(&q.counters[k * kCounterStride], 1);
+      if (j < bounds[k + 1]) {
+        idx = j;
+        cur = k;
+      } else {
+        empty |= 1u << k;
+      }
+    }
+  }
+  *state = (int32_t)(empty | (uint32_t)cur << 8 | 1u << 11);
+  if (idx >= 0 && visits) atomicAdd(visits + idx, 1);
+  return idx;
 }
 
 }  // namespace zl

@@ -138,10 +138,10 @@ __device__ __forceinline__ void dma_v(const FwdCtx<D>& cx, uint32_t v_lds, int b
 }
 
 // Clears the queue counters, the split-item counters and the visit counters before a launch.
-__global__ __launch_bounds__(256) void zero_counters_kernel(int32_t* counters, int32_t* split_cnt, int32_t n_split,
-                                                            int32_t* visits, int32_t n_visits) {
+__global__ __launch_bounds__(256) void zero_counters_kernel(int32_t* counters, int32_t grid, int32_t* split_cnt,
+                                                            int32_t n_split, int32_t* visits, int32_t n_visits) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < kQueues) counters[i * kCounterStride] = 0;
+  if (i < kQueues) counters[i * kCounterStride] = home_count(grid, i);  // past the static first items
   for (int j = i; j < n_split; j += gridDim.x * 256) split_cnt[j] = 0;
   if (visits)
     for (int j = i; j < n_visits; j += gridDim.x * 256) visits[j] = 0;
@@ -418,6 +418,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   const uint32_t v_lds0 = lds0, v_lds1 = lds0 + C::kVBytes;
   const uint32_t k_lds0 = lds0 + 2 * C::kVBytes, k_lds1 = k_lds0 + C::kKBytes;
   __shared__ int32_t s_item;
+  __shared__ int32_t s_queue_mem[kQueues + 2];  // queue state of thread 0: bounds, then take_item's state
+  ZL_LDS int32_t* const s_bounds = (ZL_LDS int32_t*)s_queue_mem;
+  ZL_LDS int32_t* const s_taker = s_bounds + kQueues + 1;
   __shared__ int32_t s_last;
 
   const int tid = threadIdx.x;
@@ -446,9 +449,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   }
 
   const int home = blockIdx.x % kQueues;
-  int drained = 0;
+  if (tid == 0) {
+    stage_bounds(p.queue, s_bounds);
+    *s_taker = home << 8;
+  }
   for (;;) {
-    if (tid == 0) s_item = take_item(p.queue, home, drained, p.visits);
+    if (tid == 0) s_item = take_item(p.queue, s_bounds, s_taker, p.visits);
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item);  // the same for every lane
     if (item < 0) break;
@@ -638,8 +644,8 @@ int launch_fwd(int d, const FwdParams& p, int grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int64_t nz = std::max<int64_t>(p.n_split, p.visits ? p.n_visits : 0);
   const int zgrid = nz > 0 ? (int)std::min<int64_t>(64, (nz + 255) / 256) : 1;
-  hipLaunchKernelGGL(zero_counters_kernel, dim3(zgrid), dim3(256), 0, s, p.queue.counters, p.split_cnt, p.n_split,
-                     p.visits, p.n_visits);
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(zgrid), dim3(256), 0, s, p.queue.counters, grid, p.split_cnt,
+                     p.n_split, p.visits, p.n_visits);
   if (d == 64 && p.packed)
     hipLaunchKernelGGL((fwd_kernel<64, true>), dim3(grid), dim3(256), 0, s, p);
   else if (d == 64)

@@ -37,12 +37,18 @@ constexpr int kHostOnlyKvSlots = 256;
 constexpr int kHostOnlyDqSlots = 256 * (8 / kDqWaves);
 constexpr int kBwdKeys = 128;
 constexpr int kBwdRows = 64;
-// Rows (token, head pairs) per item of the backward pre-pass.
-constexpr int kPreRows = 256;
+// Rows (token, head pairs) per item of the backward pre-pass: one pass of its workgroup (16
+// groups of 16 lanes, 8 rows each).
+constexpr int kPreRows = 128;
 // Work queues per launch: one per XCD. Workgroup b starts on queue b % kQueues (the XCD the
 // hardware dispatches it to) and steals from the others once its own queue is empty.
 constexpr int kQueues = 8;
 constexpr int kCounterStride = 16;  // ints between queue counters (64 bytes)
+
+// Workgroups of a grid of `grid` whose home is queue k. The j-th of them takes item j of its
+// home queue as its first item without an atomic, so a launch starts queue k's counter at this
+// count and the atomics hand out the items after those.
+__host__ __device__ constexpr int32_t home_count(int grid, int k) { return (grid - k + kQueues - 1) / kQueues; }
 
 // A segment as the kernels see it. Rows are (token, head) pairs of d contiguous values.
 // O, LSE and dO always use the planar query-side layout (q_row0, nh rows per token). Q, K, V
@@ -109,11 +115,12 @@ struct alignas(16) Tile {
 static_assert(sizeof(Tile) == 32, "Tile must stay 32 bytes");
 
 // A set of kQueues work queues: items stored queue by queue, bounds[k]..bounds[k+1] for
-// queue k, and one counter per queue (kCounterStride ints apart) in the caller's workspace.
+// queue k (kernel arguments, so that no item index waits on a load of them), and one counter
+// per queue (kCounterStride ints apart) in the caller's workspace.
 struct Queues {
   const Tile* items;
-  const int32_t* bounds;
   int32_t* counters;
+  int32_t bounds[kQueues + 1];
 };
 
 struct FwdParams {
@@ -168,6 +175,8 @@ struct BwdParams {
   int32_t* kv_visits;     // per dK/dV item, per dQ item: workgroups that took it (ZL_PLAN_COUNT_VISITS),
   int32_t* dq_visits;     // or null; both cleared by the pre-pass
   int32_t n_kv_visits, n_dq_visits;
+  int32_t kv_grid, dq_grid;  // workgroups of the dK/dV and dQ launches (the pre-pass sets their
+                             // queue counters to the home counts)
 };
 
 // Kernel launchers (defined next to their kernels). They return the launch status.
@@ -215,11 +224,11 @@ struct zl_plan {
   int32_t kv_split_tiles = 0;   // dK/dV items cut into pieces of their query blocks
   int32_t kv_split_pieces = 0;  // pieces of those items
   // device copies: one block carved into the tables at table_off (segments, forward, dK/dV,
-  // pre-pass and dQ items, key-range chains, queue bounds, groups); owned (dev_block) unless the
+  // pre-pass and dQ items, key-range chains, groups); owned (dev_block) unless the
   // plan was built with ZL_PLAN_DEFERRED_UPLOAD, whose tables zl_plan_upload copies into caller
   // memory from `image` (kept until then)
   size_t dev_bytes = 0;
-  size_t table_off[8] = {};
+  size_t table_off[7] = {};
   std::vector<char> image;
   void* dev_block = nullptr;
   const zl::SegDev* d_segs = nullptr;
@@ -228,6 +237,5 @@ struct zl_plan {
   const zl::Tile* d_pre = nullptr;
   const zl::Tile* d_dq = nullptr;
   const int32_t* d_ranges = nullptr;
-  const int32_t* d_bounds = nullptr;  // fwd, bwd, dq bounds, kQueues + 1 each
   const zl::GroupDev* d_groups = nullptr;
 };

@@ -36,8 +36,7 @@ void set_table_pointers(zl_plan* plan, void* block) {
   plan->d_pre = (const Tile*)(b + plan->table_off[3]);
   plan->d_dq = (const Tile*)(b + plan->table_off[4]);
   plan->d_ranges = (const int32_t*)(b + plan->table_off[5]);
-  plan->d_bounds = (const int32_t*)(b + plan->table_off[6]);
-  plan->d_groups = (const GroupDev*)(b + plan->table_off[7]);
+  plan->d_groups = (const GroupDev*)(b + plan->table_off[6]);
 }
 
 }  // namespace zl
@@ -520,9 +519,6 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   if (!(flags & ZL_PLAN_HOST_ONLY)) {
     // One image of every device table, carved at 256-byte aligned offsets.
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    std::vector<int32_t> all_bounds;
-    for (const auto* b : {&plan->fwd_bounds, &plan->bwd_bounds, &plan->dq_bounds})
-      all_bounds.insert(all_bounds.end(), b->begin(), b->end());
     const struct {
       const void* src;
       size_t bytes;
@@ -532,16 +528,17 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
                  {plan->pre_tiles.data(), plan->pre_tiles.size() * sizeof(zl::Tile)},
                  {plan->dq_tiles.data(), plan->dq_tiles.size() * sizeof(zl::Tile)},
                  {plan->kv_ranges.data(), plan->kv_ranges.size() * sizeof(int32_t)},
-                 {all_bounds.data(), all_bounds.size() * sizeof(int32_t)},
                  {plan->gdev.data(), plan->gdev.size() * sizeof(zl::GroupDev)}};
     size_t total = 0;
-    for (int i = 0; i < 8; ++i) {
+    constexpr int kTables = sizeof(parts) / sizeof(parts[0]);
+    static_assert(kTables == sizeof(plan->table_off) / sizeof(plan->table_off[0]), "one offset per table");
+    for (int i = 0; i < kTables; ++i) {
       plan->table_off[i] = total;
       total += align(parts[i].bytes);
     }
     plan->dev_bytes = total;
     plan->image.assign(total, 0);
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < kTables; ++i)
       if (parts[i].bytes) std::memcpy(plan->image.data() + plan->table_off[i], parts[i].src, parts[i].bytes);
     if (!(flags & ZL_PLAN_DEFERRED_UPLOAD)) {
       if (hipMalloc(&plan->dev_block, total) != hipSuccess) {
