@@ -22,6 +22,7 @@ import argparse
 import json
 import os
 import sys
+import statistics
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -297,18 +298,23 @@ def main() -> int:
     torch.cuda.set_device(dev)
     pack = W.config(args.config)
     # Plan build: the first build in the process also loads the library's kernels; a per-batch
-    # engine pays the warm figure (the second build), reported beside it. Neither is in the step.
+    # engine pays the warm figure (the median of five later builds, each destroyed after),
+    # reported beside it. Neither is in the step.
     build = lambda: zl.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale,
                             split=not args.no_split)
     t0 = time.perf_counter()
     plan = build()
     plan_ms = (time.perf_counter() - t0) * 1e3
-    t0 = time.perf_counter()
-    plan_warm = build()
-    plan_warm_ms = (time.perf_counter() - t0) * 1e3
-    t0 = time.perf_counter()
-    plan_warm.close()
-    plan_destroy_ms = (time.perf_counter() - t0) * 1e3
+    warm, destroy = [], []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        plan_warm = build()
+        warm.append((time.perf_counter() - t0) * 1e3)
+        t0 = time.perf_counter()
+        plan_warm.close()
+        destroy.append((time.perf_counter() - t0) * 1e3)
+    plan_warm_ms = statistics.median(warm)
+    plan_destroy_ms = statistics.median(destroy)
     info = plan.info
     ins = W.draw(pack)
     q, k, v, do = (ins[n].to(dev) for n in ("q", "k", "v", "do"))

@@ -122,14 +122,23 @@ void distribute(const std::vector<Item>& items, const std::vector<int64_t>& unit
     members[q].push_back(ci);
   }
   out->clear();
+  out->reserve(items.size());
   bounds->assign(1, 0);
+  // Per queue: decreasing cost, ties in (segment, head, block) order, as (cost, position) keys.
+  struct Key {
+    int64_t cost;
+    size_t pos;
+  };
+  std::vector<Key> keys;
+  keys.reserve(items.size());
   for (int q = 0; q < zl::kQueues; ++q) {
     std::sort(members[q].begin(), members[q].end());  // back to (segment, head, block) order
-    std::vector<Item> mine;
+    keys.clear();
     for (size_t ci : members[q])
-      for (size_t k = chunks[ci].begin; k < chunks[ci].end; ++k) mine.push_back(items[k]);
-    std::stable_sort(mine.begin(), mine.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
-    for (const Item& it : mine) out->push_back(it.t);
+      for (size_t k = chunks[ci].begin; k < chunks[ci].end; ++k) keys.push_back({items[k].cost, k});
+    std::sort(keys.begin(), keys.end(),
+              [](const Key& a, const Key& b) { return a.cost != b.cost ? a.cost > b.cost : a.pos < b.pos; });
+    for (const Key& k : keys) out->push_back(items[k.pos].t);
     bounds->push_back((int32_t)out->size());
   }
 }
@@ -439,6 +448,27 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   // L2; each queue is then sorted by decreasing item cost with a stable tie order.
   std::vector<Item> fwd, bwd, dq;
   std::vector<int64_t> fwd_unit, bwd_unit, dq_unit;  // (segment, head) unit of each item
+  {
+    size_t n_fwd = 0, n_bwd = 0, n_dq = 0, n_pre = 0;
+    for (int i = 0; i < n_seg; ++i) {
+      const zl_segment& g = segs[i];
+      const size_t nh = (size_t)(g.head_end - g.head_begin);
+      const size_t nq = (size_t)(g.q_end - g.q_begin), nk = (size_t)(g.kv_end - g.kv_begin);
+      n_fwd += nh * ((nq + zl::kFwdRows - 1) / zl::kFwdRows);
+      n_bwd += nh * ((nk + zl::kBwdKeys - 1) / zl::kBwdKeys);
+      if (g.part <= 0) {
+        n_dq += nh * ((nq + zl::kDqRows - 1) / zl::kDqRows);
+        n_pre += nq / (size_t)std::max<size_t>(1, zl::kPreRows / nh) + 1;
+      }
+    }
+    fwd.reserve(n_fwd);
+    fwd_unit.reserve(n_fwd);
+    bwd.reserve(n_bwd);
+    bwd_unit.reserve(n_bwd);
+    dq.reserve(n_dq);
+    dq_unit.reserve(n_dq);
+    plan->pre_tiles.reserve(n_pre);
+  }
   for (int i = 0; i < n_seg; ++i) {
     const zl_segment& g = segs[i];
     const int64_t nq = g.q_end - g.q_begin, nk = g.kv_end - g.kv_begin;
