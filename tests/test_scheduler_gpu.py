@@ -9,7 +9,12 @@ last-piece counters finish only if every piece runs once.
 
 Packs: the mixed image-video pack (the benchmark's), one head of a 32,760-token video (forward
 and dQ items split into pieces), one head of 8,192 tokens (forward, dQ and dK/dV items split),
-and the ring shard (dQ items walking 8-part key chains). The counting plan's outputs must also equal a plain plan's bit for bit: the items and
+the ring shard (dQ items walking 8-part key chains), and a few-item pack (512 + 2,048 tokens,
+one head each), unsplit and split. In the few-item pack the 512-token sequence's four forward
+items share one queue chunk. The grid is one workgroup per item, and the queues are uneven:
+queue 0 holds more items than it has home workgroups, and other queues hold fewer. So the
+workgroups take static first items, find their home queue short, and take the rest by stealing
+after the one-round-trip counter check. The counting plan's outputs must also equal a plain plan's bit for bit: the items and
 their order are the same, and every output is written once by one workgroup.
 """
 import pytest
@@ -38,18 +43,28 @@ def _run(plan, pack, ins, dev):
 def _pack(name):
     if name == "head8k":  # one head of 8,192 tokens: forward, dQ and dK/dV items all split
         return W.Pack("head8k", (8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, 8)
+    if name.startswith("few"):  # 20 forward items in 17 queue chunks
+        return W.Pack("few", (512, 2048), (512, 2048), (1, 1),
+                      ((0, 0, 1, 0, 512, 0, 512, -1), (1, 0, 1, 0, 2048, 0, 2048, -1)), 128, 9)
     return W.config(name)
 
 
-@pytest.mark.parametrize("name", ["mixed", "head1", "head8k", "ring"])
+@pytest.mark.parametrize("name", ["mixed", "head1", "head8k", "ring", "few", "few_nosplit"])
 def test_every_item_taken_exactly_once(name):
     z = H.zl()
     pack = _pack(name)
+    split = name != "few_nosplit"
     print(f"[case] visits {name}", flush=True)
     dev = torch.device("cuda:0")
     ins = W.draw(pack)
-    plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale, count_visits=True)
+    plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale, count_visits=True,
+                  split=split)
     info = plan.info
+    if name == "few_nosplit":  # uneven queues: queue 0 has more items than home workgroups
+        bounds = plan.queues(0)
+        sizes = [b - a for a, b in zip(bounds, bounds[1:])]
+        homes = [(info["fwd_tiles"] - k + 7) // 8 for k in range(8)]
+        assert sizes[0] > homes[0] and any(n < h for n, h in zip(sizes, homes)), (sizes, homes)
     if name == "head1":
         assert info["split_tiles"] > 0 and info["dq_split_tiles"] > 0
     if name == "head8k":
@@ -62,7 +77,7 @@ def test_every_item_taken_exactly_once(name):
         print(f"  {key}: {n_items} items, visits min {int(c.min())} max {int(c.max())}", flush=True)
         assert bool((c == 1).all()), f"{key}: items taken {int((c == 0).sum())} x never, {int((c > 1).sum())} x more than once"
     # the same plan without counters gives the same bits
-    plain = H.make_plan(pack)
+    plain = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale, split=split)
     ref, _, _ = _run(plain, pack, ins, dev)
     for n in out:
         assert torch.equal(out[n], ref[n]), f"{n}: the counting plan's output differs from the plain plan's"
