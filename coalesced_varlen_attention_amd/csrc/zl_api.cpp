@@ -40,8 +40,8 @@ constexpr int64_t kMaxBwdQueryRows = INT64_C(1) << 29;
 size_t split_bytes(const zl_plan* plan) {
   const size_t n = (size_t)plan->split_pieces;
   if (n == 0) return 0;
-  return align256(n * sizeof(int32_t)) + align256(n * zl::kFwdRows * plan->d * sizeof(float)) +
-         align256(n * zl::kFwdRows * sizeof(float));
+  return align256(n * sizeof(int32_t)) + align256(n * (size_t)plan->fwd_rows * plan->d * sizeof(float)) +
+         align256(n * (size_t)plan->fwd_rows * sizeof(float));
 }
 
 void set_split(const zl_plan* plan, void* workspace, zl::FwdParams* p) {
@@ -52,7 +52,7 @@ void set_split(const zl_plan* plan, void* workspace, zl::FwdParams* p) {
   p->split_cnt = (int32_t*)base;
   base += align256(n * sizeof(int32_t));
   p->split_o = (float*)base;
-  base += align256(n * zl::kFwdRows * plan->d * sizeof(float));
+  base += align256(n * (size_t)plan->fwd_rows * plan->d * sizeof(float));
   p->split_lse = (float*)base;
 }
 
@@ -160,6 +160,7 @@ extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   info->kv_split_tiles = plan->kv_split_tiles;
   info->kv_split_pieces = plan->kv_split_pieces;
   info->dev_bytes = plan->dev_bytes;
+  info->fwd_rows = plan->fwd_rows;
   info->visits_fwd = info->visits_dkdv = info->visits_dq = -1;
   if (counts_visits(plan)) {
     info->visits_fwd = (int64_t)fwd_visit_offset(plan);
@@ -253,10 +254,10 @@ extern "C" zl_status zl_attn_fwd(const zl_plan* plan, const void* q, const void*
   set_split(plan, workspace, &p);
   set_fwd_visits(plan, workspace, &p);
   p.packed = (plan->flags & ZL_PLAN_QKV_PACKED) ? 1 : 0;
-  const int per_cu = zl::fwd_blocks_per_cu(plan->d);
+  const int per_cu = zl::fwd_blocks_per_cu(plan->d, plan->fwd_rows);
   if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_fwd: forward kernel cannot be resident");
   const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, (int64_t)plan->fwd_tiles.size());
-  return launch_status(zl::launch_fwd(plan->d, p, grid, stream), "zl_attn_fwd");
+  return launch_status(zl::launch_fwd(plan->d, plan->fwd_rows, p, grid, stream), "zl_attn_fwd");
 }
 
 extern "C" zl_status zl_attn_fwd_accumulate(const zl_plan* plan, const void* q, const void* k, const void* v,
@@ -290,10 +291,10 @@ extern "C" zl_status zl_attn_fwd_accumulate(const zl_plan* plan, const void* q, 
   set_split(plan, workspace, &p);
   set_fwd_visits(plan, workspace, &p);
   p.packed = (plan->flags & ZL_PLAN_QKV_PACKED) ? 1 : 0;
-  const int per_cu = zl::fwd_blocks_per_cu(plan->d);
+  const int per_cu = zl::fwd_blocks_per_cu(plan->d, plan->fwd_rows);
   if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_attn_fwd_accumulate: forward kernel cannot be resident");
   const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, (int64_t)plan->fwd_tiles.size());
-  return launch_status(zl::launch_fwd(plan->d, p, grid, stream), "zl_attn_fwd_accumulate");
+  return launch_status(zl::launch_fwd(plan->d, plan->fwd_rows, p, grid, stream), "zl_attn_fwd_accumulate");
 }
 
 extern "C" zl_status zl_lse_merge(int32_t n_parts, int64_t n_rows, int32_t d_head, const float* o_part,

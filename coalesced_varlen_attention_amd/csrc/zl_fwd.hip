@@ -1,7 +1,6 @@
-// Forward kernel: persistent, per-XCD cost-ordered queues of (segment, head, 128 query rows)
-// items.
+// Forward kernel: persistent, per-XCD cost-ordered queues of (segment, head, query rows) items.
 //
-// Computes, per item, softmax attention of 128 query rows against the segment's key rows
+// Computes, per item, softmax attention of its query rows against the segment's key rows
 // (dense bidirectional attention of one sequence, Zellige page §II-A; segments never read
 // another sequence's keys, §IV-D), with an online softmax over blocks of 64 keys, and
 // writes either the final O and LSE at the query rows or, for a ring part, the normalised
@@ -12,7 +11,9 @@
 // device-scope counter) merges the pieces by their log-sum-exps, read back with
 // device-coherent loads, and stores the item's result as an unsplit item would.
 //
-// Shape of one workgroup: 4 waves x 32 query rows. Each wave keeps its 32 query rows in
+// Shape of one workgroup: W waves x 32 query rows, W = 4 (narrow items of 128 rows, two
+// workgroups per CU) or 8 (wide items of 256 rows, one workgroup per CU, every K/V block in LDS
+// shared by twice the rows); the plan picks the size. Each wave keeps its 32 query rows in
 // registers as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so every lane owns
 // one query row of the score tile: the running max and sum are per-lane values that only
 // combine with the partner lane l^32. The exponentiated scores, rounded to bf16, are already
@@ -46,9 +47,10 @@
 namespace zl {
 namespace {
 
-template <int D>
+template <int D, int W = 4>
 struct FwdCfg {
-  static constexpr int kThreads = 256;
+  static constexpr int kWaves = W;
+  static constexpr int kRows = 32 * W;                    // query rows per item
   static constexpr int kBk = 64;                          // keys per block
   static constexpr int kKb = kBk / 32;                    // 32x32 S^T tiles per block
   static constexpr int kKs = kBk / 16;                    // 16-key steps of O^T += V^T P^T
@@ -62,8 +64,8 @@ struct FwdCfg {
   static constexpr int kKbStride = 32 / kGroupRows * kGroupPitch;  // bytes between 32-row K tiles
   static constexpr int kVBytes = kBk * kRowBytes;
   static constexpr int kVCbStride = kBk * 64;             // bytes between V column blocks
-  static constexpr int kKDma = kBk / kGroupRows / 4;      // K loads per thread per block
-  static constexpr int kVDma = kVBytes / 1024 / 4;        // V loads per thread per block
+  static constexpr int kKDma = kBk / kGroupRows / W;      // K loads per thread per block
+  static constexpr int kVDma = kVBytes / 1024 / W;        // V loads per thread per block
   static_assert(kKDma >= 1 && kVDma >= 1, "every wave loads part of each block");
   static constexpr float kSlack = 8.0f;                   // lazy-rescale slack, log2 units
   static constexpr int kAhead = 2;                        // MFMAs between an operand read and its use
@@ -98,42 +100,42 @@ struct FwdState {
   float mx;     // row max of the pending score block, log2 units
 };
 
-// Global -> LDS load of K block blk. Lane offsets are relative to the block's first key row;
-// in a partial last block, rows past the end of the segment read its last row.
-template <int D>
+// Global -> LDS load of K block blk by W waves. Lane offsets are relative to the block's first
+// key row; in a partial last block, rows past the end of the segment read its last row.
+template <int D, int W>
 __device__ __forceinline__ void dma_k(const FwdCtx<D>& cx, uint32_t k_lds, int blk) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, W>;
   const char* base = (const char*)cx.kbase + (int64_t)blk * cx.blk_bytes;
   if ((blk + 1) * C::kBk <= cx.n_kv) {
 #pragma unroll
     for (int i = 0; i < C::kKDma; ++i)
-      lds_dma16(k_lds + (i * 4 + cx.wave) * C::kGroupPitch, base + i * cx.k_dma_step, cx.koff_dma);
+      lds_dma16(k_lds + (i * W + cx.wave) * C::kGroupPitch, base + i * cx.k_dma_step, cx.koff_dma);
   } else {
     const int last = cx.n_kv - 1 - blk * C::kBk;
 #pragma unroll
     for (int i = 0; i < C::kKDma; ++i) {
-      const int row = min((i * 4 + cx.wave) * C::kGroupRows + cx.dma_krow, last);
-      lds_dma16(k_lds + (i * 4 + cx.wave) * C::kGroupPitch, base, (uint32_t)row * cx.row_bytes + cx.dma_kcol);
+      const int row = min((i * W + cx.wave) * C::kGroupRows + cx.dma_krow, last);
+      lds_dma16(k_lds + (i * W + cx.wave) * C::kGroupPitch, base, (uint32_t)row * cx.row_bytes + cx.dma_kcol);
     }
   }
 }
 
 // Each 1 KB of the V tile is 16 keys x 64 bytes of one column block; load i of wave w fills
-// the (4i + w)-th such piece: column block (4i + w) / (kBk / 16), key group (4i + w) % (kBk / 16).
-template <int D>
+// the (Wi + w)-th such piece: column block (Wi + w) / (kBk / 16), key group (Wi + w) % (kBk / 16).
+template <int D, int W>
 __device__ __forceinline__ void dma_v(const FwdCtx<D>& cx, uint32_t v_lds, int blk) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, W>;
   const char* base = (const char*)cx.vbase + (int64_t)blk * cx.blk_bytes;
   if ((blk + 1) * C::kBk <= cx.n_kv) {
 #pragma unroll
     for (int i = 0; i < C::kVDma; ++i)
-      lds_dma16(v_lds + (i * 4 + cx.wave) * 1024, base + 64 * (4 / (C::kBk / 16)) * i, cx.voff_dma);
+      lds_dma16(v_lds + (i * W + cx.wave) * 1024, base + 64 * (W / (C::kBk / 16)) * i, cx.voff_dma);
   } else {
     const int row = min(cx.dma_vrow, cx.n_kv - 1 - blk * C::kBk);
 #pragma unroll
     for (int i = 0; i < C::kVDma; ++i)
-      lds_dma16(v_lds + (i * 4 + cx.wave) * 1024, base,
-                (uint32_t)row * cx.row_bytes + cx.dma_vcol + 64 * (4 / (C::kBk / 16)) * i);
+      lds_dma16(v_lds + (i * W + cx.wave) * 1024, base,
+                (uint32_t)row * cx.row_bytes + cx.dma_vcol + 64 * (W / (C::kBk / 16)) * i);
   }
 }
 
@@ -353,13 +355,13 @@ __device__ __forceinline__ void round_score_interleaved(const FwdCtx<D>& cx, uin
 //   region 1: the P(t-1) V(t-1) MFMAs, with the exponentials of S(t) computed in place;
 //   region 2: rounding of those exponentials into `pb` (free once region 1 has issued its
 //             MFMAs), with the S(t+1) MFMAs accumulating into `sc`, then its row max.
-template <int D, bool kPrev, bool kNext>
+template <int D, int W, bool kPrev, bool kNext>
 __device__ __forceinline__ void fwd_step(const FwdCtx<D>& cx, FwdState<D>& st, int t, uint32_t k_dma, uint32_t v_dma,
                                          uint32_t k_rd, uint32_t v_rd, f32x16 (&sc)[FwdCfg<D>::kKb],
                                          bf16x8 (&pb)[FwdCfg<D>::kKs], int hi) {
   using C = FwdCfg<D>;
-  if (kNext && t + 2 < cx.n_blk) dma_k<D>(cx, k_dma, t + 2);
-  dma_v<D>(cx, v_dma, t);
+  if (kNext && t + 2 < cx.n_blk) dma_k<D, W>(cx, k_dma, t + 2);
+  dma_v<D, W>(cx, v_dma, t);
 
   // Lazy rescaling: the exponent reference only moves when the block max exceeds it by more
   // than kSlack, so exponentials stay below 2^kSlack. P(t) uses the new reference; the
@@ -409,9 +411,9 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D>& cx, FwdState<D>& st, i
   __syncthreads();
 }
 
-template <int D, bool kPacked>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
-  using C = FwdCfg<D>;
+template <int D, bool kPacked, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void fwd_kernel(const FwdParams p) {
+  using C = FwdCfg<D, W>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::kVBytes + 2 * C::kKBytes];
   // LDS byte addresses of the double-buffered V and K blocks.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(ZL_LDS char*)smem;
@@ -468,7 +470,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
     cx.blk_bytes = (int64_t)C::kBk * cx.rs * 2;
     cx.koff_dma = (uint32_t)(wave * C::kGroupRows + cx.dma_krow) * cx.row_bytes + cx.dma_kcol;
     cx.voff_dma = (uint32_t)cx.dma_vrow * cx.row_bytes + cx.dma_vcol;
-    cx.k_dma_step = (int64_t)4 * C::kGroupRows * cx.rs * 2;
+    cx.k_dma_step = (int64_t)W * C::kGroupRows * cx.rs * 2;
     cx.n_kv = tile.kv_end - tile.kv_begin;  // the segment's keys, or one piece of them
     cx.n_blk = (cx.n_kv + C::kBk - 1) / C::kBk;
     cx.kbase = (const bf16*)p.k + (qr.k0 + (int64_t)tile.kv_begin * qr.t_stride + h) * D;
@@ -477,8 +479,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
 
     // Prologue: K(0), K(1) into LDS; this lane's query row into registers (clamped to the
     // last valid row; results of clamped rows are dropped); S(0) and its row max.
-    dma_k<D>(cx, k_lds0, 0);
-    if (n > 1) dma_k<D>(cx, k_lds1, 1);
+    dma_k<D, W>(cx, k_lds0, 0);
+    if (n > 1) dma_k<D, W>(cx, k_lds1, 1);
     const int qi = wave * 32 + l32;
     const bool q_valid = qi < tile.nrows;
     const int qtok = tile.row0 + (q_valid ? qi : tile.nrows - 1);
@@ -504,16 +506,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
     // Step t reads K(t+1) from k_lds[(t+1)&1] and V(t-1) from v_lds[(t-1)&1], and refills
     // k_lds[t&1] with K(t+2) and v_lds[t&1] with V(t).
     if (n == 1) {
-      fwd_step<D, false, false>(cx, st, 0, k_lds0, v_lds0, k_lds1, v_lds1, sc, pb, hi);
+      fwd_step<D, W, false, false>(cx, st, 0, k_lds0, v_lds0, k_lds1, v_lds1, sc, pb, hi);
     } else {
-      fwd_step<D, false, true>(cx, st, 0, k_lds0, v_lds0, k_lds1, v_lds1, sc, pb, hi);
+      fwd_step<D, W, false, true>(cx, st, 0, k_lds0, v_lds0, k_lds1, v_lds1, sc, pb, hi);
       for (int t = 1; t < n - 1; ++t) {
         const bool odd = t & 1;
-        fwd_step<D, true, true>(cx, st, t, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, odd ? k_lds0 : k_lds1,
+        fwd_step<D, W, true, true>(cx, st, t, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, odd ? k_lds0 : k_lds1,
                                 odd ? v_lds0 : v_lds1, sc, pb, hi);
       }
       const bool odd = (n - 1) & 1;
-      fwd_step<D, true, false>(cx, st, n - 1, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, odd ? k_lds0 : k_lds1,
+      fwd_step<D, W, true, false>(cx, st, n - 1, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, odd ? k_lds0 : k_lds1,
                                odd ? v_lds0 : v_lds1, sc, pb, hi);
     }
     value_block<D>(cx, ((n - 1) & 1) ? v_lds1 : v_lds0, pb, st.oacc);  // P(n-1) V(n-1)
@@ -535,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
       const int n_pieces = tile.piece >> 16;
       const int64_t slot = tile.split + (tile.piece & 0xffff);
       if (q_valid) {
-        float* so = p.split_o + (slot * kFwdRows + qi) * D;
+        float* so = p.split_o + (slot * C::kRows + qi) * D;
 #pragma unroll
         for (int cb = 0; cb < C::kCb; ++cb)
 #pragma unroll
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
             store_dev16(so + cb * 32 + 8 * g + 4 * hi, val);
           }
         if (hi == 0)
-          __hip_atomic_store(p.split_lse + slot * kFwdRows + qi, lse_b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(p.split_lse + slot * C::kRows + qi, lse_b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       store_dev_wait();
       __syncthreads();
@@ -555,20 +557,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
       __syncthreads();
       store = s_last;
       if (store && q_valid) {
-        const float* sl = p.split_lse + (int64_t)tile.split * kFwdRows + qi;
+        const float* sl = p.split_lse + (int64_t)tile.split * C::kRows + qi;
         float m = -INFINITY;
         for (int c = 0; c < n_pieces; ++c)
-          m = fmaxf(m, __hip_atomic_load(sl + c * kFwdRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          m = fmaxf(m, __hip_atomic_load(sl + c * C::kRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         float tot = 0.f;
         for (int c = 0; c < n_pieces; ++c)
-          tot += expf(__hip_atomic_load(sl + c * kFwdRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - m);
+          tot += expf(__hip_atomic_load(sl + c * C::kRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - m);
         lse_b = m + logf(tot);
 #pragma unroll
         for (int cb = 0; cb < C::kCb; ++cb) st.oacc[cb] = f32x16{};
         for (int c = 0; c < n_pieces; ++c) {
           const float w =
-              expf(__hip_atomic_load(sl + c * kFwdRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - lse_b);
-          const float* so = p.split_o + (((int64_t)tile.split + c) * kFwdRows + qi) * D + 4 * hi;
+              expf(__hip_atomic_load(sl + c * C::kRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - lse_b);
+          const float* so = p.split_o + (((int64_t)tile.split + c) * C::kRows + qi) * D + 4 * hi;
           // this lane's D/2 values of the row: D/8 chunks of 16 bytes, 8 floats apart; chunk k
           // holds (column block k/4, group k%4)
           f32x4 x[D / 8];
@@ -624,36 +626,48 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdParams p) {
   }
 }
 
-// Resident forward workgroups per compute unit, queried once (a function-local static, so
-// concurrent first calls are safe); 0 if the query fails.
-template <int D>
+// Resident forward workgroups per compute unit for W-wave items, queried once per instance (a
+// function-local static, so concurrent first calls are safe); 0 if the query fails.
+template <int D, int W>
 int blocks_per_cu_impl() {
   static const int cached = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<D, false>, 256, 0) != hipSuccess) n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<D, false, W>, 64 * W, 0) != hipSuccess) n = 0;
     return n;
   }();
   return cached;
 }
 
+template <int D, int W>
+void launch_fwd_impl(const FwdParams& p, int grid, hipStream_t s) {
+  if (p.packed)
+    hipLaunchKernelGGL((fwd_kernel<D, true, W>), dim3(grid), dim3(64 * W), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, false, W>), dim3(grid), dim3(64 * W), 0, s, p);
+}
+
 }  // namespace
 
-int fwd_blocks_per_cu(int d) { return d == 64 ? blocks_per_cu_impl<64>() : blocks_per_cu_impl<128>(); }
+int fwd_blocks_per_cu(int d, int rows) {
+  if (rows == kFwdRowsWide) return d == 64 ? blocks_per_cu_impl<64, 8>() : blocks_per_cu_impl<128, 8>();
+  return d == 64 ? blocks_per_cu_impl<64, 4>() : blocks_per_cu_impl<128, 4>();
+}
 
-int launch_fwd(int d, const FwdParams& p, int grid, void* stream) {
+int launch_fwd(int d, int rows, const FwdParams& p, int grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int64_t nz = std::max<int64_t>(p.n_split, p.visits ? p.n_visits : 0);
   const int zgrid = nz > 0 ? (int)std::min<int64_t>(64, (nz + 255) / 256) : 1;
   hipLaunchKernelGGL(zero_counters_kernel, dim3(zgrid), dim3(256), 0, s, p.queue.counters, grid, p.split_cnt,
                      p.n_split, p.visits, p.n_visits);
-  if (d == 64 && p.packed)
-    hipLaunchKernelGGL((fwd_kernel<64, true>), dim3(grid), dim3(256), 0, s, p);
+  const bool wide = rows == kFwdRowsWide;
+  if (d == 64 && wide)
+    launch_fwd_impl<64, 8>(p, grid, s);
   else if (d == 64)
-    hipLaunchKernelGGL((fwd_kernel<64, false>), dim3(grid), dim3(256), 0, s, p);
-  else if (p.packed)
-    hipLaunchKernelGGL((fwd_kernel<128, true>), dim3(grid), dim3(256), 0, s, p);
+    launch_fwd_impl<64, 4>(p, grid, s);
+  else if (wide)
+    launch_fwd_impl<128, 8>(p, grid, s);
   else
-    hipLaunchKernelGGL((fwd_kernel<128, false>), dim3(grid), dim3(256), 0, s, p);
+    launch_fwd_impl<128, 4>(p, grid, s);
   return hipPeekAtLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -10,11 +10,19 @@
 
 namespace zl {
 
-// Forward queue item: 128 query rows of one (segment, head). Backward dK/dV queue item: 128
-// key rows of one (segment, head), looping over the segment's query rows in blocks of 64.
+// Forward queue item: fwd_rows query rows of one (segment, head), 32 per wave of the forward
+// workgroup. A plan uses one size for all its forward items: narrow items (4 waves, two
+// workgroups per CU) or wide items (8 waves, one workgroup per CU). Backward dK/dV queue item:
+// 128 key rows of one (segment, head), looping over the segment's query rows in blocks of 64.
 // Backward dQ queue item: kDqRows query rows of one (final segment or ring group, head),
 // looping over every key range of the segment (all parts of a ring group).
-constexpr int kFwdRows = 128;
+constexpr int kFwdRowsNarrow = 128;
+constexpr int kFwdRowsWide = 256;
+// Wide items share each K/V block in LDS among 8 waves, which halves the global-to-LDS loads
+// per query row. But a compute unit sits idle once its one workgroup runs out of work, so a
+// plan takes them only when its forward queue holds at least kWideRounds rounds of wide items
+// for the resident workgroups.
+constexpr int kWideRounds = 8;
 constexpr int kDqWaves = 8;                // waves per dQ workgroup, 32 query rows each
 constexpr int kDqRows = 32 * kDqWaves;
 constexpr int kFwdKeys = 64;  // keys per forward step
@@ -30,9 +38,10 @@ constexpr int kSplitTargetWaves = 1;  // about one piece per resident workgroup:
                                       // costs a partial write and its share of a merge
 constexpr int kMaxPieces = 16;
 constexpr int kMinPieceKeys = 1024;
-// Resident workgroups assumed by a host-only plan: 256 CUs x 2 for the forward kernel, x 1 for
-// the dK/dV kernel, and one 8-wave (two 4-wave) dQ workgroups per CU.
+// Resident workgroups assumed by a host-only plan: 256 CUs x 2 for the narrow forward kernel,
+// x 1 for the wide one and for the dK/dV kernel, and one 8-wave (two 4-wave) dQ workgroups per CU.
 constexpr int kHostOnlySlots = 512;
+constexpr int kHostOnlyWideSlots = 256;
 constexpr int kHostOnlyKvSlots = 256;
 constexpr int kHostOnlyDqSlots = 256 * (8 / kDqWaves);
 constexpr int kBwdKeys = 128;
@@ -137,8 +146,8 @@ struct FwdParams {
   int32_t accumulate;  // ring parts fold into o/lse (running merge) instead of the slab
   int32_t n_split;     // pieces of split items (slots of split_cnt, split_o, split_lse)
   int32_t* split_cnt;  // per split item (at its piece-0 slot): pieces finished
-  float* split_o;      // [n_split][kFwdRows][D] normalised piece results
-  float* split_lse;    // [n_split][kFwdRows]
+  float* split_o;      // [n_split][fwd_rows][D] normalised piece results
+  float* split_lse;    // [n_split][fwd_rows]
   int32_t packed;      // Q, K, V in the QKV-packed layout (selects the kernel instance)
   int32_t* visits;     // per forward item: workgroups that took it (ZL_PLAN_COUNT_VISITS), or null
   int32_t n_visits;    // forward items (counters cleared before the launch)
@@ -180,14 +189,15 @@ struct BwdParams {
 };
 
 // Kernel launchers (defined next to their kernels). They return the launch status.
-int launch_fwd(int d, const FwdParams& p, int grid, void* stream);
+int launch_fwd(int d, int rows, const FwdParams& p, int grid, void* stream);
 int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages, void* stream);
 int launch_plan_merge(int d, const GroupDev* groups, int32_t n_groups, int64_t n_blocks, const float* o_part,
                       const float* lse_part, float* o, float* lse, int grid, void* stream);
 int launch_merge(int d, int32_t n_parts, int64_t n_rows, const float* o_part, const float* lse_part,
                  float* o, float* lse, int grid, void* stream);
-// Workgroups of each persistent kernel that fit on one compute unit.
-int fwd_blocks_per_cu(int d);
+// Workgroups of each persistent kernel that fit on one compute unit (the forward kernel's for
+// items of `rows` query rows).
+int fwd_blocks_per_cu(int d, int rows);
 int bwd_blocks_per_cu(int d);
 int dq_blocks_per_cu(int d);
 
@@ -208,6 +218,7 @@ struct zl_plan {
   int device = -1;
   int n_cu = 0;
   int64_t q_rows = 0, kv_rows = 0, part_rows = 0;
+  int32_t fwd_rows = zl::kFwdRowsNarrow;  // query rows per forward item
   int32_t n_parts_max = 0;
   double fwd_flops = 0.0;
   std::vector<zl::SegDev> segs;

@@ -245,8 +245,10 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   if (d_head != 64 && d_head != 128)
     return fail(ZL_ERR_UNSUPPORTED, "zl_plan_build: d_head " + std::to_string(d_head) + " is not 64 or 128");
   if (flags & ~(ZL_PLAN_HOST_ONLY | ZL_PLAN_NO_SPLIT | ZL_PLAN_QKV_PACKED | ZL_PLAN_COUNT_VISITS |
-                ZL_PLAN_DEFERRED_UPLOAD))
+                ZL_PLAN_DEFERRED_UPLOAD | ZL_PLAN_FWD_NARROW | ZL_PLAN_FWD_WIDE))
     return fail(ZL_ERR_INVALID, "zl_plan_build: unknown flag bits");
+  if ((flags & ZL_PLAN_FWD_NARROW) && (flags & ZL_PLAN_FWD_WIDE))
+    return fail(ZL_ERR_INVALID, "zl_plan_build: ZL_PLAN_FWD_NARROW and ZL_PLAN_FWD_WIDE exclude each other");
   if (n_seq < 1) return fail(ZL_ERR_INVALID, "zl_plan_build: n_seq must be >= 1");
   if (!cu_q || !cu_kv || !seq_heads) return fail(ZL_ERR_INVALID, "zl_plan_build: NULL sequence array");
   if (n_seg < 1 || !segs) return fail(ZL_ERR_INVALID, "zl_plan_build: need at least one segment");
@@ -442,6 +444,34 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     d.chain_len = (int32_t)members.size();
   }
 
+  if (!(flags & ZL_PLAN_HOST_ONLY)) {
+    if (hipGetDevice(&plan->device) != hipSuccess) return fail(ZL_ERR_HIP, "zl_plan_build: hipGetDevice failed");
+    if (hipDeviceGetAttribute(&plan->n_cu, hipDeviceAttributeMultiprocessorCount, plan->device) != hipSuccess ||
+        plan->n_cu < 1)
+      return fail(ZL_ERR_HIP, "zl_plan_build: cannot query the compute unit count");
+  }
+
+  // Forward item size: wide items when the forward queue holds at least kWideRounds rounds of
+  // them for the resident wide workgroups, unless a flag fixes the size.
+  {
+    int rows = (flags & ZL_PLAN_FWD_WIDE) ? zl::kFwdRowsWide : zl::kFwdRowsNarrow;
+    if (!(flags & (ZL_PLAN_FWD_NARROW | ZL_PLAN_FWD_WIDE))) {
+      int64_t wide_items = 0;
+      for (int i = 0; i < n_seg; ++i)
+        wide_items += (int64_t)(segs[i].head_end - segs[i].head_begin) *
+                      ((segs[i].q_end - segs[i].q_begin + zl::kFwdRowsWide - 1) / zl::kFwdRowsWide);
+      int64_t wide_slots = zl::kHostOnlyWideSlots;
+      if (!(flags & ZL_PLAN_HOST_ONLY)) {
+        const int per_cu = zl::fwd_blocks_per_cu(d_head, zl::kFwdRowsWide);
+        if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_plan_build: wide forward kernel cannot be resident");
+        wide_slots = (int64_t)plan->n_cu * per_cu;
+      }
+      if (wide_items >= (int64_t)zl::kWideRounds * wide_slots) rows = zl::kFwdRowsWide;
+    }
+    plan->fwd_rows = rows;
+  }
+  const int fwd_rows = plan->fwd_rows;
+
   // Work queues. Items of one (segment, head) that share K/V (forward, dQ) or Q/dO (dK/dV)
   // are grouped into chunks of bounded cost; chunks go to the kQueues per-XCD queues by
   // longest-processing-time-first, so that each head's data is mostly read through one XCD's
@@ -454,7 +484,7 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
       const zl_segment& g = segs[i];
       const size_t nh = (size_t)(g.head_end - g.head_begin);
       const size_t nq = (size_t)(g.q_end - g.q_begin), nk = (size_t)(g.kv_end - g.kv_begin);
-      n_fwd += nh * ((nq + zl::kFwdRows - 1) / zl::kFwdRows);
+      n_fwd += nh * ((nq + fwd_rows - 1) / fwd_rows);
       n_bwd += nh * ((nk + zl::kBwdKeys - 1) / zl::kBwdKeys);
       if (g.part <= 0) {
         n_dq += nh * ((nq + zl::kDqRows - 1) / zl::kDqRows);
@@ -481,8 +511,8 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
     }
     for (int h = g.head_begin; h < g.head_end; ++h) {
       const int64_t unit = (int64_t)i * 65536 + h;
-      for (int64_t r = g.q_begin; r < g.q_end; r += zl::kFwdRows) {
-        const int32_t n = (int32_t)std::min<int64_t>(zl::kFwdRows, g.q_end - r);
+      for (int64_t r = g.q_begin; r < g.q_end; r += fwd_rows) {
+        const int32_t n = (int32_t)std::min<int64_t>(fwd_rows, g.q_end - r);
         fwd.push_back({{i, h, (int32_t)r, n, g.kv_begin, g.kv_end, -1, 1 << 16}, (int64_t)n * nk});
         fwd_unit.push_back(unit);
       }
@@ -510,16 +540,10 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
             {i, g.head_begin, (int32_t)t, (int32_t)std::min<int64_t>(toks, g.q_end - t), 0, 0, -1, 1 << 16});
     }
   }
-  if (!(flags & ZL_PLAN_HOST_ONLY)) {
-    if (hipGetDevice(&plan->device) != hipSuccess) return fail(ZL_ERR_HIP, "zl_plan_build: hipGetDevice failed");
-    if (hipDeviceGetAttribute(&plan->n_cu, hipDeviceAttributeMultiprocessorCount, plan->device) != hipSuccess ||
-        plan->n_cu < 1)
-      return fail(ZL_ERR_HIP, "zl_plan_build: cannot query the compute unit count");
-  }
   if (!(flags & ZL_PLAN_NO_SPLIT)) {
-    int64_t slots = zl::kHostOnlySlots;
+    int64_t slots = fwd_rows == zl::kFwdRowsWide ? zl::kHostOnlyWideSlots : zl::kHostOnlySlots;
     if (!(flags & ZL_PLAN_HOST_ONLY)) {
-      const int per_cu = zl::fwd_blocks_per_cu(d_head);
+      const int per_cu = zl::fwd_blocks_per_cu(d_head, fwd_rows);
       if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_plan_build: forward kernel cannot be resident");
       slots = (int64_t)plan->n_cu * per_cu;
     }

@@ -36,8 +36,11 @@ def _rows(lay, s, q0, q1, h0, h1):
     return np.concatenate([lay.q_index(s, q0, q1, h) for h in range(h0, h1)])
 
 
-@pytest.mark.parametrize("d,order", [(64, (2, 0, 3, 1)), (128, (0, 1, 2, 3)), (128, (3, 2, 1, 0))])
-def test_ring_blocks_folded_one_call_at_a_time(d, order):
+@pytest.mark.parametrize("d,order,rows", [(64, (2, 0, 3, 1), None), (128, (0, 1, 2, 3), None),
+                                          (128, (3, 2, 1, 0), None), (64, (1, 3, 0, 2), 256),
+                                          (128, (2, 1, 3, 0), 256)])
+def test_ring_blocks_folded_one_call_at_a_time(d, order, rows):
+    """rows: the forward item size (256 forces the 8-wave forward; None is the plan's choice)."""
     z = H.zl()
     dev = torch.device("cuda:0")
     pack = W.Pack(f"acc{d}", SEQ_Q, SEQ_KV, HEADS, (WHOLE1,), d, 31 + d)
@@ -50,14 +53,14 @@ def test_ring_blocks_folded_one_call_at_a_time(d, order):
     o = torch.full((n_q, d), float("nan"), dtype=torch.float32, device=dev)
     lse = torch.full((n_q,), float("nan"), dtype=torch.float32, device=dev)
     lse[torch.as_tensor(np.concatenate([rows0, rows2]), device=dev)] = float("-inf")
-    print(f"[case] accumulate d={d} order={order}", flush=True)
+    print(f"[case] accumulate d={d} order={order} fwd_rows={rows or 'plan'}", flush=True)
     for i, b in enumerate(order):
         segs = [(0, 0, 3, 0, 150, BLOCKS0[b][0], BLOCKS0[b][1], 0)]
         if i < len(BLOCKS2):
             segs.append((2, 0, 2, 20, 100, BLOCKS2[i][0], BLOCKS2[i][1], 0))
         if i == 0:
             segs.append(WHOLE1)
-        plan = z.Plan(SEQ_Q, SEQ_KV, HEADS, tuple(segs), d)
+        plan = z.Plan(SEQ_Q, SEQ_KV, HEADS, tuple(segs), d, fwd_rows=rows)
         z.attn_fwd_accumulate(plan, q, k, v, o, lse)
         if i == 0:
             torch.cuda.synchronize()

@@ -46,12 +46,14 @@ def _same(name, a, b):
     assert torch.equal(torch.nan_to_num(a), torch.nan_to_num(b)), f"{name}: values differ"
 
 
-def _packed_matches(pack, ins, planar):
-    """Run `pack` in the QKV-packed layout and compare every output with the planar run bit for bit."""
+def _packed_matches(pack, ins, planar, rows=None):
+    """Run `pack` in the QKV-packed layout (forward items of `rows` query rows, or the plan's
+    choice) and compare every output with the planar run bit for bit."""
     z = H.zl()
     dev = torch.device("cuda:0")
     d = pack.d
-    plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, d, qkv_packed=True)
+    plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, d, qkv_packed=True, fwd_rows=rows)
+    assert plan.info["fwd_rows"] == planar["plan"].info["fwd_rows"]
     info = plan.info
     assert info["qkv_rows"] == 3 * info["q_rows"]
     qkv = _pack_qkv(pack, ins["q"].to(dev), ins["k"].to(dev), ins["v"].to(dev))
@@ -86,17 +88,18 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("rows", [None, 256])
 @pytest.mark.parametrize("d", [64, 128])
-def test_packed_matches_planar_bitwise(d):
+def test_packed_matches_planar_bitwise(d, rows):
     lens, heads, seg = CASES["mixed_segments"]
     pack = W.Pack(f"packed{d}", lens, lens, heads, seg, d, 90 + d)
     ins = W.draw(pack)
-    print(f"[case] packed vs planar d={d}", flush=True)
-    planar = H.run_pack(pack, ins)
+    print(f"[case] packed vs planar d={d} fwd_rows={rows or 'plan'}", flush=True)
+    planar = H.run_pack(pack, ins, fwd_rows=rows)
     assert planar["plan"].info["split_tiles"] > 0
     ref = H.oracle_pack(pack, ins)
     H.compare_full(pack, ins, planar, ref)
-    _packed_matches(pack, ins, planar)
+    _packed_matches(pack, ins, planar, rows)
 
 
 def test_packed_rejects_distinct_pointers():

@@ -3,7 +3,9 @@
 Packs with few long items make the plan cut every forward item into key pieces; the result
 must match the oracle element by element as an unsplit forward does, for final segments,
 ring parts (partials in the slab, then the plan merge) and the running merge, with ragged
-piece tails, at d_head 64 and 128. The backward runs on the split forward's O and LSE.
+piece tails, at d_head 64 and 128. The backward runs on the split forward's O and LSE. The
+whole-sequence and ring cases run with both forward item sizes (the pieces of a 256-row item
+use 256-row slots of the split workspace).
 """
 import numpy as np
 import pytest
@@ -16,28 +18,31 @@ from tests import gpu_harness as H
 pytestmark = [pytest.mark.gpu, H.requires_gpu]
 
 
-def _run(pack):
+def _run(pack, rows=None):
     ins = W.draw(pack)
-    print(f"[case] {pack.name} d={pack.d} seqs={pack.seq_q}/{pack.seq_kv} segs={len(pack.segments)}", flush=True)
-    out = H.run_pack(pack, ins)
+    print(f"[case] {pack.name} d={pack.d} seqs={pack.seq_q}/{pack.seq_kv} segs={len(pack.segments)} "
+          f"fwd_rows={rows or 'plan'}", flush=True)
+    out = H.run_pack(pack, ins, fwd_rows=rows)
     assert out["plan"].info["split_tiles"] > 0, "the pack was meant to be split"
     ref = H.oracle_pack(pack, ins)
     H.compare_full(pack, ins, out, ref)
     return out, ref, ins
 
 
+@pytest.mark.parametrize("rows", [None, 256])
 @pytest.mark.parametrize("d", [64, 128])
-def test_split_whole_sequences(d):
+def test_split_whole_sequences(d, rows):
     seg = ((0, 0, 1, 0, 4100, 0, 4100, -1), (1, 0, 2, 0, 700, 0, 2500, -1), (2, 0, 2, 0, 90, 0, 90, -1))
-    _run(W.Pack(f"split_whole{d}", (4100, 700, 90), (4100, 2500, 90), (1, 2, 2), seg, d, 51 + d))
+    _run(W.Pack(f"split_whole{d}", (4100, 700, 90), (4100, 2500, 90), (1, 2, 2), seg, d, 51 + d), rows)
 
 
+@pytest.mark.parametrize("rows", [None, 256])
 @pytest.mark.parametrize("d", [64, 128])
-def test_split_ring_parts(d):
+def test_split_ring_parts(d, rows):
     """Ring parts long enough to be split: each part's pieces merge into its slab rows, then
     the plan merge combines the parts."""
     seg = ((0, 0, 2, 0, 333, 0, 2100, 1), (0, 0, 2, 0, 333, 2100, 6000, 0), (1, 1, 2, 0, 150, 0, 3000, -1))
-    _run(W.Pack(f"split_ring{d}", (333, 150), (6000, 3000), (2, 2), seg, d, 61 + d))
+    _run(W.Pack(f"split_ring{d}", (333, 150), (6000, 3000), (2, 2), seg, d, 61 + d), rows)
 
 
 def test_split_matches_unsplit_plan():

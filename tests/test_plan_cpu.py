@@ -21,11 +21,41 @@ def expect_error(status, seq_q, seq_kv, heads, segs, d=128, scale=None, match=No
         assert match in str(e.value), str(e.value)
 
 
-@pytest.mark.parametrize("name,fwd,bwd", [("tiny", 44, 44), ("image", 10752, 10752), ("mixed", 33675, 33675),
-                                          ("ring", 23680, 23680), ("long", 29685, 29685)])
-def test_tile_counts(name, fwd, bwd):
+@pytest.mark.parametrize("name,rows,fwd,bwd", [("tiny", 128, 44, 44), ("image", 256, 5376, 10752),
+                                               ("mixed", 256, 16840, 33675), ("ring", 256, 11840, 23680),
+                                               ("long", 256, 14845, 29685), ("shard", 128, 1280, 1280)])
+def test_tile_counts(name, rows, fwd, bwd):
+    """Item counts, with the forward item size the plan picks: 256 rows when the forward queue
+    holds at least 8 rounds of 256-row items for the 256 resident wide workgroups of a host-only
+    plan (image: 5,376 items, 21 rounds), else 128 rows (the 5-head shard: 640 wide items, 2.5
+    rounds)."""
     p = host_plan(W.config(name))
+    assert p.info["fwd_rows"] == rows
     assert p.info["fwd_tiles"] == fwd and p.info["bwd_tiles"] == bwd
+    assert all(t[3] <= rows for t in p.tiles(0)) and max(t[3] for t in p.tiles(0)) == rows
+
+
+def test_forward_rows_rule_and_flags():
+    """The choice flips at exactly 8 rounds: 2,048 wide items for 256 host-only slots; the flags
+    fix the size either way and exclude each other."""
+    def plan(n_heads, **kw):  # n_heads x 8 wide items of one 2,048-token sequence
+        return z.Plan((2048,), (2048,), (n_heads,), ((0, 0, n_heads, 0, 2048, 0, 2048, -1),), 64,
+                      host_only=True, **kw)
+    assert plan(256).info["fwd_rows"] == 256 and plan(256).info["fwd_tiles"] == 2048
+    assert plan(255).info["fwd_rows"] == 128 and plan(255).info["fwd_tiles"] == 255 * 16
+    assert plan(255, fwd_rows=256).info["fwd_rows"] == 256
+    assert plan(256, fwd_rows=128).info["fwd_rows"] == 128
+    with pytest.raises(ValueError):
+        plan(4, fwd_rows=192)
+    lib = z.lib()
+    out = ctypes.c_void_p()
+    seg = z._Segment(0, 0, 1, 0, 4, 0, 4, -1)
+    cu = (ctypes.c_int64 * 2)(0, 4)
+    heads = (ctypes.c_int32 * 1)(1)
+    st = lib.zl_plan_build(1, ctypes.addressof(cu), ctypes.addressof(cu), ctypes.addressof(heads), 1,
+                           ctypes.addressof(seg), 64, 0.0, 1 | z.ZL_PLAN_FWD_NARROW | z.ZL_PLAN_FWD_WIDE,
+                           ctypes.byref(out))
+    assert st == ZL_ERR_INVALID and b"exclude" in lib.zl_last_error()
 
 
 @pytest.mark.parametrize("name", list(W.CONFIGS))
@@ -73,7 +103,7 @@ def test_queue_covers_every_block_once_in_cost_order(name, which):
     bounds = p.queues(which)
     assert len(bounds) == 9 and bounds[0] == 0 and bounds[-1] == len(tiles)
     assert all(a <= b for a, b in zip(bounds, bounds[1:]))
-    block = 128
+    block = p.info["fwd_rows"] if which == 0 else 128
     seen = set()
     for (seg, h, r0, n) in tiles:
         s, h0, h1, q0, q1, k0, k1, part = pack.segments[seg]
@@ -205,7 +235,7 @@ def test_bad_sequence_arrays():
                            ctypes.addressof(seg), 64, 0.0, 1, ctypes.byref(out))
     assert st == ZL_ERR_INVALID and b"seq_heads" in lib.zl_last_error()
     st = lib.zl_plan_build(1, ctypes.addressof(cu), ctypes.addressof(cu), ctypes.addressof(heads), 1,
-                           ctypes.addressof(seg), 64, 0.0, 32, ctypes.byref(out))
+                           ctypes.addressof(seg), 64, 0.0, 128, ctypes.byref(out))
     assert st == ZL_ERR_INVALID and b"flag" in lib.zl_last_error()
     assert lib.zl_plan_build(1, None, None, None, 1, None, 64, 0.0, 1, ctypes.byref(out)) == ZL_ERR_INVALID
 
@@ -287,6 +317,11 @@ def test_split_kv_cuts_long_items_of_a_short_queue():
     assert nosplit.info["split_tiles"] == 0 and nosplit.info["fwd_tiles"] == 64
     extra = p.info["ws_fwd"] - nosplit.info["ws_fwd"]
     assert extra >= 512 * (4 + 128 * 128 * 4 + 128 * 4)
+    # with 256-row items each piece holds 256 O rows and LSEs
+    wide = z.Plan((8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, host_only=True, fwd_rows=256)
+    assert wide.info["fwd_rows"] == 256 and wide.info["split_tiles"] == 32
+    n = wide.info["split_pieces"]
+    assert wide.info["ws_fwd"] - nosplit.info["ws_fwd"] >= n * (4 + 256 * 128 * 4 + 256 * 4)
 
 
 def test_split_kv_ragged_and_short_items():
