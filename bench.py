@@ -267,6 +267,8 @@ def main() -> int:
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a 2 GiB device copy (counter scale)")
     ap.add_argument("--no-split", action="store_true", help="build the plan without split-KV of forward items")
+    ap.add_argument("--item-rows", type=int, choices=(128, 256), default=None,
+                    help="fix the forward and dQ item sizes (default: the plan's choice)")
     ap.add_argument("--ring-fold", action="store_true",
                     help="forward ring groups block by block with the running merge (one launch per ring "
                          "block, folding into O/LSE) instead of one launch plus the LSE merge")
@@ -301,7 +303,7 @@ def main() -> int:
     # engine pays the warm figure (the median of five later builds, each destroyed after),
     # reported beside it. Neither is in the step.
     build = lambda: zl.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale,
-                            split=not args.no_split)
+                            split=not args.no_split, item_rows=args.item_rows)
     t0 = time.perf_counter()
     plan = build()
     plan_ms = (time.perf_counter() - t0) * 1e3
@@ -342,7 +344,7 @@ def main() -> int:
             if b == 0:
                 segs += tuple(sg for sg in pack.segments if sg[7] < 0)
             fold_plans.append(zl.Plan(pack.seq_q, pack.seq_kv, pack.heads, segs, pack.d, pack.scale,
-                                      split=not args.no_split))
+                                      split=not args.no_split, item_rows=args.item_rows))
         ws_f = torch.empty(max(fp.info["ws_fwd"] for fp in fold_plans), dtype=torch.uint8, device=dev)
     group_rows = [(g["o_row"], g["n_rows"]) for g in plan.groups]
     # The exact merge of ring partials: zl_lse_merge per group when every group covers all of its
@@ -393,7 +395,7 @@ def main() -> int:
     step()
     t0 = time.perf_counter()
     plan_next = zl.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale,
-                        split=not args.no_split, deferred=True)
+                        split=not args.no_split, item_rows=args.item_rows, deferred=True)
     plan_next.upload()
     plan_deferred_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
@@ -489,6 +491,7 @@ def main() -> int:
                        "ring_forward": (f"running merge, {len(fold_plans)} launches" if fold_plans
                                         else ("partials + zl_lse_merge" if lse_merge_calls is not None
                                               else "partials + zl_plan_merge") if has_groups else "none"),
+                       "item_rows": {"fwd": info["fwd_rows"], "dq": info["dq_rows"]},
                        "split_kv": {"fwd_items_split": info["split_tiles"], "pieces": info["split_pieces"],
                                     "dq_items_split": info["dq_split_tiles"], "dq_pieces": info["dq_split_pieces"],
                                     "dkdv_items_split": info["kv_split_tiles"], "dkdv_pieces": info["kv_split_pieces"]}},

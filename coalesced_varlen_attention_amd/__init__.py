@@ -40,8 +40,8 @@ ZL_PLAN_NO_SPLIT = 2
 ZL_PLAN_QKV_PACKED = 4
 ZL_PLAN_COUNT_VISITS = 8
 ZL_PLAN_DEFERRED_UPLOAD = 16
-ZL_PLAN_FWD_NARROW = 32
-ZL_PLAN_FWD_WIDE = 64
+ZL_PLAN_NARROW_ITEMS = 32
+ZL_PLAN_WIDE_ITEMS = 64
 BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ZL_NOALLOC_SCRATCH_BYTES
 SEGMENT_FIELDS = ("seq", "head_begin", "head_end", "q_begin", "q_end", "kv_begin", "kv_end", "part")
@@ -69,7 +69,8 @@ class _PlanInfo(ctypes.Structure):
                 ("dq_split_tiles", ctypes.c_int32), ("dq_split_pieces", ctypes.c_int32),
                 ("kv_split_tiles", ctypes.c_int32), ("kv_split_pieces", ctypes.c_int32),
                 ("visits_fwd", ctypes.c_int64), ("visits_dkdv", ctypes.c_int64), ("visits_dq", ctypes.c_int64),
-                ("dev_bytes", ctypes.c_size_t), ("fwd_rows", ctypes.c_int32)]
+                ("dev_bytes", ctypes.c_size_t), ("fwd_rows", ctypes.c_int32),
+                ("dq_rows", ctypes.c_int32)]
 
 
 class _GroupInfo(ctypes.Structure):
@@ -146,14 +147,14 @@ class Plan:
     ``segments``: tuples ``(seq, head_begin, head_end, q_begin, q_end, kv_begin, kv_end, part)``.
     ``count_visits``: the scheduler check of ``ZL_PLAN_COUNT_VISITS`` (read with ``visits``).
     ``deferred``: ``ZL_PLAN_DEFERRED_UPLOAD``; the plan runs after ``upload()``.
-    ``fwd_rows``: 128 or 256 fixes the forward item size (``ZL_PLAN_FWD_NARROW`` / ``_WIDE``);
-    None lets the plan choose (``info["fwd_rows"]``).
+    ``item_rows``: 128 or 256 fixes the forward and dQ item sizes (``ZL_PLAN_NARROW_ITEMS`` /
+    ``ZL_PLAN_WIDE_ITEMS``); None lets the plan choose (``info["fwd_rows"]``, ``info["dq_rows"]``).
     """
 
     def __init__(self, seq_q: Sequence[int], seq_kv: Sequence[int], heads: Sequence[int], segments, d: int,
                  scale: Optional[float] = None, host_only: bool = False, split: bool = True,
                  qkv_packed: bool = False, count_visits: bool = False, deferred: bool = False,
-                 fwd_rows: Optional[int] = None):
+                 item_rows: Optional[int] = None):
         n = len(seq_q)
         if len(seq_kv) != n or len(heads) != n:
             raise ValueError("seq_q, seq_kv and heads must have the same length")
@@ -171,10 +172,10 @@ class Plan:
         flags = ((ZL_PLAN_HOST_ONLY if host_only else 0) | (0 if split else ZL_PLAN_NO_SPLIT) |
                  (ZL_PLAN_QKV_PACKED if qkv_packed else 0) | (ZL_PLAN_COUNT_VISITS if count_visits else 0) |
                  (ZL_PLAN_DEFERRED_UPLOAD if deferred else 0))
-        if fwd_rows is not None:
-            if fwd_rows not in (128, 256):
-                raise ValueError("fwd_rows must be 128, 256 or None (the plan's choice)")
-            flags |= ZL_PLAN_FWD_WIDE if fwd_rows == 256 else ZL_PLAN_FWD_NARROW
+        if item_rows is not None:
+            if item_rows not in (128, 256):
+                raise ValueError("item_rows must be 128, 256 or None (the plan's choice)")
+            flags |= ZL_PLAN_WIDE_ITEMS if item_rows == 256 else ZL_PLAN_NARROW_ITEMS
         self._tables = None
         _check(lib().zl_plan_build(n, ctypes.cast(cu_q, ctypes.c_void_p), ctypes.cast(cu_kv, ctypes.c_void_p),
                                   ctypes.cast(hs, ctypes.c_void_p), len(segments), ctypes.cast(segs, ctypes.c_void_p),

@@ -61,7 +61,7 @@ void set_split(const zl_plan* plan, void* workspace, zl::FwdParams* p) {
 size_t dq_split_bytes(const zl_plan* plan) {
   const size_t n = (size_t)plan->dq_split_pieces;
   if (n == 0) return 0;
-  return align256(n * sizeof(int32_t)) + align256(n * zl::kDqRows * plan->d * sizeof(float));
+  return align256(n * sizeof(int32_t)) + align256(n * (size_t)plan->dq_rows * plan->d * sizeof(float));
 }
 
 // Then, for split dK/dV items: one counter per piece slot, then each piece's partial tau dK and
@@ -161,6 +161,7 @@ extern "C" zl_status zl_plan_info(const zl_plan* plan, zl_plan_info_t* info) {
   info->kv_split_pieces = plan->kv_split_pieces;
   info->dev_bytes = plan->dev_bytes;
   info->fwd_rows = plan->fwd_rows;
+  info->dq_rows = plan->dq_rows;
   info->visits_fwd = info->visits_dkdv = info->visits_dq = -1;
   if (counts_visits(plan)) {
     info->visits_fwd = (int64_t)fwd_visit_offset(plan);
@@ -390,12 +391,12 @@ extern "C" zl_status zl_attn_bwd_stages(const zl_plan* plan, const void* q, cons
   p.scale_log2 = plan->scale * 1.4426950408889634f;
   p.packed = (plan->flags & ZL_PLAN_QKV_PACKED) ? 1 : 0;
   const int per_cu = zl::bwd_blocks_per_cu(plan->d);
-  const int per_cu_dq = zl::dq_blocks_per_cu(plan->d);
+  const int per_cu_dq = zl::dq_blocks_per_cu(plan->d, plan->dq_rows);
   if (per_cu < 1 || per_cu_dq < 1) return fail(ZL_ERR_HIP, "zl_attn_bwd: backward kernels cannot be resident");
   const int grid = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu, (int64_t)plan->bwd_tiles.size());
   const int grid_dq = (int)std::min<int64_t>((int64_t)plan->n_cu * per_cu_dq, (int64_t)plan->dq_tiles.size());
   const int grid_pre = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)plan->n_cu * 8, p.n_pre));
   p.kv_grid = grid;
   p.dq_grid = grid_dq;
-  return launch_status(zl::launch_bwd(plan->d, p, grid_pre, grid, grid_dq, stages, stream), "zl_attn_bwd");
+  return launch_status(zl::launch_bwd(plan->d, plan->dq_rows, p, grid_pre, grid, grid_dq, stages, stream), "zl_attn_bwd");
 }

@@ -20,8 +20,9 @@
 //   loads into a ring of three stages, issued two steps ahead, so a step costs one barrier and
 //   waits only for loads issued a step earlier. dK and dV accumulate in registers and are
 //   written once.
-// dQ kernel: one item = kDqRows (256) query rows of one (segment or ring group, head);
-//   kDqWaves (8) waves x 32 query rows, the forward's shape per wave: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers
+// dQ kernel: one item = 32 W query rows of one (segment or ring group, head), W = 8 (256 rows,
+//   one workgroup per CU) for deep queues, else 4 (128 rows, two per CU); W waves x 32 query
+//   rows, the forward's shape per wave: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers
 //   (lane = one query row, whose LSE and D are then per-lane scalars), and
 //   dQ^T += K^T dS^T with K^T from transposed LDS reads. K and V blocks reach LDS by direct
 //   global-to-LDS loads in the key-major kernel's layout, one block ahead, walking the chain
@@ -596,9 +597,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------------------------
 // dQ kernel.
 
-template <int D>
+template <int D, int W = 8>
 struct DqCfg {
-  static constexpr int kWaves = kDqWaves;                 // 32 query rows each
+  static constexpr int kWaves = W;                        // 32 query rows each
+  static constexpr int kRows = 32 * W;                    // query rows per item
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kBk = kBwdRows;                    // keys per block (64)
   static constexpr int kSteps = D / 16;
@@ -614,11 +616,11 @@ struct DqCfg {
 
 // Global -> LDS loads of one key block: rows [0, 64) after `kblk` / `vblk` (the block's first
 // key row), rows at or past `rows` read row rows - 1.
-template <int D>
+template <int D, int W>
 __device__ __forceinline__ void dq_dma(uint32_t stage, const char* kblk, const char* vblk, int64_t rs_bytes, int rows,
                                        uint32_t lane_off, int lane_row, int lane_col, int wave) {
   using L = KvCfg<D>;
-  using C = DqCfg<D>;
+  using C = DqCfg<D, W>;
   if (rows >= L::kBq) {
 #pragma unroll
     for (int i = 0; i < C::kDma; ++i) {
@@ -732,9 +734,9 @@ __device__ __forceinline__ void dq_mask(f32x16& s, int vr) {
     if (8 * (i / 4) + (i % 4) >= vr) s[i] = -INFINITY;
 }
 
-template <int D, bool kPacked>
-__global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const BwdParams p) {
-  using C = DqCfg<D>;
+template <int D, bool kPacked, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void dq_kernel(const BwdParams p) {
+  using C = DqCfg<D, W>;
   using L = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
   __shared__ int32_t s_item;
@@ -811,7 +813,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
     }
     {
       const int64_t off = (int64_t)(cw.kv0 + cw.key0) * rs_bytes;
-      dq_dma<D>(lds0, kseq + off, vseq + off, rs_bytes, cw.n_kv - cw.key0, lane_off, dma_row, dma_col, wave_u);
+      dq_dma<D, W>(lds0, kseq + off, vseq + off, rs_bytes, cw.n_kv - cw.key0, lane_off, dma_row, dma_col, wave_u);
     }
 
     // This lane's query row (clamped; results of clamped rows are dropped), with its Q and dO
@@ -845,7 +847,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
       if (j + 1 < n_blk) {
         cw.next(C::kBk);
         const int64_t off = (int64_t)(cw.kv0 + cw.key0) * rs_bytes;
-        dq_dma<D>(lds0 + ((j + 1) & 1) * C::kStageBytes, kseq + off, vseq + off, rs_bytes, cw.n_kv - cw.key0,
+        dq_dma<D, W>(lds0 + ((j + 1) & 1) * C::kStageBytes, kseq + off, vseq + off, rs_bytes, cw.n_kv - cw.key0,
                   lane_off, dma_row, dma_col, wave_u);
       }
       ZL_LDS const char* kt = (ZL_LDS const char*)cur;
@@ -883,7 +885,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
       const int n_pieces = tile.piece >> 16;
       const int64_t slot = tile.split + (tile.piece & 0xffff);
       if (q_valid) {
-        float* so = p.dq_split + (slot * kDqRows + qi) * D;
+        float* so = p.dq_split + (slot * C::kRows + qi) * D;
 #pragma unroll
         for (int cb = 0; cb < C::kCb; ++cb)
 #pragma unroll
@@ -903,7 +905,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void dq_kernel(const B
 #pragma unroll
         for (int cb = 0; cb < C::kCb; ++cb) acc[cb] = f32x16{};
         for (int c = 0; c < n_pieces; ++c) {
-          const float* so = p.dq_split + (((int64_t)tile.split + c) * kDqRows + qi) * D + 4 * hi;
+          const float* so = p.dq_split + (((int64_t)tile.split + c) * C::kRows + qi) * D + 4 * hi;
           // this lane's D/2 values of the row: D/8 chunks of 16 bytes, 8 floats apart; chunk k
           // holds (column block k/4, group k%4)
           f32x4 x[D / 8];
@@ -950,29 +952,39 @@ int bwd_blocks_per_cu(int d) {
   return d == 64 ? c64 : c128;
 }
 
-int dq_blocks_per_cu(int d) {
-  static const int c64 = occupancy(dq_kernel<64, false>, DqCfg<64>::kThreads);
-  static const int c128 = occupancy(dq_kernel<128, false>, DqCfg<128>::kThreads);
-  return d == 64 ? c64 : c128;
+int dq_blocks_per_cu(int d, int rows) {
+  static const int c64w = occupancy(dq_kernel<64, false, 8>, DqCfg<64, 8>::kThreads);
+  static const int c128w = occupancy(dq_kernel<128, false, 8>, DqCfg<128, 8>::kThreads);
+  static const int c64n = occupancy(dq_kernel<64, false, 4>, DqCfg<64, 4>::kThreads);
+  static const int c128n = occupancy(dq_kernel<128, false, 4>, DqCfg<128, 4>::kThreads);
+  if (rows == kDqRowsWide) return d == 64 ? c64w : c128w;
+  return d == 64 ? c64n : c128n;
 }
 
 template <int D, bool kPacked>
-void launch_bwd_impl(const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages, hipStream_t s) {
+void launch_bwd_impl(const BwdParams& p, int dq_rows, int grid_pre, int grid, int grid_dq, unsigned stages,
+                     hipStream_t s) {
   if (stages & ZL_BWD_PRE) hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(grid_pre), dim3(256), 0, s, p);
   if (stages & ZL_BWD_DKDV) hipLaunchKernelGGL((dkdv_kernel<D, kPacked>), dim3(grid), dim3(256), 0, s, p);
-  if (stages & ZL_BWD_DQ) hipLaunchKernelGGL((dq_kernel<D, kPacked>), dim3(grid_dq), dim3(DqCfg<D>::kThreads), 0, s, p);
+  if (stages & ZL_BWD_DQ) {
+    if (dq_rows == kDqRowsWide)
+      hipLaunchKernelGGL((dq_kernel<D, kPacked, 8>), dim3(grid_dq), dim3(DqCfg<D, 8>::kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((dq_kernel<D, kPacked, 4>), dim3(grid_dq), dim3(DqCfg<D, 4>::kThreads), 0, s, p);
+  }
 }
 
-int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages, void* stream) {
+int launch_bwd(int d, int dq_rows, const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages,
+               void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (d == 64 && p.packed)
-    launch_bwd_impl<64, true>(p, grid_pre, grid, grid_dq, stages, s);
+    launch_bwd_impl<64, true>(p, dq_rows, grid_pre, grid, grid_dq, stages, s);
   else if (d == 64)
-    launch_bwd_impl<64, false>(p, grid_pre, grid, grid_dq, stages, s);
+    launch_bwd_impl<64, false>(p, dq_rows, grid_pre, grid, grid_dq, stages, s);
   else if (p.packed)
-    launch_bwd_impl<128, true>(p, grid_pre, grid, grid_dq, stages, s);
+    launch_bwd_impl<128, true>(p, dq_rows, grid_pre, grid, grid_dq, stages, s);
   else
-    launch_bwd_impl<128, false>(p, grid_pre, grid, grid_dq, stages, s);
+    launch_bwd_impl<128, false>(p, dq_rows, grid_pre, grid, grid_dq, stages, s);
   return hipPeekAtLastError() == hipSuccess ? 0 : 1;
 }
 

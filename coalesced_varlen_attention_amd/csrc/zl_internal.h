@@ -10,21 +10,21 @@
 
 namespace zl {
 
-// Forward queue item: fwd_rows query rows of one (segment, head), 32 per wave of the forward
-// workgroup. A plan uses one size for all its forward items: narrow items (4 waves, two
-// workgroups per CU) or wide items (8 waves, one workgroup per CU). Backward dK/dV queue item:
-// 128 key rows of one (segment, head), looping over the segment's query rows in blocks of 64.
-// Backward dQ queue item: kDqRows query rows of one (final segment or ring group, head),
-// looping over every key range of the segment (all parts of a ring group).
+// Query-major queue items: a forward item is fwd_rows query rows of one (segment, head); a
+// backward dQ item is dq_rows query rows of one (final segment or ring group, head), looping
+// over every key range of the segment (all parts of a ring group). Each is 32 rows per wave of
+// its workgroup, and a plan uses one size per queue: narrow items (4 waves, two workgroups per
+// CU) or wide items (8 waves, one workgroup per CU). Backward dK/dV queue item: 128 key rows
+// of one (segment, head), looping over the segment's query rows in blocks of 64.
 constexpr int kFwdRowsNarrow = 128;
 constexpr int kFwdRowsWide = 256;
+constexpr int kDqRowsNarrow = 128;
+constexpr int kDqRowsWide = 256;
 // Wide items share each K/V block in LDS among 8 waves, which halves the global-to-LDS loads
 // per query row. But a compute unit sits idle once its one workgroup runs out of work, so a
-// plan takes them only when its forward queue holds at least kWideRounds rounds of wide items
-// for the resident workgroups.
-constexpr int kWideRounds = 8;
-constexpr int kDqWaves = 8;                // waves per dQ workgroup, 32 query rows each
-constexpr int kDqRows = 32 * kDqWaves;
+// plan takes narrow items for a queue of 1 to kWideRounds rounds of wide items, and for a few
+// short items (see zl_plan_build).
+constexpr int kWideRounds = 4;
 constexpr int kFwdKeys = 64;  // keys per forward step
 // Split-KV of forward items (short queues leave compute units idle): a plan whose forward
 // queue holds fewer than kSplitWaves waves of items for the device's resident workgroups cuts
@@ -38,12 +38,11 @@ constexpr int kSplitTargetWaves = 1;  // about one piece per resident workgroup:
                                       // costs a partial write and its share of a merge
 constexpr int kMaxPieces = 16;
 constexpr int kMinPieceKeys = 1024;
-// Resident workgroups assumed by a host-only plan: 256 CUs x 2 for the narrow forward kernel,
-// x 1 for the wide one and for the dK/dV kernel, and one 8-wave (two 4-wave) dQ workgroups per CU.
+// Resident workgroups assumed by a host-only plan: 256 CUs x 2 for the narrow forward and dQ
+// kernels, x 1 for the wide ones and for the dK/dV kernel.
 constexpr int kHostOnlySlots = 512;
 constexpr int kHostOnlyWideSlots = 256;
 constexpr int kHostOnlyKvSlots = 256;
-constexpr int kHostOnlyDqSlots = 256 * (8 / kDqWaves);
 constexpr int kBwdKeys = 128;
 constexpr int kBwdRows = 64;
 // Rows (token, head pairs) per item of the backward pre-pass: one pass of its workgroup (16
@@ -177,7 +176,7 @@ struct BwdParams {
   int32_t packed;    // Q, K, V and their gradients in the QKV-packed layout (kernel instance)
   int32_t n_dq_split;     // pieces of split dQ items (slots of dq_split_cnt, dq_split)
   int32_t* dq_split_cnt;  // per split dQ item (at its piece-0 slot): pieces finished
-  float* dq_split;        // [n_dq_split][kDqRows][D] scaled partial dQ of each piece
+  float* dq_split;        // [n_dq_split][dq_rows][D] scaled partial dQ of each piece
   int32_t n_kv_split;     // pieces of split dK/dV items (slots of kv_split_cnt, kv_split)
   int32_t* kv_split_cnt;  // per split dK/dV item (at its piece-0 slot): pieces finished
   float* kv_split;        // [n_kv_split][kBwdKeys][2][D] partial tau dK and dV of each piece
@@ -190,7 +189,8 @@ struct BwdParams {
 
 // Kernel launchers (defined next to their kernels). They return the launch status.
 int launch_fwd(int d, int rows, const FwdParams& p, int grid, void* stream);
-int launch_bwd(int d, const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages, void* stream);
+int launch_bwd(int d, int dq_rows, const BwdParams& p, int grid_pre, int grid, int grid_dq, unsigned stages,
+               void* stream);
 int launch_plan_merge(int d, const GroupDev* groups, int32_t n_groups, int64_t n_blocks, const float* o_part,
                       const float* lse_part, float* o, float* lse, int grid, void* stream);
 int launch_merge(int d, int32_t n_parts, int64_t n_rows, const float* o_part, const float* lse_part,
@@ -199,7 +199,7 @@ int launch_merge(int d, int32_t n_parts, int64_t n_rows, const float* o_part, co
 // items of `rows` query rows).
 int fwd_blocks_per_cu(int d, int rows);
 int bwd_blocks_per_cu(int d);
-int dq_blocks_per_cu(int d);
+int dq_blocks_per_cu(int d, int rows);
 
 void set_error(const std::string& msg);
 
@@ -219,6 +219,7 @@ struct zl_plan {
   int n_cu = 0;
   int64_t q_rows = 0, kv_rows = 0, part_rows = 0;
   int32_t fwd_rows = zl::kFwdRowsNarrow;  // query rows per forward item
+  int32_t dq_rows = zl::kDqRowsNarrow;    // query rows per dQ item
   int32_t n_parts_max = 0;
   double fwd_flops = 0.0;
   std::vector<zl::SegDev> segs;

@@ -245,10 +245,10 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
   if (d_head != 64 && d_head != 128)
     return fail(ZL_ERR_UNSUPPORTED, "zl_plan_build: d_head " + std::to_string(d_head) + " is not 64 or 128");
   if (flags & ~(ZL_PLAN_HOST_ONLY | ZL_PLAN_NO_SPLIT | ZL_PLAN_QKV_PACKED | ZL_PLAN_COUNT_VISITS |
-                ZL_PLAN_DEFERRED_UPLOAD | ZL_PLAN_FWD_NARROW | ZL_PLAN_FWD_WIDE))
+                ZL_PLAN_DEFERRED_UPLOAD | ZL_PLAN_NARROW_ITEMS | ZL_PLAN_WIDE_ITEMS))
     return fail(ZL_ERR_INVALID, "zl_plan_build: unknown flag bits");
-  if ((flags & ZL_PLAN_FWD_NARROW) && (flags & ZL_PLAN_FWD_WIDE))
-    return fail(ZL_ERR_INVALID, "zl_plan_build: ZL_PLAN_FWD_NARROW and ZL_PLAN_FWD_WIDE exclude each other");
+  if ((flags & ZL_PLAN_NARROW_ITEMS) && (flags & ZL_PLAN_WIDE_ITEMS))
+    return fail(ZL_ERR_INVALID, "zl_plan_build: ZL_PLAN_NARROW_ITEMS and ZL_PLAN_WIDE_ITEMS exclude each other");
   if (n_seq < 1) return fail(ZL_ERR_INVALID, "zl_plan_build: n_seq must be >= 1");
   if (!cu_q || !cu_kv || !seq_heads) return fail(ZL_ERR_INVALID, "zl_plan_build: NULL sequence array");
   if (n_seg < 1 || !segs) return fail(ZL_ERR_INVALID, "zl_plan_build: need at least one segment");
@@ -451,26 +451,49 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
       return fail(ZL_ERR_HIP, "zl_plan_build: cannot query the compute unit count");
   }
 
-  // Forward item size: wide items when the forward queue holds at least kWideRounds rounds of
-  // them for the resident wide workgroups, unless a flag fixes the size.
+  // Query-major item sizes (forward and dQ queues), unless a flag fixes them. With r rounds of
+  // wide items for the resident wide workgroups:
+  //   r >= kWideRounds      wide: the tail is short, and each K/V block serves twice the rows;
+  //   1 < r < kWideRounds   narrow: a narrow unit's second workgroup keeps it busy through the
+  //                         tail, where a wide unit sits idle;
+  //   1/2 <= r <= 1         wide: every unit is busy with either size;
+  //   r < 1/2               wide if some item is long enough to be cut into key pieces (the
+  //                         split below then fills the device), else narrow, which spreads few
+  //                         short items over twice the units.
   {
-    int rows = (flags & ZL_PLAN_FWD_WIDE) ? zl::kFwdRowsWide : zl::kFwdRowsNarrow;
-    if (!(flags & (ZL_PLAN_FWD_NARROW | ZL_PLAN_FWD_WIDE))) {
-      int64_t wide_items = 0;
-      for (int i = 0; i < n_seg; ++i)
-        wide_items += (int64_t)(segs[i].head_end - segs[i].head_begin) *
-                      ((segs[i].q_end - segs[i].q_begin + zl::kFwdRowsWide - 1) / zl::kFwdRowsWide);
-      int64_t wide_slots = zl::kHostOnlyWideSlots;
-      if (!(flags & ZL_PLAN_HOST_ONLY)) {
-        const int per_cu = zl::fwd_blocks_per_cu(d_head, zl::kFwdRowsWide);
-        if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_plan_build: wide forward kernel cannot be resident");
-        wide_slots = (int64_t)plan->n_cu * per_cu;
-      }
-      if (wide_items >= (int64_t)zl::kWideRounds * wide_slots) rows = zl::kFwdRowsWide;
+    int64_t wide_fwd = 0, wide_dq = 0, keys_fwd = 0, keys_dq = 0;
+    for (int i = 0; i < n_seg; ++i) {
+      const int64_t n = (int64_t)(segs[i].head_end - segs[i].head_begin) *
+                        ((segs[i].q_end - segs[i].q_begin + zl::kFwdRowsWide - 1) / zl::kFwdRowsWide);
+      wide_fwd += n;
+      keys_fwd = std::max<int64_t>(keys_fwd, segs[i].kv_end - segs[i].kv_begin);
+      if (segs[i].part > 0) continue;  // a ring group's dQ items belong to its part 0
+      wide_dq += n;
+      int64_t chain = 0;
+      for (int c = 0; c < plan->segs[i].chain_len; ++c)
+        chain += plan->kv_ranges[2 * (plan->segs[i].chain_off + c) + 1] - plan->kv_ranges[2 * (plan->segs[i].chain_off + c)];
+      keys_dq = std::max(keys_dq, chain);
     }
-    plan->fwd_rows = rows;
+    int64_t fwd_slots = zl::kHostOnlyWideSlots, dq_slots = zl::kHostOnlyWideSlots;
+    if (!(flags & ZL_PLAN_HOST_ONLY)) {
+      const int per_cu = zl::fwd_blocks_per_cu(d_head, zl::kFwdRowsWide);
+      const int per_cu_dq = zl::dq_blocks_per_cu(d_head, zl::kDqRowsWide);
+      if (per_cu < 1 || per_cu_dq < 1) return fail(ZL_ERR_HIP, "zl_plan_build: wide kernels cannot be resident");
+      fwd_slots = (int64_t)plan->n_cu * per_cu;
+      dq_slots = (int64_t)plan->n_cu * per_cu_dq;
+    }
+    const bool split = !(flags & ZL_PLAN_NO_SPLIT);
+    auto wide = [&](int64_t items, int64_t slots, int64_t longest_keys) {
+      if (flags & (ZL_PLAN_NARROW_ITEMS | ZL_PLAN_WIDE_ITEMS)) return (flags & ZL_PLAN_WIDE_ITEMS) != 0;
+      if (items >= (int64_t)zl::kWideRounds * slots) return true;
+      if (items > slots) return false;
+      if (2 * items >= slots) return true;
+      return split && longest_keys >= 2 * zl::kMinPieceKeys;
+    };
+    plan->fwd_rows = wide(wide_fwd, fwd_slots, keys_fwd) ? zl::kFwdRowsWide : zl::kFwdRowsNarrow;
+    plan->dq_rows = wide(wide_dq, dq_slots, keys_dq) ? zl::kDqRowsWide : zl::kDqRowsNarrow;
   }
-  const int fwd_rows = plan->fwd_rows;
+  const int fwd_rows = plan->fwd_rows, dq_rows = plan->dq_rows;
 
   // Work queues. Items of one (segment, head) that share K/V (forward, dQ) or Q/dO (dK/dV)
   // are grouped into chunks of bounded cost; chunks go to the kQueues per-XCD queues by
@@ -487,7 +510,7 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
       n_fwd += nh * ((nq + fwd_rows - 1) / fwd_rows);
       n_bwd += nh * ((nk + zl::kBwdKeys - 1) / zl::kBwdKeys);
       if (g.part <= 0) {
-        n_dq += nh * ((nq + zl::kDqRows - 1) / zl::kDqRows);
+        n_dq += nh * ((nq + dq_rows - 1) / dq_rows);
         n_pre += nq / (size_t)std::max<size_t>(1, zl::kPreRows / nh) + 1;
       }
     }
@@ -517,8 +540,8 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
         fwd_unit.push_back(unit);
       }
       if (g.part <= 0)
-        for (int64_t r = g.q_begin; r < g.q_end; r += zl::kDqRows) {
-          const int32_t n = (int32_t)std::min<int64_t>(zl::kDqRows, g.q_end - r);
+        for (int64_t r = g.q_begin; r < g.q_end; r += dq_rows) {
+          const int32_t n = (int32_t)std::min<int64_t>(dq_rows, g.q_end - r);
           // A dQ item's key range is its block range [0, chain_blocks) of the segment's chain.
           dq.push_back({{i, h, (int32_t)r, n, 0, (int32_t)chain_blocks, -1, 1 << 16}, (int64_t)n * chain_keys});
           dq_unit.push_back(unit);
@@ -548,9 +571,9 @@ extern "C" zl_status zl_plan_build(int32_t n_seq, const int64_t* cu_q, const int
       slots = (int64_t)plan->n_cu * per_cu;
     }
     split_forward(slots, &fwd, &fwd_unit, &plan->split_tiles, &plan->split_pieces);
-    int64_t dq_slots = zl::kHostOnlyDqSlots;
+    int64_t dq_slots = dq_rows == zl::kDqRowsWide ? zl::kHostOnlyWideSlots : zl::kHostOnlySlots;
     if (!(flags & ZL_PLAN_HOST_ONLY)) {
-      const int per_cu = zl::dq_blocks_per_cu(d_head);
+      const int per_cu = zl::dq_blocks_per_cu(d_head, dq_rows);
       if (per_cu < 1) return fail(ZL_ERR_HIP, "zl_plan_build: dQ kernel cannot be resident");
       dq_slots = (int64_t)plan->n_cu * per_cu;
     }

@@ -100,6 +100,7 @@ typedef struct {
   size_t dev_bytes;        /* bytes of the plan's device tables (0 for a host-only plan): what
                               zl_plan_upload needs for a ZL_PLAN_DEFERRED_UPLOAD plan */
   int32_t fwd_rows;        /* query rows per forward item: 128 or 256 (see zl_plan_build) */
+  int32_t dq_rows;         /* query rows per dQ item: 128 or 256 */
 } zl_plan_info_t;
 
 /*
@@ -140,9 +141,9 @@ typedef struct {
                                    the offsets zl_plan_info reports (visits_*). The forward launch
                                    clears the forward's, the backward pre-pass the backward's. After
                                    a forward and a backward every counter must read exactly 1. */
-#define ZL_PLAN_FWD_NARROW 32u /* forward items of 128 query rows whatever the queue's depth */
-#define ZL_PLAN_FWD_WIDE 64u   /* forward items of 256 query rows whatever the queue's depth (at
-                                  most one of the two; see zl_plan_build) */
+#define ZL_PLAN_NARROW_ITEMS 32u /* forward and dQ items of 128 query rows whatever the queues' depth */
+#define ZL_PLAN_WIDE_ITEMS 64u   /* forward and dQ items of 256 query rows whatever the queues' depth
+                                    (at most one of the two; see zl_plan_build) */
 
 /*
  * Validate the segment list and lower it into device work queues.
@@ -155,23 +156,23 @@ typedef struct {
  *   softmax_scale         tau in softmax(tau * Q K^T); <= 0 selects 1/sqrt(d_head)
  *   flags                 0 or an OR of ZL_PLAN_HOST_ONLY, ZL_PLAN_NO_SPLIT, ZL_PLAN_QKV_PACKED,
  *                         ZL_PLAN_COUNT_VISITS, ZL_PLAN_DEFERRED_UPLOAD and at most one of
- *                         ZL_PLAN_FWD_NARROW, ZL_PLAN_FWD_WIDE
+ *                         ZL_PLAN_NARROW_ITEMS, ZL_PLAN_WIDE_ITEMS
  *   out                   receives the plan; the caller frees it with zl_plan_destroy
  * The host arrays are copied; the plan owns its device tables (allocated on the current
  * device) and nothing else. The forward queue holds one item per (segment, head, block of
- * info.fwd_rows query rows): 256-row items (one 8-wave workgroup per compute unit, each K/V
- * block shared by twice the rows) when the queue holds at least 8 rounds of them for the
- * resident workgroups, else 128-row items (two 4-wave workgroups per compute unit, which keep a
- * unit busy while one of them runs out of work); ZL_PLAN_FWD_WIDE or ZL_PLAN_FWD_NARROW fixes
- * the choice. The backward has a dK/dV queue with one item per (segment, head, block of 128 key
- * rows) and a dQ queue with one item per (final segment or ring group, head, block of 256 query
- * rows). Each is split into one queue per XCD (zl_plan_queues): chunks of
+ * info.fwd_rows query rows); the backward has a dK/dV queue with one item per (segment, head,
+ * block of 128 key rows) and a dQ queue with one item per (final segment or ring group, head,
+ * block of info.dq_rows query rows). Each query-major queue (forward, dQ) takes 256-row items
+ * (one 8-wave workgroup per compute unit, each K/V block in LDS shared by twice the rows) when it
+ * holds at least 8 rounds of them for the resident workgroups, else 128-row items (two 4-wave
+ * workgroups per compute unit, which keep a unit busy while one of them runs out of work);
+ * ZL_PLAN_WIDE_ITEMS or ZL_PLAN_NARROW_ITEMS fixes both choices. Each is split into one queue per XCD (zl_plan_queues): chunks of
  * consecutive items of one (segment, head) go to the least-loaded queue, largest first, and
  * each queue is sorted by decreasing cost (rows x length of the other side), ties kept in
  * (segment, head, block) order. A workgroup drains its own XCD's queue, then the others.
  * Split-KV: when the forward queue holds fewer items than there are resident forward
  * workgroups (the device's CU count times the kernel's occupancy; for a host-only plan 512
- * for 128-row items, 256 for 256-row items),
+ * for 128-row items, 256 for 256-row items and for the dK/dV kernel),
  * so that compute units would sit idle, every item costing more than a workgroup's fair share
  * (the queue's total cost over the resident workgroups) is cut into block-aligned key pieces
  * of about that share (at most 16, each at least 1024 keys). Each piece is a normalised partial over its keys; the

@@ -69,14 +69,14 @@ def row_bound(ref: np.ndarray) -> np.ndarray:
     return b[:, None] if r.ndim > 1 else b
 
 
-def make_plan(pack: W.Pack, fwd_rows=None):
-    """The pack's plan; ``fwd_rows`` 128 or 256 fixes the forward item size (None: the plan's
-    choice, which is 128 rows for every pack small enough for the oracle)."""
+def make_plan(pack: W.Pack, item_rows=None):
+    """The pack's plan; ``item_rows`` 128 or 256 fixes the forward and dQ item sizes (None: the
+    plan's choice, which is 128 rows for every pack small enough for the oracle)."""
     z = zl()
-    return z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale, fwd_rows=fwd_rows)
+    return z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, pack.scale, item_rows=item_rows)
 
 
-def run_pack(pack: W.Pack, ins: dict, fill=float("nan"), fwd_rows=None):
+def run_pack(pack: W.Pack, ins: dict, fill=float("nan"), item_rows=None):
     """Forward, ring merges and backward of a whole pack on cuda:0. Returns device tensors.
 
     Output buffers start filled with ``fill`` so that rows no segment covers can be checked
@@ -84,9 +84,9 @@ def run_pack(pack: W.Pack, ins: dict, fill=float("nan"), fwd_rows=None):
     """
     z = zl()
     dev = torch.device("cuda:0")
-    plan = make_plan(pack, fwd_rows)
-    if fwd_rows is not None:
-        assert plan.info["fwd_rows"] == fwd_rows
+    plan = make_plan(pack, item_rows)
+    if item_rows is not None:
+        assert plan.info["fwd_rows"] == item_rows and plan.info["dq_rows"] == item_rows
     info = plan.info
     q, k, v, do = (ins[n].to(dev) for n in ("q", "k", "v", "do"))
     o = torch.full((info["q_rows"], pack.d), fill, dtype=torch.float32, device=dev)

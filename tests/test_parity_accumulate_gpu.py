@@ -53,14 +53,14 @@ def test_ring_blocks_folded_one_call_at_a_time(d, order, rows):
     o = torch.full((n_q, d), float("nan"), dtype=torch.float32, device=dev)
     lse = torch.full((n_q,), float("nan"), dtype=torch.float32, device=dev)
     lse[torch.as_tensor(np.concatenate([rows0, rows2]), device=dev)] = float("-inf")
-    print(f"[case] accumulate d={d} order={order} fwd_rows={rows or 'plan'}", flush=True)
+    print(f"[case] accumulate d={d} order={order} item_rows={rows or 'plan'}", flush=True)
     for i, b in enumerate(order):
         segs = [(0, 0, 3, 0, 150, BLOCKS0[b][0], BLOCKS0[b][1], 0)]
         if i < len(BLOCKS2):
             segs.append((2, 0, 2, 20, 100, BLOCKS2[i][0], BLOCKS2[i][1], 0))
         if i == 0:
             segs.append(WHOLE1)
-        plan = z.Plan(SEQ_Q, SEQ_KV, HEADS, tuple(segs), d, fwd_rows=rows)
+        plan = z.Plan(SEQ_Q, SEQ_KV, HEADS, tuple(segs), d, item_rows=rows)
         z.attn_fwd_accumulate(plan, q, k, v, o, lse)
         if i == 0:
             torch.cuda.synchronize()

@@ -52,7 +52,7 @@ def _packed_matches(pack, ins, planar, rows=None):
     z = H.zl()
     dev = torch.device("cuda:0")
     d = pack.d
-    plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, d, qkv_packed=True, fwd_rows=rows)
+    plan = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, d, qkv_packed=True, item_rows=rows)
     assert plan.info["fwd_rows"] == planar["plan"].info["fwd_rows"]
     info = plan.info
     assert info["qkv_rows"] == 3 * info["q_rows"]
@@ -94,8 +94,8 @@ def test_packed_matches_planar_bitwise(d, rows):
     lens, heads, seg = CASES["mixed_segments"]
     pack = W.Pack(f"packed{d}", lens, lens, heads, seg, d, 90 + d)
     ins = W.draw(pack)
-    print(f"[case] packed vs planar d={d} fwd_rows={rows or 'plan'}", flush=True)
-    planar = H.run_pack(pack, ins, fwd_rows=rows)
+    print(f"[case] packed vs planar d={d} item_rows={rows or 'plan'}", flush=True)
+    planar = H.run_pack(pack, ins, item_rows=rows)
     assert planar["plan"].info["split_tiles"] > 0
     ref = H.oracle_pack(pack, ins)
     H.compare_full(pack, ins, planar, ref)

@@ -24,8 +24,8 @@ ROWS = pytest.mark.parametrize("rows", [None, 256])
 def _run(pack, ins=None, stress=False, rows=None):
     ins = W.draw(pack) if ins is None else ins
     print(f"[case] {pack.name} d={pack.d} seqs={pack.seq_q}/{pack.seq_kv} segs={len(pack.segments)} "
-          f"fwd_rows={rows or 'plan'}", flush=True)
-    out = H.run_pack(pack, ins, fwd_rows=rows)
+          f"item_rows={rows or 'plan'}", flush=True)
+    out = H.run_pack(pack, ins, item_rows=rows)
     ref = H.oracle_pack(pack, ins)
     H.compare_full(pack, ins, out, ref, scaled_max_abs=stress)
     return out, ref
@@ -138,7 +138,7 @@ def test_bitwise_reproducible(rows):
     seg = ((0, 0, 2, 0, 300, 0, 200, 0), (0, 0, 2, 0, 300, 200, 500, 1), (1, 0, 3, 0, 129, 0, 129, -1))
     pack = W.Pack("repro", (300, 129), (500, 129), (2, 3), seg, 128, 19)
     ins = W.draw(pack)
-    a = H.run_pack(pack, ins, fwd_rows=rows)
-    b = H.run_pack(pack, ins, fwd_rows=rows)
+    a = H.run_pack(pack, ins, item_rows=rows)
+    b = H.run_pack(pack, ins, item_rows=rows)
     for n in ("o", "lse", "dq", "dk", "dv", "o_part", "lse_part"):
         assert torch.equal(a[n].cpu(), b[n].cpu()), n

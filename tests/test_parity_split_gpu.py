@@ -21,8 +21,8 @@ pytestmark = [pytest.mark.gpu, H.requires_gpu]
 def _run(pack, rows=None):
     ins = W.draw(pack)
     print(f"[case] {pack.name} d={pack.d} seqs={pack.seq_q}/{pack.seq_kv} segs={len(pack.segments)} "
-          f"fwd_rows={rows or 'plan'}", flush=True)
-    out = H.run_pack(pack, ins, fwd_rows=rows)
+          f"item_rows={rows or 'plan'}", flush=True)
+    out = H.run_pack(pack, ins, item_rows=rows)
     assert out["plan"].info["split_tiles"] > 0, "the pack was meant to be split"
     ref = H.oracle_pack(pack, ins)
     H.compare_full(pack, ins, out, ref)

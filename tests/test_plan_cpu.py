@@ -21,39 +21,53 @@ def expect_error(status, seq_q, seq_kv, heads, segs, d=128, scale=None, match=No
         assert match in str(e.value), str(e.value)
 
 
-@pytest.mark.parametrize("name,rows,fwd,bwd", [("tiny", 128, 44, 44), ("image", 256, 5376, 10752),
-                                               ("mixed", 256, 16840, 33675), ("ring", 256, 11840, 23680),
-                                               ("long", 256, 14845, 29685), ("shard", 128, 1280, 1280)])
-def test_tile_counts(name, rows, fwd, bwd):
-    """Item counts, with the forward item size the plan picks: 256 rows when the forward queue
-    holds at least 8 rounds of 256-row items for the 256 resident wide workgroups of a host-only
-    plan (image: 5,376 items, 21 rounds), else 128 rows (the 5-head shard: 640 wide items, 2.5
-    rounds)."""
+@pytest.mark.parametrize("name,rows,fwd,bwd,dq_rows,dq", [
+    ("tiny", 128, 44, 44, 128, 44), ("image", 256, 5376, 10752, 256, 5376),
+    ("mixed", 256, 16840, 33675, 256, 16840), ("ring", 256, 11840, 23680, 256, 1480),
+    ("long", 256, 14845, 29685, 256, 14845), ("shard", 128, 1280, 1280, 128, 1280)])
+def test_tile_counts(name, rows, fwd, bwd, dq_rows, dq):
+    """Item counts, with the query-major item sizes the plan picks: 256 rows when the queue holds
+    at least 4 rounds of 256-row items for the 256 resident wide workgroups of a host-only plan
+    (image: 5,376 items, 21 rounds; the ring shard's dQ queue, one item list per group rather
+    than per part: 1,480 items, 5.8 rounds), else 128 rows (the 5-head shard: 640 wide items,
+    2.5 rounds; the tiny pack's 24, too short to split)."""
     p = host_plan(W.config(name))
-    assert p.info["fwd_rows"] == rows
-    assert p.info["fwd_tiles"] == fwd and p.info["bwd_tiles"] == bwd
+    assert p.info["fwd_rows"] == rows and p.info["dq_rows"] == dq_rows
+    assert p.info["fwd_tiles"] == fwd and p.info["bwd_tiles"] == bwd and p.info["dq_tiles"] == dq
     assert all(t[3] <= rows for t in p.tiles(0)) and max(t[3] for t in p.tiles(0)) == rows
+    assert max(t[3] for t in p.tiles(2)) == dq_rows
 
 
-def test_forward_rows_rule_and_flags():
-    """The choice flips at exactly 8 rounds: 2,048 wide items for 256 host-only slots; the flags
-    fix the size either way and exclude each other."""
-    def plan(n_heads, **kw):  # n_heads x 8 wide items of one 2,048-token sequence
-        return z.Plan((2048,), (2048,), (n_heads,), ((0, 0, n_heads, 0, 2048, 0, 2048, -1),), 64,
-                      host_only=True, **kw)
-    assert plan(256).info["fwd_rows"] == 256 and plan(256).info["fwd_tiles"] == 2048
-    assert plan(255).info["fwd_rows"] == 128 and plan(255).info["fwd_tiles"] == 255 * 16
-    assert plan(255, fwd_rows=256).info["fwd_rows"] == 256
-    assert plan(256, fwd_rows=128).info["fwd_rows"] == 128
+def test_item_rows_rule_and_flags():
+    """The size rule for r rounds of wide items (256 host-only wide workgroups), for the forward
+    and the dQ queue alike: wide from 4 rounds (1,024 items); narrow above one round and below 4;
+    wide from half a round to one; below half a round wide only if split pieces will fill the
+    device (an item of at least 2,048 keys, split on). The flags fix both sizes either way and
+    exclude each other."""
+    def plan(n_heads, keys=2048, **kw):  # n_heads x 8 wide items of one 2,048-query sequence
+        return z.Plan((2048,), (keys,), (n_heads,), ((0, 0, n_heads, 0, 2048, 0, keys, -1),), 64,
+                      host_only=True, **kw).info
+    def rows(info):
+        return info["fwd_rows"], info["dq_rows"]
+    assert rows(plan(128)) == (256, 256) and plan(128)["fwd_tiles"] == plan(128)["dq_tiles"] == 1024
+    assert rows(plan(127)) == (128, 128) and plan(127)["fwd_tiles"] == 127 * 16
+    assert rows(plan(33)) == (128, 128)                               # 264 items: just over one round
+    assert rows(plan(32)) == rows(plan(16)) == (256, 256)             # 256 and 128 items
+    assert rows(plan(16, keys=100, split=False)) == (256, 256)
+    assert rows(plan(15)) == (256, 256) and plan(15)["split_tiles"] > 0 and plan(15)["dq_split_tiles"] > 0
+    assert rows(plan(15, keys=2047)) == (128, 128)                    # too short to cut into two pieces
+    assert rows(plan(15, split=False)) == (128, 128)
+    assert rows(plan(127, item_rows=256)) == (256, 256)
+    assert rows(plan(128, item_rows=128)) == (128, 128)
     with pytest.raises(ValueError):
-        plan(4, fwd_rows=192)
+        plan(4, item_rows=192)
     lib = z.lib()
     out = ctypes.c_void_p()
     seg = z._Segment(0, 0, 1, 0, 4, 0, 4, -1)
     cu = (ctypes.c_int64 * 2)(0, 4)
     heads = (ctypes.c_int32 * 1)(1)
     st = lib.zl_plan_build(1, ctypes.addressof(cu), ctypes.addressof(cu), ctypes.addressof(heads), 1,
-                           ctypes.addressof(seg), 64, 0.0, 1 | z.ZL_PLAN_FWD_NARROW | z.ZL_PLAN_FWD_WIDE,
+                           ctypes.addressof(seg), 64, 0.0, 1 | z.ZL_PLAN_NARROW_ITEMS | z.ZL_PLAN_WIDE_ITEMS,
                            ctypes.byref(out))
     assert st == ZL_ERR_INVALID and b"exclude" in lib.zl_last_error()
 
@@ -294,9 +308,10 @@ def _pieces_by_item(p):
 
 
 def test_split_kv_cuts_long_items_of_a_short_queue():
-    """One head of 8192 tokens: 64 forward items, far below 4 per resident workgroup (512
-    assumed for a host-only plan), so every item is cut into 8 key pieces of 1024 keys."""
-    p = z.Plan((8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, host_only=True)
+    """One head of 8192 tokens in 128-row forward items: 64 items, far below one per resident
+    workgroup (512 assumed for a host-only plan), so every item is cut into 8 key pieces of 1024
+    keys. (Left to choose, the plan takes 256-row items here, whose pieces fill its 256 slots.)"""
+    p = z.Plan((8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, host_only=True, item_rows=128)
     assert p.info["split_tiles"] == 64 and p.info["split_pieces"] == 64 * 8
     assert p.info["fwd_tiles"] == 64 * 8
     slots = set()
@@ -313,12 +328,13 @@ def test_split_kv_cuts_long_items_of_a_short_queue():
         slots.add(pieces[0][2])
     assert sorted(slots) == list(range(0, 512, 8))
     # the workspace holds a counter, 128 O rows and 128 LSEs per piece
-    nosplit = z.Plan((8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, host_only=True, split=False)
+    nosplit = z.Plan((8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, host_only=True, split=False,
+                     item_rows=128)
     assert nosplit.info["split_tiles"] == 0 and nosplit.info["fwd_tiles"] == 64
     extra = p.info["ws_fwd"] - nosplit.info["ws_fwd"]
     assert extra >= 512 * (4 + 128 * 128 * 4 + 128 * 4)
     # with 256-row items each piece holds 256 O rows and LSEs
-    wide = z.Plan((8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, host_only=True, fwd_rows=256)
+    wide = z.Plan((8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, host_only=True, item_rows=256)
     assert wide.info["fwd_rows"] == 256 and wide.info["split_tiles"] == 32
     n = wide.info["split_pieces"]
     assert wide.info["ws_fwd"] - nosplit.info["ws_fwd"] >= n * (4 + 256 * 128 * 4 + 256 * 4)
@@ -342,8 +358,8 @@ def test_split_kv_ragged_and_short_items():
 def test_split_kv_leaves_large_packs_alone():
     for name in ("image", "mixed", "ring", "long", "shard"):
         assert host_plan(W.config(name)).info["split_tiles"] == 0, name
-    p = host_plan(W.config("head1"))  # 256 items < 512 resident workgroups: 2 pieces each
-    assert p.info["split_tiles"] == 256 and p.info["split_pieces"] == 256 * 2
+    p = host_plan(W.config("head1"))  # 128 wide items < 256 resident wide workgroups: 2 pieces each
+    assert p.info["fwd_rows"] == 256 and p.info["split_tiles"] == 128 and p.info["split_pieces"] == 128 * 2
 
 
 def test_qkv_packed_plan():
@@ -364,15 +380,15 @@ def _dq_pieces(p):
 
 
 def test_dq_split_cuts_items_of_a_short_queue():
-    """One head of 8192 tokens: 8192 / R dQ items of R query rows over a chain of 128 key blocks,
-    far fewer than the resident dQ workgroups a host-only plan assumes (one per CU x 256 CUs for
-    8-wave workgroups): each item becomes 8 pieces of 16 blocks (1024 keys), contiguous, with one
-    workspace slot per item."""
+    """One head of 8192 tokens: 32 dQ items of 256 query rows over a chain of 128 key blocks, far
+    fewer than the resident wide dQ workgroups a host-only plan assumes (one per CU x 256 CUs):
+    each item becomes 8 pieces of 16 blocks (1024 keys), contiguous, with one workspace slot per
+    item."""
     seg = ((0, 0, 1, 0, 8192, 0, 8192, -1),)
-    p = z.Plan((8192,), (8192,), (1,), seg, 128, host_only=True)
-    nosplit = z.Plan((8192,), (8192,), (1,), seg, 128, host_only=True, split=False)
+    p = z.Plan((8192,), (8192,), (1,), seg, 128, host_only=True, item_rows=256)
+    nosplit = z.Plan((8192,), (8192,), (1,), seg, 128, host_only=True, split=False, item_rows=256)
     rows = max(t[3] for t in nosplit.tiles(2))
-    assert rows in (128, 256)
+    assert rows == 256 and p.info["dq_rows"] == 256
     n_items = 8192 // rows
     assert p.info["dq_split_tiles"] == n_items and p.info["dq_split_pieces"] == 8 * n_items
     assert p.info["dq_tiles"] == 8 * n_items and nosplit.info["dq_split_tiles"] == 0
@@ -424,7 +440,8 @@ def test_random_packs_build_valid_plans():
         pack = R.random_pack(seed)
         p = z.Plan(pack.seq_q, pack.seq_kv, pack.heads, pack.segments, pack.d, host_only=True)
         assert p.info["q_rows"] == pack.q_rows() and p.info["kv_rows"] == pack.kv_rows()
-        n_fwd = sum((s[2] - s[1]) * -(-(s[4] - s[3]) // 128) for s in pack.segments)
+        rows = p.info["fwd_rows"]
+        n_fwd = sum((s[2] - s[1]) * -(-(s[4] - s[3]) // rows) for s in pack.segments)
         assert len({t[:3] for t in p.tiles(0)}) == n_fwd
         n_bwd = sum((s[2] - s[1]) * -(-(s[6] - s[5]) // 128) for s in pack.segments)
         assert len({t[:3] for t in p.tiles(1)}) == n_bwd
