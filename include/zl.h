@@ -163,10 +163,12 @@ typedef struct {
  * info.fwd_rows query rows); the backward has a dK/dV queue with one item per (segment, head,
  * block of 128 key rows) and a dQ queue with one item per (final segment or ring group, head,
  * block of info.dq_rows query rows). Each query-major queue (forward, dQ) takes 256-row items
- * (one 8-wave workgroup per compute unit, each K/V block in LDS shared by twice the rows) when it
- * holds at least 8 rounds of them for the resident workgroups, else 128-row items (two 4-wave
- * workgroups per compute unit, which keep a unit busy while one of them runs out of work);
- * ZL_PLAN_WIDE_ITEMS or ZL_PLAN_NARROW_ITEMS fixes both choices. Each is split into one queue per XCD (zl_plan_queues): chunks of
+ * (one 8-wave workgroup per compute unit, each K/V block in LDS shared by twice the rows) or
+ * 128-row items (two 4-wave workgroups per compute unit, which keep a unit busy while one of
+ * them runs out of work). With r rounds of 256-row items for the resident workgroups: 256 rows
+ * for r >= 4; 128 for 1 < r < 4; 256 for 1/2 <= r <= 1; below that 256 if some item has at
+ * least 2048 keys and split-KV (below) is on, else 128. ZL_PLAN_WIDE_ITEMS or
+ * ZL_PLAN_NARROW_ITEMS fixes both choices. Each is split into one queue per XCD (zl_plan_queues): chunks of
  * consecutive items of one (segment, head) go to the least-loaded queue, largest first, and
  * each queue is sorted by decreasing cost (rows x length of the other side), ties kept in
  * (segment, head, block) order. A workgroup drains its own XCD's queue, then the others.
