@@ -374,19 +374,26 @@ def main() -> int:
                         lse_part=lse_part if has_groups else None, workspace=ws_f)
 
     def step(ev=None):
-        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
-        rec(0)
+        """One step. With `ev` (six events) the backward runs as its three stage launches with an
+        event around each; without, as one call."""
+        if ev is None:
+            forward()
+            if has_groups and not fold_plans:
+                merge()
+            zl.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+            return
+        ev[0].record(stream)
         forward()
-        rec(1)
+        ev[1].record(stream)
         if has_groups and not fold_plans:
             merge()
-        rec(2)
+        ev[2].record(stream)
         zl.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b, stages=zl.BWD_PRE)
-        rec(3)
+        ev[3].record(stream)
         zl.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b, stages=zl.BWD_DKDV)
-        rec(4)
+        ev[4].record(stream)
         zl.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b, stages=zl.BWD_DQ)
-        rec(5)
+        ev[5].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -400,12 +407,18 @@ def main() -> int:
     plan_deferred_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
     plan_next.close()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # Per-kernel durations come from HIP events on the launch stream inside the timed region, on
+    # a tenth of the steps (at least one, spread evenly): a timing event costs the GPU a few us,
+    # which on a 0.07 ms step would be a third of the step.
+    n_inst = max(1, args.steps // 10)
+    every = args.steps // n_inst
+    instrumented = [j * every + every // 2 for j in range(n_inst)]
+    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(6)] for i in instrumented}
     torch.cuda.synchronize()
     finish_power = start_power_sampler() if args.power else None
     t_start = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(events.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     smi = finish_power() if finish_power else None
@@ -425,8 +438,8 @@ def main() -> int:
             graph.replay()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
-    avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in events) / args.steps
-    per_step = sorted(e[0].elapsed_time(e[5]) for e in events)
+    avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in events.values()) / len(events)
+    per_step = sorted(e[0].elapsed_time(e[5]) for e in events.values())
     fwd_ms, merge_ms, pre_ms, dkdv_ms, dq_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4), avg(4, 5)
     bwd_ms = pre_ms + dkdv_ms + dq_ms
     ms_per_step = wall * 1e3 / args.steps
