@@ -89,12 +89,29 @@ KERNEL_SOURCES = [os.path.join(ROOT, "coalesced_varlen_attention_amd", "csrc", f
     os.path.join(ROOT, "coalesced_varlen_attention_amd", "build.py")]  # compile flags shape the kernels too
 
 
+def _code_only(path: str) -> bytes:
+    """The source without comments and with whitespace runs collapsed, so that an edit of
+    comments alone leaves the hash (and the counters stored under it) valid."""
+    import io
+    import re
+    import tokenize
+    with open(path) as fh:
+        text = fh.read()
+    if path.endswith(".py"):
+        toks = [t for t in tokenize.generate_tokens(io.StringIO(text).readline) if t.type != tokenize.COMMENT]
+        text = " ".join(t.string for t in toks if t.string.strip())
+    else:  # C++: drop // and /* */ comments, keep string literals (inline assembly)
+        pat = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+        text = pat.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+        text = " ".join(text.split())
+    return text.encode()
+
+
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        h.update(_code_only(f))
     return h.hexdigest()[:16]
 
 

@@ -41,8 +41,8 @@ namespace zl {
 namespace {
 
 // ---------------------------------------------------------------------------------------------
-// Pre-pass: D_i = sum_c dO_ic O_ic and LSE_i log2(e) for every covered query row (16 lanes per
-// row), written head-major.
+// Pre-pass: -D_i = -sum_c dO_ic O_ic and -LSE_i / tau for every covered query row (16 lanes per
+// row, 8 rows in flight per lane group), written head-major.
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
