@@ -138,6 +138,7 @@ struct KvCfg {
   static constexpr int kDmaPerStep = 2 * kDma;            // tile loads per wave per step (+1 rows
                                                           // load on waves 0 and 1)
   static constexpr int kSub = kSteps / 4;                 // k-steps per operand base
+  static constexpr int kAhead = 3;                        // MFMAs between an operand read and its use
 };
 
 // Chunk swizzle of row r (r % 8 matters only).
@@ -249,39 +250,41 @@ __device__ __forceinline__ f32x16 kv_rowinit(ZL_LDS const float* vals, int mb, i
   return r;
 }
 
-// The first two operands of a phase: the row reads of scores half mb, or the transposed reads
-// of gradients half mb.
+// Operand m of a phase: the row reads of scores half mb, or the transposed reads of gradients
+// half mb (used for a phase's first kAhead operands).
 template <int D, bool kGrads>
 __device__ __forceinline__ bf16x8 kv_first_op(ZL_LDS const char* qt, ZL_LDS const char* dot, const int (&rbase)[4],
                                               const int (&tbase)[KvCfg<D>::kCb], int mb, int m) {
-  if (kGrads) return kv_tr_op<D>(m & 1 ? qt : dot, tbase, mb, 0, 0);
-  return kv_row_op<D>(m & 1 ? dot : qt, rbase, mb, 0);
+  if (kGrads) return kv_tr_op<D>(m & 1 ? qt : dot, tbase, mb, (m >> 1) / KvCfg<D>::kCb, (m >> 1) % KvCfg<D>::kCb);
+  return kv_row_op<D>(m & 1 ? dot : qt, rbase, mb, m >> 1);
 }
 
 // S' = Q K^T - LSE / tau and dP' = dO V^T - D of one 32-row half (16 MFMAs, alternating; sacc
-// and dpacc hold the row initialisers on entry), operands two MFMAs ahead: the first two come
-// in `first`, and the last two slots read the next phase's first two into `next` (the scores
-// of half 1 after half 0, the gradients of half 0 after half 1), so that no phase starts on an
-// LDS wait. With kValu, the P = exp2(S' tau log2e) and dS = P dP' of the other half (element m
-// per MFMA, rounded per 8) in the slots.
+// and dpacc hold the row initialisers on entry), operands kAhead (three) MFMAs ahead: the first
+// kAhead come in `first`, and the last kAhead slots read the next phase's first kAhead into
+// `next` (the scores of half 1 after half 0, the gradients of half 0 after half 1), so that no
+// phase starts on an LDS wait. With kValu, the P = exp2(S' tau log2e) and dS = P dP' of the
+// other half (element m per MFMA, rounded per 8) in the slots.
 template <int D, bool kValu>
 __device__ __forceinline__ void kv_scores(ZL_LDS const char* qt, ZL_LDS const char* dot, const int (&rbase)[4],
                                           const int (&tbase)[KvCfg<D>::kCb], int mb,
                                           const bf16x8 (&kreg)[KvCfg<D>::kSteps],
                                           const bf16x8 (&vreg)[KvCfg<D>::kSteps], f32x16& sacc, f32x16& dpacc,
                                           const f32x16& s_o, const f32x16& dp_o, float scale_log2, bf16x8 (&pb)[2],
-                                          bf16x8 (&dsb)[2], const bf16x8 (&first)[2], bf16x8 (&next)[2]) {
+                                          bf16x8 (&dsb)[2], const bf16x8 (&first)[KvCfg<D>::kAhead],
+                                          bf16x8 (&next)[KvCfg<D>::kAhead]) {
   using C = KvCfg<D>;
   constexpr int kM = 2 * C::kSteps;
+  constexpr int A = C::kAhead;
   bf16x8 op[kM];
-  op[0] = first[0];
-  op[1] = first[1];
+#pragma unroll
+  for (int j = 0; j < A; ++j) op[j] = first[j];
   f32x8 pe, ds;
 #pragma unroll
   for (int m = 0; m < kM; ++m) {
-    if (m + 2 < kM) op[m + 2] = kv_row_op<D>((m + 2) & 1 ? dot : qt, rbase, mb, (m + 2) >> 1);
-    else if (mb == 0) next[m + 2 - kM] = kv_first_op<D, false>(qt, dot, rbase, tbase, 1, m + 2 - kM);
-    else next[m + 2 - kM] = kv_first_op<D, true>(qt, dot, rbase, tbase, 0, m + 2 - kM);
+    if (m + A < kM) op[m + A] = kv_row_op<D>((m + A) & 1 ? dot : qt, rbase, mb, (m + A) >> 1);
+    else if (mb == 0) next[m + A - kM] = kv_first_op<D, false>(qt, dot, rbase, tbase, 1, m + A - kM);
+    else next[m + A - kM] = kv_first_op<D, true>(qt, dot, rbase, tbase, 0, m + A - kM);
     if (m & 1)
       dpacc = mfma32(op[m], vreg[m >> 1], dpacc);
     else
@@ -303,27 +306,29 @@ __device__ __forceinline__ void kv_scores(ZL_LDS const char* qt, ZL_LDS const ch
 }
 
 // dV^T += dO^T P and dK^T += Q^T dS of one half (16 MFMAs, alternating), transposed operands
-// two MFMAs ahead; with kValu, the P / dS of the other half in the slots.
-// (Half 0's last two slots read half 1's first two operands into `next`; half 1 has none.)
+// kAhead MFMAs ahead; with kValu, the P / dS of the other half in the slots.
+// (Half 0's last kAhead slots read half 1's first kAhead operands into `next`; half 1 has none.)
 template <int D, bool kValu>
 __device__ __forceinline__ void kv_grads(ZL_LDS const char* qt, ZL_LDS const char* dot,
                                          const int (&tbase)[KvCfg<D>::kCb], int mb, const bf16x8 (&pb)[2],
                                          const bf16x8 (&dsb)[2], f32x16 (&dv_acc)[KvCfg<D>::kCb],
                                          f32x16 (&dk_acc)[KvCfg<D>::kCb], const f32x16& s_o, const f32x16& dp_o,
                                          float scale_log2, bf16x8 (&pb_o)[2], bf16x8 (&dsb_o)[2],
-                                         const bf16x8 (&first)[2], bf16x8 (&next)[2]) {
+                                         const bf16x8 (&first)[KvCfg<D>::kAhead], bf16x8 (&next)[KvCfg<D>::kAhead]) {
   using C = KvCfg<D>;
   constexpr int kM = 4 * C::kCb;  // (hs, cb) x {dV, dK}
+  constexpr int A = C::kAhead;
   bf16x8 op[kM];
-  op[0] = first[0];
-  op[1] = first[1];
+#pragma unroll
+  for (int j = 0; j < A; ++j) op[j] = first[j];
   f32x8 pe, ds;
 #pragma unroll
   for (int m = 0; m < kM; ++m) {
-    if (m + 2 < kM)
-      op[m + 2] = kv_tr_op<D>((m + 2) & 1 ? qt : dot, tbase, mb, ((m + 2) >> 1) / C::kCb, ((m + 2) >> 1) % C::kCb);
+    if (m + A < kM)
+      op[m + A] = kv_tr_op<D>((m + A) & 1 ? qt : dot, tbase, mb, ((m + A) >> 1) / C::kCb, ((m + A) >> 1) % C::kCb);
     else if (mb == 0)
-      next[m + 2 - kM] = kv_tr_op<D>((m + 2 - kM) & 1 ? qt : dot, tbase, 1, 0, 0);
+      next[m + A - kM] = kv_tr_op<D>((m + A - kM) & 1 ? qt : dot, tbase, 1, ((m + A - kM) >> 1) / C::kCb,
+                                     ((m + A - kM) >> 1) % C::kCb);
     const int hs = (m >> 1) / C::kCb, cb = (m >> 1) % C::kCb;
     if (m & 1)
       mfma32_acc(op[m], dsb[hs], dk_acc[cb]);
@@ -487,9 +492,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
       dp0 = kv_rowinit(dd_s, 0, hi);
       s1 = kv_rowinit(lse_s, 1, hi);
       dp1 = kv_rowinit(dd_s, 1, hi);
-      bf16x8 opa[2], opb[2];
-      opa[0] = kv_first_op<D, false>(qt, dot, rbase, tbase, 0, 0);
-      opa[1] = kv_first_op<D, false>(qt, dot, rbase, tbase, 0, 1);
+      bf16x8 opa[C::kAhead], opb[C::kAhead];
+#pragma unroll
+      for (int j = 0; j < C::kAhead; ++j) opa[j] = kv_first_op<D, false>(qt, dot, rbase, tbase, 0, j);
       kv_scores<D, false>(qt, dot, rbase, tbase, 0, kreg, vreg, s0, dp0, s1, dp1, p.scale_log2, pb1, dsb1, opa, opb);
       __builtin_amdgcn_sched_barrier(0);
       kv_scores<D, true>(qt, dot, rbase, tbase, 1, kreg, vreg, s1, dp1, s0, dp0, p.scale_log2, pb0, dsb0, opb, opa);
