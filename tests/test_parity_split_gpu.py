@@ -160,3 +160,38 @@ def test_dkdv_split_many_queries(d):
     out = H.run_pack(pack, ins)
     assert out["plan"].info["kv_split_tiles"] > 0, "the dK/dV queue was meant to be split"
     H.compare_full(pack, ins, out, H.oracle_pack(pack, ins), row_scaled=True)
+
+
+@pytest.mark.parametrize("name", ["dq_split_repro", "ring_group"])
+def test_staged_backward_matches_one_call(name):
+    """The pre-pass, dK/dV and dQ launched by three calls on one workspace (the way the
+    benchmark times them) give the same bits as one call: the pre-pass alone sets both queues'
+    counters, the split counters and the row values the later launches read. Cases: one head of
+    3,000 tokens (dQ and dK/dV queues cut into pieces) and a ring group with a whole sequence."""
+    z = H.zl()
+    dev = torch.device("cuda:0")
+    if name == "dq_split_repro":
+        pack = W.Pack(name, (3000,), (3000,), (2,), ((0, 0, 2, 0, 3000, 0, 3000, -1),), 128, 97)
+    else:
+        seg = ((0, 0, 2, 0, 300, 0, 200, 0), (0, 0, 2, 0, 300, 200, 500, 1), (1, 0, 3, 0, 129, 0, 129, -1))
+        pack = W.Pack(name, (300, 129), (500, 129), (2, 3), seg, 128, 19)
+    ins = W.draw(pack)
+    q, k, v, do = (ins[n].to(dev) for n in ("q", "k", "v", "do"))
+    print(f"[case] staged backward: {name}", flush=True)
+    plan = H.make_plan(pack)
+    if name == "dq_split_repro":
+        assert plan.info["dq_split_tiles"] > 0 and plan.info["kv_split_tiles"] > 0
+    o, lse, o_part, lse_part = z.attn_fwd(plan, q, k, v)
+    if plan.info["n_groups"]:
+        z.merge_groups(plan, o_part, lse_part, o, lse)
+    one = z.attn_bwd(plan, q, k, v, o, lse, do)
+    info = plan.info
+    nan = lambda rows: torch.full((rows, pack.d), float("nan"), device=dev)
+    dq, dk, dv = nan(info["q_rows"]), nan(info["kv_rows"]), nan(info["kv_rows"])
+    ws = torch.empty(info["ws_bwd"], dtype=torch.uint8, device=dev)
+    for stage in (z.BWD_PRE, z.BWD_DKDV, z.BWD_DQ):
+        z.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, stages=stage)
+    torch.cuda.synchronize()
+    for n, a, b in zip(("dq", "dk", "dv"), one, (dq, dk, dv)):
+        assert torch.equal(torch.isnan(a), torch.isnan(b)), n
+        assert torch.equal(torch.nan_to_num(a), torch.nan_to_num(b)), f"{n}: staged calls differ from one call"
