@@ -5,11 +5,12 @@ backward, Zellige page §V-A). For the longest heads of the benchmark packs the 
 minutes per head to produce them, too long for a test, so this script computes them once and
 the full-size parity test reads them back:
   * mixed pack (seed 3): the 5 heads of the 75,600-token Ulysses shard (sequence 22);
-  * long pack (seed 5): heads 0 and 4 of the 497,760-token shard (sequence 0).
+  * long pack (seed 5): the 5 heads of the 497,760-token shard (sequence 0).
 Per head it stores LSE and D of every query row (rounded to float32 for storage: a relative
 error of 6e-8 in LSE or D moves p_ij and dS_ij by about that much, far inside the parity bar)
 and the sha256 of the head's bf16 Q, K, V and dO rows, so that the test uses the cache only
-on the inputs it was made from.
+on the inputs it was made from. Heads already in the file whose input digests match are kept,
+so that a run computes only the heads the file lacks.
 
 Calls only ``oracle/`` (``head_forward``, ``head_delta``) and the seeded input generator of
 ``workloads/``. The oracle is row-wise, so query rows are split into chunks that worker
@@ -30,7 +31,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 sys.path.insert(0, ROOT)
 
 # (pack, sequence, heads) of the cached heads
-TARGETS = {"mixed": (22, (0, 1, 2, 3, 4)), "long": (0, (0, 4))}
+TARGETS = {"mixed": (22, (0, 1, 2, 3, 4)), "long": (0, (0, 1, 2, 3, 4))}
 CHUNK = 2048
 
 _G = {}
@@ -69,8 +70,20 @@ def compute(name: str, workers: int) -> None:
     ins = W.draw(pack)
     s, heads = TARGETS[name]
     out = {"pack": np.array(name), "seed": np.array(pack.seed), "seq": np.array(s), "heads": np.array(heads)}
+    old = {}
+    if os.path.exists(path_for(name)):
+        with np.load(path_for(name)) as z:
+            old = {k: z[k] for k in z.files}
     for h in heads:
         rows = head_rows(pack, ins, s, h)
+        dig = digest(rows)
+        if all(str(old.get(f"sha_{key}_{h}", "")) == val for key, val in dig.items()):
+            for key in ("q", "k", "v", "do"):
+                out[f"sha_{key}_{h}"] = old[f"sha_{key}_{h}"]
+            out[f"lse_{h}"] = old[f"lse_{h}"]
+            out[f"d_{h}"] = old[f"d_{h}"]
+            print(f"{name} head {h}: kept from {path_for(name)}", flush=True)
+            continue
         f64 = lambda t: t.to(torch.float64).numpy()
         _G.update(q=f64(rows["q"]), k=f64(rows["k"]), v=f64(rows["v"]), do=f64(rows["do"]), tau=pack.softmax_scale())
         n = _G["q"].shape[0]
@@ -83,7 +96,7 @@ def compute(name: str, workers: int) -> None:
                 dd[i0:i0 + d.size] = d
                 if k % 50 == 0:
                     print(f"  {name} head {h}: {k * CHUNK}/{n} rows, {time.time() - t0:.0f} s", flush=True)
-        for key, val in digest(rows).items():
+        for key, val in dig.items():
             out[f"sha_{key}_{h}"] = np.array(val)
         out[f"lse_{h}"] = lse.astype(np.float32)
         out[f"d_{h}"] = dd.astype(np.float32)

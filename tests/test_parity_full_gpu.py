@@ -10,8 +10,8 @@ rows the oracle computes one by one:
   * dK and dV on sampled key rows, which need every query row's LSE_i and D_i = dO_i . O_i:
     - segments of up to 4,096 tokens: every head, the oracle redoing the head in full;
     - 32,760-token sequences: two heads per segment, redone in full;
-    - the 75,600-token shard of the mixed pack (all 5 heads) and heads 0 and 4 of the
-      497,760-token shard of the long pack: LSE and D of every query row from
+    - the 75,600-token shard of the mixed pack and the 497,760-token shard of the long pack
+      (all 5 heads of each): LSE and D of every query row from
       tests/golden/long_rows_<pack>.npz, written by tests/golden/make_long_rows.py, which
       calls only the oracle (checked against the sha256 of this run's bf16 inputs before
       use). On the 75,600-token shard half of the sampled keys lie at tokens >= 52,557, whose
