@@ -302,7 +302,7 @@ def main() -> int:
     if args.price_table:
         return price_table(args.price_reps, args.json_out)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+        print(f"bench.py: the library runs one GPU's share on one GPU (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding is a design, not a measured path", file=sys.stderr)
         return 2
 
