@@ -7,7 +7,9 @@ workgroups that took it. Covering every output row (the NaN fills of the parity 
 "at least once"; the counters show "exactly once", which the split items rely on: their
 last-piece counters finish only if every piece runs once.
 
-Packs: the mixed image-video pack (the benchmark's), one head of a 32,760-token video (forward
+Packs: the mixed image-video pack (the benchmark's), many tiny images (2,000 whole sequences of
+1 to 130 tokens at 2 heads: thousands of one-block items in every queue, most of them taken by
+atomics and stealing), one head of a 32,760-token video (forward
 and dQ items split into pieces), one head of 8,192 tokens (forward, dQ and dK/dV items split),
 the ring shard (dQ items walking 8-part key chains), and a few-item pack (512 + 2,048 tokens,
 one head each), unsplit and split. In the few-item pack the 512-token sequence's four forward
@@ -40,7 +42,18 @@ def _run(plan, pack, ins, dev):
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, ws_f, ws_b
 
 
+def _many_pack():
+    """2,000 whole sequences of 1 to 130 tokens (the tile-edge lengths among them), 2 heads, d 128."""
+    import numpy as np
+    rng = np.random.default_rng(12)
+    lens = [int(x) for x in rng.integers(1, 131, size=2000)]
+    lens[:8] = [1, 2, 63, 64, 65, 127, 128, 129]
+    return W.whole_pack("many", lens, [2] * len(lens), 128, 12)
+
+
 def _pack(name):
+    if name == "many":
+        return _many_pack()
     if name == "head8k":  # one head of 8,192 tokens: forward, dQ and dK/dV items all split
         return W.Pack("head8k", (8192,), (8192,), (1,), ((0, 0, 1, 0, 8192, 0, 8192, -1),), 128, 8)
     if name.startswith("few"):  # 20 forward items in 17 queue chunks
@@ -49,7 +62,7 @@ def _pack(name):
     return W.config(name)
 
 
-@pytest.mark.parametrize("name", ["mixed", "head1", "head8k", "ring", "few", "few_nosplit"])
+@pytest.mark.parametrize("name", ["mixed", "many", "head1", "head8k", "ring", "few", "few_nosplit"])
 def test_every_item_taken_exactly_once(name):
     z = H.zl()
     pack = _pack(name)
@@ -85,3 +98,15 @@ def test_every_item_taken_exactly_once(name):
     out2, _, _ = _run(plan, pack, ins, dev)
     counts = plan.visits(ws_f, ws_b)
     assert all(bool((c == 1).all()) for c in counts.values())
+
+
+def test_many_tiny_sequences_match_the_oracle():
+    """The many-tiny-images pack element by element against the oracle: every row of all 2,000
+    sequences, uncovered rows none."""
+    pack = _many_pack()
+    ins = W.draw(pack)
+    print(f"[case] many: {len(pack.seq_q)} sequences, {sum(pack.seq_q)} tokens", flush=True)
+    out = H.run_pack(pack, ins)
+    info = out["plan"].info
+    print(f"  items: fwd {info['fwd_tiles']}, dK/dV {info['bwd_tiles']}, dQ {info['dq_tiles']}", flush=True)
+    H.compare_full(pack, ins, out, H.oracle_pack(pack, ins))
